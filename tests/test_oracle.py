@@ -1,0 +1,325 @@
+"""Pins for the CPU oracle: hand-worked fixtures, brute force, closed forms and invariants.
+
+None of these re-types the oracle's formulas: each checks a property that the
+MoBiSlice recursion (MoBiQuant explainer, section 2.A) and the 2-bit min/max quantizer
+force, so that a dropped term, a wrong sign or index, or a transposed operand in the
+oracle fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mbq_oracle as O
+from token_adaptive_bit_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- hand-worked example
+def test_pack_hand_worked(golden):
+    g = golden["pack"]
+    W = np.array(g["W"], np.float32)
+    p = O.pack(W, g["group"], g["slices"])
+    assert p["codes"].tolist() == g["codes"]
+    assert p["scale"].view(np.uint16).tolist() == g["scale_bits"]
+    assert p["zero"].view(np.uint16).tolist() == g["zero_bits"]
+    np.testing.assert_array_equal(p["residuals"][-1], np.array(g["residual"], np.float32))
+    assert p["flags"] == 0
+
+
+def test_linear_hand_worked(golden):
+    g = golden["pack"]
+    p = O.pack(np.array(g["W"], np.float32), g["group"], g["slices"])
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], g["group"])
+    x = np.array(golden["linear"]["x"])
+    assert O.linear(x, deq, np.array([1]))[0, 0] == golden["linear"]["y_b1"]
+    assert O.linear(x, deq, np.array([2]))[0, 0] == golden["linear"]["y_b2"]
+
+
+def test_route_hand_worked(golden):
+    L = np.array(golden["route"]["logits"])
+    assert O.route_from_logits(L).tolist() == golden["route"]["budget"]
+
+
+def test_regroup_hand_worked(golden):
+    perm, off = O.regroup(np.array(golden["regroup"]["budget"]), 3)
+    assert perm.tolist() == golden["regroup"]["perm"]
+    assert off.tolist() == golden["regroup"]["offsets"]
+
+
+# ---------------------------------------------------------------- the quantizer
+def _small(seed=11, N=24, K=256, group=64, outliers=3):
+    d = inputs.make_linear(seed, N, K, 5, group=group, dtype="f32", n_outliers=outliers,
+                           outlier_scale=20.0)
+    return d["W"]
+
+
+def _levels(scale, zero, group):
+    s = np.repeat(scale.astype(np.float64), group, axis=-1)
+    z = np.repeat(zero.astype(np.float64), group, axis=-1)
+    return np.stack([z + q * s for q in range(4)], axis=-1), s, z
+
+
+@pytest.mark.parametrize("group", [64, 128, 8])
+def test_slice_codes_are_nearest_level(group):
+    """Brute force over the four levels: each code picks a nearest grid point."""
+    W = _small(group=64 if group == 8 else group)
+    p = O.pack(W, group, 3)
+    for j in range(3):
+        R = p["residuals"][j].astype(np.float64)
+        lev, s, z = _levels(p["scale"][j], p["zero"][j], group)
+        dist = np.abs(R[..., None] - lev)
+        chosen = np.take_along_axis(dist, p["codes"][j][..., None].astype(np.int64), -1)[..., 0]
+        slack = 2.0 ** -20 * (np.abs(R) + np.abs(z) + 3 * s)
+        assert np.all(chosen <= dist.min(-1) + slack)
+        assert p["codes"][j].max() <= 3
+
+
+def test_grid_spans_group_range():
+    """Level 0 sits on the group minimum and level 3 on the maximum, up to half rounding."""
+    W = _small()
+    G = 64
+    p = O.pack(W, G, 3)
+    for j in range(3):
+        Rg = p["residuals"][j].reshape(W.shape[0], -1, G).astype(np.float64)
+        lo, hi = Rg.min(-1), Rg.max(-1)
+        s = p["scale"][j].astype(np.float64)
+        z = p["zero"][j].astype(np.float64)
+        assert np.all(np.abs(z - lo) <= 2.0 ** -11 * np.abs(lo) + 2.0 ** -24)
+        top = z + 3 * s
+        assert np.all(np.abs(top - hi) <= 2.0 ** -10 * (np.abs(lo) + np.abs(hi)) + 2.0 ** -22)
+        # groups that straddle zero use both end codes
+        straddle = (lo < 0) & (hi > 0)
+        cg = p["codes"][j].reshape(W.shape[0], -1, G)
+        assert np.all(cg.min(-1)[straddle] == 0)
+        assert np.all(cg.max(-1)[straddle] == 3)
+
+
+def test_residual_within_half_step_and_shrinks():
+    """|R_j| <= s_j/2 (+ the params' half rounding), and max|R_j| <= max|R_{j-1}|/3 (+ same)."""
+    W = _small(seed=5, N=40, K=512, group=128)
+    G = 128
+    p = O.pack(W, G, 3)
+    for j in range(3):
+        prev = p["residuals"][j].reshape(W.shape[0], -1, G).astype(np.float64)
+        cur = p["residuals"][j + 1].reshape(W.shape[0], -1, G).astype(np.float64)
+        s = p["scale"][j].astype(np.float64)
+        z = p["zero"][j].astype(np.float64)
+        lo, hi = prev.min(-1), prev.max(-1)
+        eps = np.abs(z - lo) + np.abs(3 * s - (hi - lo)) + 2.0 ** -20 * (np.abs(lo) + np.abs(hi))
+        assert np.all(np.abs(cur).max(-1) <= s / 2 + eps)
+        assert np.all(np.abs(cur).max(-1) <= np.abs(prev).max(-1) / 3 + eps)
+
+
+def test_error_nonincreasing_on_workload_inputs():
+    """Reconstruction error falls with every slice (Frobenius and max), config-1-like data."""
+    d = inputs.make_linear(1, 512, 256, 16, group=64, dtype="f32", n_outliers=4, outlier_scale=20.0)
+    p = O.pack(d["W"], 64, 3)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 64)
+    W = d["W"].astype(np.float64)
+    errs = [np.linalg.norm(W - O.reconstruct(deq, b)) for b in (1, 2, 3)]
+    maxes = [np.abs(W - O.reconstruct(deq, b)).max() for b in (1, 2, 3)]
+    assert errs[0] > errs[1] > errs[2]
+    assert maxes[0] > maxes[1] > maxes[2]
+    # 2 more bits per slice: error shrinks by roughly the 3 steps of the 2-bit grid
+    assert errs[1] < errs[0] / 2.5 and errs[2] < errs[1] / 2.5
+
+
+def test_reconstruction_telescopes_to_residual():
+    """W - sum_j deq_j equals the last residual, up to float32 rounding of each step."""
+    W = _small(seed=9)
+    p = O.pack(W, 64, 3)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 64)
+    diff = W.astype(np.float64) - O.reconstruct(deq, 3) - p["residuals"][3]
+    assert np.abs(diff).max() <= 8 * 2.0 ** -24 * np.abs(W).max()
+
+
+def test_closed_form_grid_group():
+    """Values exactly on z + q*s with all four levels present are reproduced by slice 1."""
+    z, s = np.float16(-0.375), np.float16(0.125)
+    q = np.array([0, 3, 1, 2, 2, 1, 0, 3] * 8, np.uint8)
+    W = (np.float32(z) + q.astype(np.float32) * np.float32(s)).reshape(1, 64)
+    p = O.pack(W, 64, 3)
+    assert p["codes"][0].ravel().tolist() == q.tolist()
+    assert p["scale"][0, 0, 0] == s and p["zero"][0, 0, 0] == z
+    assert np.all(p["residuals"][1] == 0)
+    for j in (1, 2):
+        assert np.all(p["codes"][j] == 0)
+        assert p["scale"][j, 0, 0] == 0 and p["zero"][j, 0, 0] == 0
+
+
+def test_constant_group_is_degenerate():
+    W = np.full((2, 64), 0.1, np.float32)
+    p = O.pack(W, 64, 2)
+    assert np.all(p["codes"] == 0)
+    assert np.all(p["scale"][0] == 0)
+    assert np.all(p["zero"][0] == np.float16(0.1))
+    np.testing.assert_array_equal(p["residuals"][1], np.float32(0.1) - np.float32(np.float16(0.1)))
+
+
+def test_power_of_two_scaling_is_equivariant():
+    """W * 2^k scales every param by 2^k exactly and leaves the codes alone."""
+    W = _small(seed=3) * np.float32(256.0)   # lift tiny residual minima out of half subnormals
+    a = O.pack(W, 64, 3)
+
+    def normal_params(p):      # the property needs every nonzero param to be a normal half
+        v = np.abs(np.concatenate([p["scale"].ravel(), p["zero"].ravel()]).astype(np.float64))
+        return np.all((v == 0) | (v >= 2.0 ** -14))
+
+    assert normal_params(a)
+    for k in (2, 5):
+        b = O.pack(W * np.float32(2.0 ** k), 64, 3)
+        assert normal_params(b)
+        np.testing.assert_array_equal(a["codes"], b["codes"])
+        np.testing.assert_array_equal(a["scale"].astype(np.float64) * 2.0 ** k, b["scale"].astype(np.float64))
+        np.testing.assert_array_equal(a["zero"].astype(np.float64) * 2.0 ** k, b["zero"].astype(np.float64))
+
+
+def test_row_and_group_permutation_equivariance():
+    W = _small(seed=4)
+    G = 64
+    a = O.pack(W, G, 3)
+    rp = np.random.default_rng(0).permutation(W.shape[0])
+    gp = np.array([2, 0, 3, 1])
+    Wp = W[rp].reshape(W.shape[0], 4, G)[:, gp].reshape(W.shape)
+    b = O.pack(Wp, G, 3)
+    ca = a["codes"][:, rp].reshape(3, W.shape[0], 4, G)[:, :, gp].reshape(b["codes"].shape)
+    np.testing.assert_array_equal(ca, b["codes"])
+    np.testing.assert_array_equal(a["scale"][:, rp][:, :, gp], b["scale"])
+    np.testing.assert_array_equal(a["zero"][:, rp][:, :, gp], b["zero"])
+
+
+def test_flags():
+    W = _small()
+    W[0, 0] = np.inf
+    assert O.pack(W, 64, 1)["flags"] & 1
+    W = _small()
+    W[0, 0] = 3.0e5          # range / 3 exceeds the largest half
+    assert O.pack(W, 64, 1)["flags"] & 2
+    assert O.pack(_small(), 64, 3)["flags"] == 0
+
+
+# ---------------------------------------------------------------- linear, route, regroup
+def test_linear_matches_triple_loop():
+    """Brute force: explicit float64 loops over (t, n, k) on a tiny shape."""
+    d = inputs.make_linear(21, 6, 64, 5, group=16, dtype="f32", slices=3)
+    p = O.pack(d["W"], 16, 3)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 16)
+    budget = np.array([1, 3, 2, 3, 1], np.int32)
+    Y = O.linear(d["X"], deq, budget)
+    for t in range(5):
+        for n in range(6):
+            acc = 0.0
+            for k in range(64):
+                w = 0.0
+                for j in range(budget[t]):
+                    g = k // 16
+                    w += float(p["zero"][j, n, g]) + float(p["codes"][j, n, k]) * float(p["scale"][j, n, g])
+                acc += float(d["X"][t, k]) * w
+            assert abs(Y[t, n] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+def test_linear_telescopes_per_slice():
+    """With one budget for every token, y(b) - y(b-1) = X . deq_b^T."""
+    d = inputs.make_linear(22, 32, 256, 7, group=64, dtype="f32")
+    p = O.pack(d["W"], 64, 3)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 64)
+    X = d["X"].astype(np.float64)
+    prev = np.zeros((7, 32))
+    for b in (1, 2, 3):
+        y = O.linear(X, deq, np.full(7, b))
+        np.testing.assert_allclose(y - prev, X @ deq[b - 1].T, rtol=0, atol=1e-12)
+        prev = y
+    # all three slices: X . (W - R_3)^T up to float32 rounding of the residuals
+    ref = X @ (d["W"].astype(np.float64) - p["residuals"][3]).T
+    np.testing.assert_allclose(prev, ref, rtol=0, atol=1e-5)
+
+
+def test_route_matches_argmax():
+    L = np.random.default_rng(1).standard_normal((300, 3))
+    assert np.array_equal(O.route_from_logits(L), np.argmax(L, axis=1) + 1)
+    Lt = np.round(np.random.default_rng(2).standard_normal((300, 4)))   # many ties
+    assert np.array_equal(O.route_from_logits(Lt), np.argmax(Lt, axis=1) + 1)
+
+
+def test_router_logits_match_loops():
+    d = inputs.make_linear(23, 4, 32, 3, group=16, dtype="f32")
+    L = O.router_logits(d["X"], d["Wr"])
+    for t in range(3):
+        for j in range(3):
+            ref = sum(float(d["X"][t, k]) * float(d["Wr"][k, j]) for k in range(32))
+            assert abs(L[t, j] - ref) < 1e-12
+
+
+def test_regroup_matches_python_stable_sort():
+    b = np.random.default_rng(3).integers(1, 4, 500).astype(np.int32)
+    perm, off = O.regroup(b, 3)
+    assert perm.tolist() == sorted(range(500), key=lambda t: b[t])
+    assert off.tolist() == [0] + np.cumsum(np.bincount(b, minlength=4)[1:]).tolist()
+    assert np.all(np.diff(b[perm]) >= 0)
+
+
+# ---------------------------------------------------------------- the packed blob format
+def test_blob_sizes_match_workloads():
+    # 2.25 bits per weight per slice at G=128, 2.5 at G=64 (codes + half scale and zero)
+    g = O.blob_geometry(18944, 3584, 128, 3)
+    assert g["slice_stride"] == 19095552 and g["total_bytes"] == 57286656
+    assert O.blob_geometry(512, 256, 64, 3)["total_bytes"] == 122880
+    assert O.blob_geometry(11008, 4096, 128, 3)["slice_stride"] == 12681216
+
+
+def test_blob_word_placement():
+    """Hand-placed words: row n, 16-input chunk at k0 lands in lane 16*c + r, word i."""
+    N, K = 16, 512
+    codes = np.zeros((1, N, K), np.uint8)
+    codes[0, 0, 0] = 1            # row 0, k 0: tile 0, lane 0, word 0, bits 0-1
+    codes[0, 1, 15] = 2           # row 1, k 15: tile 0, lane 1, word 0, bits 30-31
+    codes[0, 0, 64] = 3           # row 0, k 64: tile 0, lane 0, word 1
+    codes[0, 0, 16] = 1           # row 0, k 16: tile 0, lane 16, word 0
+    codes[0, 2, 256 + 200] = 3    # row 2, k 456: tile 1, rem 200 = 3*64 + 8 -> lane 2, word 3, e 8
+    sc = np.zeros((1, N, K // 128), np.float16)
+    sc[0, 3, 2] = np.float16(1.0)
+    blob = O.to_blob(codes, sc, sc, 128)
+    w = blob[:2048].view(np.uint32)
+    assert w[0] == 1
+    assert w[4] == 2 << 30
+    assert w[1] == 3
+    assert w[64] == 1             # lane 16 starts at byte 256
+    assert w[256 + 2 * 4 + 3] == 3 << 16
+    assert np.count_nonzero(w) == 5
+    geo = O.blob_geometry(N, K, 128, 1)
+    h = blob[geo["params_offset"]:].view(np.uint16)
+    # (nb 0, g 2, r 3) -> ((0*4 + 2)*16 + 3)*4 bytes = 140 bytes -> halves 70, 71
+    assert h[70] == 0x3C00 and h[71] == 0x3C00 and np.count_nonzero(h) == 2
+
+
+def test_blob_patterned_words():
+    """codes[n, k] = (n + k) % 4 gives the four repeating byte patterns 0xE4, 0x39, 0x4E, 0x93."""
+    N, K = 16, 256
+    n, k = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+    codes = ((n + k) % 4).astype(np.uint8)[None]
+    sc = np.zeros((1, N, 2), np.float16)
+    w = O.to_blob(codes, sc, sc, 128)[:1024].view(np.uint32).reshape(64, 4)
+    pat = [0xE4E4E4E4, 0x39393939, 0x4E4E4E4E, 0x93939393]
+    for lane in range(64):
+        assert all(int(x) == pat[(lane % 16) % 4] for x in w[lane])
+
+
+def test_blob_roundtrip_and_fast_writer():
+    W = _small(seed=8, N=37, K=640, group=128)
+    p = O.pack(W, 128, 2)
+    b1 = O.to_blob(p["codes"], p["scale"], p["zero"], 128)
+    b2 = O.to_blob_fast(p["codes"], p["scale"], p["zero"], 128)
+    np.testing.assert_array_equal(b1, b2)
+    c, s, z = O.from_blob(b1, 37, 640, 128, 2)
+    np.testing.assert_array_equal(c, p["codes"])
+    np.testing.assert_array_equal(s.view(np.uint16), p["scale"].view(np.uint16))
+    np.testing.assert_array_equal(z.view(np.uint16), p["zero"].view(np.uint16))
