@@ -1,0 +1,167 @@
+/*
+ * mbq.h -- C ABI of the routed bit-sliced linear library (libmbq.so), gfx950 / MI355X.
+ *
+ * What it computes (MoBiQuant: Mixture-of-Bits Quantization for Token-Adaptive Elastic
+ * LLMs; gist.science explainers, English page section 2 "Methodology", Japanese page
+ * section 2 "Proposed method"):
+ *   - MoBiSlice (section 2.A / 2.1): a weight matrix W [N x K] is decomposed into S
+ *     2-bit slices by recursive residual quantization, R_0 = W, Q_j = Q(R_{j-1}),
+ *     R_j = R_{j-1} - deq(Q_j); the first b slices summed give a 2b-bit weight
+ *     W^(b) = sum_{j<=b} deq(Q_j), all from one stored copy.
+ *   - MoBiRoute (section 2.B / 2.2): a per-token router decides how many slices b(t)
+ *     each token activates.
+ *   - The routed linear y_t = x_t . W^(b(t))^T, where a kernel fetches only the slices
+ *     the tokens use (English page, section 3, "specialized kernel implementation").
+ *
+ * Readings of points the pages leave open (fixed here, identical in the CPU oracle):
+ *   - Q is 2-bit asymmetric min/max round-to-nearest over groups of G consecutive inputs
+ *     of one output row: scale = half((max - min) / 3), zero = half(min),
+ *     code = clamp(rint((r - zero) / scale), 0, 3) (float32, IEEE divide, ties to even,
+ *     code 0 when the stored scale is 0), deq = zero + code * scale rounded twice
+ *     (float32 multiply, then float32 add; never fused).
+ *   - The router is linear, no bias: logits = x . Wr, b(t) = 1 + first argmax.
+ *   - Tokens are regrouped by a stable ascending sort on b(t).
+ *
+ * Conventions for every call:
+ *   - All pointers except `mbq_desc*`, `bytes` and `out` are DEVICE pointers owned by the
+ *     caller.  The library allocates nothing and keeps no global state: calls are
+ *     re-entrant and thread-safe.
+ *   - Every call only enqueues work on `stream` and never synchronizes the host.
+ *   - Argument, shape and alignment checks happen before any launch; failures return a
+ *     negative mbq_status and launch nothing.  A failed launch returns MBQ_ERR_DEVICE.
+ *   - Alignment: the packed blob 256 bytes, x / y / workspace 16 bytes, others 4 bytes.
+ *   - Supported: bits == 2, 1 <= slices <= 4, group in {64, 128, 256}, K % group == 0,
+ *     N >= 1, K >= group, T >= 0 (T == 0 launches nothing).
+ */
+#ifndef MBQ_H
+#define MBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MBQ_ABI_VERSION 1
+
+typedef enum {
+  MBQ_OK = 0,
+  MBQ_ERR_ARG = -1,          /* NULL or misaligned pointer, unknown dtype, NULL desc */
+  MBQ_ERR_SHAPE = -2,        /* N, K, T out of range, K % group != 0, desc inconsistent */
+  MBQ_ERR_RANGE = -3,        /* a value outside what the blob format can hold */
+  MBQ_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than mbq_linear_workspace() */
+  MBQ_ERR_DEVICE = -5,       /* the HIP launch failed (hipGetLastError) */
+  MBQ_ERR_UNSUPPORTED = -6,  /* group, slices, bits or ABI version not supported */
+} mbq_status;
+
+typedef enum { MBQ_F32 = 0, MBQ_BF16 = 1 } mbq_dtype;
+
+/*
+ * Geometry of one packed weight (the "one checkpoint for every precision" of the
+ * English page, section 3).  Filled by mbq_describe(); treat as read-only.
+ *
+ * Blob layout (slice-major, so a token that uses b slices reads only the first b):
+ *   slice j (0-based) occupies bytes [j*slice_stride, (j+1)*slice_stride):
+ *     codes  at +0:              row_blocks*k_tiles tiles of 1024 bytes; tile
+ *                                (nb, kb) at (nb*k_tiles + kb)*1024; inside a tile,
+ *                                lane l = 16*c + r owns 16 bytes at 16*l = four 32-bit
+ *                                little-endian words; word i holds the 2-bit codes of
+ *                                row 16*nb + r at inputs 256*kb + 64*i + 16*c + e,
+ *                                e = 0..15, code e in bits [2e, 2e+1].
+ *     params at +params_offset:  entry (nb, g, r) is 4 bytes at
+ *                                ((nb*groups_padded + g)*16 + r)*4: half scale in
+ *                                bits 0..15, half zero in bits 16..31.
+ *   Rows >= n and inputs >= k are padding: code 0, params (0, 0).
+ */
+typedef struct {
+  int32_t abi;            /* MBQ_ABI_VERSION */
+  int32_t n, k;           /* output rows, inputs */
+  int32_t group;          /* G: inputs per (scale, zero) group */
+  int32_t slices;         /* S: 2-bit slices stored */
+  int32_t bits;           /* bits per slice: 2 */
+  int32_t row_blocks;     /* ceil(n / 16) */
+  int32_t k_tiles;        /* ceil(k / 256) */
+  int32_t groups_padded;  /* k_tiles * 256 / group */
+  int32_t reserved;
+  uint64_t codes_bytes;   /* per slice: row_blocks * k_tiles * 1024 */
+  uint64_t params_bytes;  /* per slice: row_blocks * groups_padded * 64 */
+  uint64_t params_offset; /* codes_bytes rounded up to 256 */
+  uint64_t slice_stride;  /* params_offset + params_bytes rounded up to 256 */
+  uint64_t total_bytes;   /* slices * slice_stride */
+} mbq_desc;
+
+/* Host only: validates the shape and fills *out.  Launches nothing. */
+mbq_status mbq_describe(int32_t n, int32_t k, int32_t group, int32_t slices, mbq_desc* out);
+
+/*
+ * MoBiSlice pack (English page section 2.A; Japanese page section 2.1).
+ *   w:          [n x k] row-major weights, float32 or bfloat16 (w_dtype).
+ *   packed:     desc->total_bytes, 256-byte aligned; fully overwritten (padding too).
+ *   dev_status: nullable int32; the kernel ORs in bit 0 if W holds a non-finite value
+ *               and bit 1 if a scale or zero overflowed half.  The caller clears it
+ *               before the call and reads it after synchronizing.  With a nonzero
+ *               status the blob contents are unspecified.
+ */
+mbq_status mbq_pack(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void* packed,
+                    int32_t* dev_status, hipStream_t stream);
+
+/*
+ * MoBiRoute (English page section 2.B; Japanese page section 2.2), linear-argmax form.
+ *   x:       [t x k] tokens (float32 or bfloat16), or NULL to route from the caller's
+ *            `logits` instead ("logits-in" mode).
+ *   wr:      [k x s] float32 router weights (ignored when x is NULL).
+ *   logits:  [t x s] float32; written (x != NULL) or read (x == NULL).
+ *   budget:  [t] int32 out, b(t) = 1 + first index of the largest logit.
+ *   perm:    [t] int32 out, stable ascending order of tokens by budget.
+ *   offsets: [s + 1] int32 out, offsets[i] = #tokens with budget <= i.
+ * NaN logits are outside the contract.  1 <= s <= 4, t <= 1<<24.
+ */
+mbq_status mbq_route(int32_t t, int32_t k, int32_t s, const void* x, mbq_dtype x_dtype,
+                     const float* wr, float* logits, int32_t* budget, int32_t* perm,
+                     int32_t* offsets, hipStream_t stream);
+
+/*
+ * Regroup tokens whose budgets are given (forced mixes): the stable counting sort of
+ * mbq_route without the router.  budget values must lie in [1, s].
+ */
+mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* perm,
+                       int32_t* offsets, hipStream_t stream);
+
+/* Host only: bytes of device workspace mbq_linear needs for t tokens (may be 0). */
+mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
+                                size_t* bytes);
+
+/*
+ * Routed linear y_t = x_t . (sum_{j <= b(t)} deq(Q_j))^T (English page sections 2.A and
+ * 3: each token reconstructs its own precision from the shared slices; slices no token
+ * uses are never read).
+ *   packed:  the blob written by mbq_pack for `desc`.
+ *   x:       [t x k] row-major, float32 or bfloat16, original token order.
+ *   perm, offsets: as produced by mbq_route / mbq_regroup for these t tokens
+ *            (offsets has desc->slices + 1 entries; the token at sorted position i has
+ *            budget b with offsets[b-1] <= i < offsets[b]).
+ *   y:       [t x n] row-major, float32 or bfloat16, original token order; every element
+ *            is written.  Accumulation is float32; bfloat16 output is rounded once.
+ *   workspace: at least mbq_linear_workspace() bytes; contents are scratch.
+ * Decode (t <= 64) runs a streaming kernel that reads each needed slice once; prefill
+ * (t > 64) dequantizes the summed slices to bfloat16 in LDS and runs an MFMA GEMM per
+ * budget group.
+ */
+mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                      mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
+                      void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Static string for a status code. */
+const char* mbq_status_str(mbq_status status);
+
+/* MBQ_ABI_VERSION of the loaded library. */
+int32_t mbq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBQ_H */

@@ -23,7 +23,8 @@ Readings where the pages leave a step open (each one is listed in the design doc):
     = clamp(rint((r - zero) / scale), 0, 3) computed with the *stored* (rounded) params,
     dequantized value zero + code * scale.  The pages only write "Q(R_e)".
   * Pack arithmetic is float32 with every operation rounded on its own (no fused
-    multiply-add), rint rounds half to even, a zero stored scale gives code 0.
+    multiply-add), rint rounds half to even, a zero stored scale gives code 0, and a
+    group minimum of -0 is stored as +0 (the pages say nothing about signed zeros).
   * The router is linear without bias; a token's slice count is 1 + the first index of
     the largest logit.  (The pages' own router is a 2-layer MLP with a threshold.)
   * Regrouping is a stable sort of tokens by ascending slice count.
@@ -59,6 +60,7 @@ def quantize_slice(R: np.ndarray, group: int):
     Rg = R.reshape(N, K // group, group)
     lo = Rg.min(axis=2)                       # exact
     hi = Rg.max(axis=2)                       # exact
+    lo = (lo + F32(0.0)).astype(F32)          # a signed-zero minimum is stored as +0
     with np.errstate(over="ignore", invalid="ignore"):
         span = (hi - lo).astype(F32)          # one float32 rounding
         step32 = (span / F32(3.0)).astype(F32)  # one float32 rounding (IEEE divide)

@@ -1,0 +1,134 @@
+"""Host-only checks of the C ABI: the library loads, exports what include/mbq.h declares,
+reports the blob geometry of the format, and rejects bad arguments before any launch.
+
+No test here touches a GPU: every call either fails validation (and so launches nothing)
+or is a host-only call (mbq_describe, mbq_linear_workspace, a t == 0 linear).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mbq.h")
+
+lib_mod = pytest.importorskip("token_adaptive_bit_amd._lib",
+                              reason="libmbq.so not built (run __graft_entry__.build())")
+L = lib_mod.LIB
+OK, ARG, SHAPE, RANGE, WS, DEV, UNSUP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+FAKE = 0x7F0000000000          # a 256-byte aligned address that is never dereferenced
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mbq_status|const char\*|int32_t)\s+(mbq_\w+)\(", text, re.M)))
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert set(names) == set(lib_mod.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.mbq_abi_version() == 1
+
+
+def test_status_strings():
+    for code in (OK, ARG, SHAPE, RANGE, WS, DEV, UNSUP):
+        assert L.mbq_status_str(code)
+    assert L.mbq_status_str(123) == b"unknown status"
+
+
+def desc(n, k, g, s):
+    d = lib_mod.MbqDesc()
+    st = L.mbq_describe(n, k, g, s, ctypes.byref(d))
+    return st, d
+
+
+def test_describe_geometry_matches_format():
+    from oracle import mbq_oracle as O   # the format description, written independently
+    for (n, k, g, s) in [(512, 256, 64, 3), (18944, 3584, 128, 3), (11008, 4096, 128, 3),
+                         (200, 640, 128, 2), (5120, 13824, 128, 3), (17, 768, 256, 4)]:
+        st, d = desc(n, k, g, s)
+        assert st == OK
+        geo = O.blob_geometry(n, k, g, s)
+        assert d.total_bytes == geo["total_bytes"]
+        assert d.slice_stride == geo["slice_stride"]
+        assert d.params_offset == geo["params_offset"]
+        assert d.codes_bytes == geo["codes_bytes"] and d.params_bytes == geo["params_bytes"]
+        assert (d.row_blocks, d.k_tiles, d.groups_padded) == (geo["NB"], geo["KB"], geo["NG"])
+
+
+@pytest.mark.parametrize("n,k,g,s,want", [
+    (16, 256, 32, 3, UNSUP), (16, 256, 96, 3, UNSUP), (16, 256, 64, 0, UNSUP),
+    (16, 256, 64, 5, UNSUP), (0, 256, 64, 3, SHAPE), (16, 100, 64, 3, SHAPE),
+    (16, 32, 64, 1, SHAPE), (-3, 256, 64, 1, SHAPE)])
+def test_describe_rejects(n, k, g, s, want):
+    st, _ = desc(n, k, g, s)
+    assert st == want
+    assert L.mbq_describe(16, 256, 64, 1, None) == ARG
+
+
+def test_pack_validation():
+    st, d = desc(64, 256, 64, 3)
+    assert st == OK
+    dp = ctypes.byref(d)
+    assert L.mbq_pack(None, P(FAKE), F32, P(FAKE), None, None) == ARG
+    assert L.mbq_pack(dp, None, F32, P(FAKE), None, None) == ARG
+    assert L.mbq_pack(dp, P(FAKE), F32, None, None, None) == ARG
+    assert L.mbq_pack(dp, P(FAKE), 7, P(FAKE), None, None) == ARG
+    assert L.mbq_pack(dp, P(FAKE), F32, P(FAKE + 16), None, None) == ARG     # blob alignment
+    assert L.mbq_pack(dp, P(FAKE + 2), F32, P(FAKE), None, None) == ARG      # f32 alignment
+    assert L.mbq_pack(dp, P(FAKE), F32, P(FAKE), P(FAKE + 2), None) == ARG   # status alignment
+    bad = lib_mod.MbqDesc.from_buffer_copy(d)
+    bad.abi = 99
+    assert L.mbq_pack(ctypes.byref(bad), P(FAKE), F32, P(FAKE), None, None) == UNSUP
+    bad = lib_mod.MbqDesc.from_buffer_copy(d)
+    bad.total_bytes += 256
+    assert L.mbq_pack(ctypes.byref(bad), P(FAKE), F32, P(FAKE), None, None) == SHAPE
+
+
+def test_route_and_regroup_validation():
+    f = P(FAKE)
+    assert L.mbq_route(4, 16, 0, f, F32, f, f, f, f, f, None) == UNSUP
+    assert L.mbq_route(4, 16, 5, f, F32, f, f, f, f, f, None) == UNSUP
+    assert L.mbq_route(-1, 16, 3, f, F32, f, f, f, f, f, None) == SHAPE
+    assert L.mbq_route(4, 0, 3, f, F32, f, f, f, f, f, None) == SHAPE
+    assert L.mbq_route(4, 16, 3, f, 9, f, f, f, f, f, None) == ARG
+    assert L.mbq_route(4, 16, 3, f, F32, None, f, f, f, f, None) == ARG
+    assert L.mbq_route(4, 16, 3, f, F32, f, None, f, f, f, None) == ARG
+    assert L.mbq_route(4, 16, 3, f, F32, f, f, f, P(FAKE + 1), f, None) == ARG
+    assert L.mbq_regroup(4, 3, None, f, f, None) == ARG
+    assert L.mbq_regroup(4, 0, f, f, f, None) == UNSUP
+    assert L.mbq_regroup(-2, 3, f, f, f, None) == SHAPE
+
+
+def test_linear_validation_and_workspace():
+    st, d = desc(200, 640, 128, 3)
+    dp = ctypes.byref(d)
+    f = P(FAKE)
+    n = ctypes.c_size_t()
+    assert L.mbq_linear_workspace(dp, 16, BF16, ctypes.byref(n)) == OK
+    need16 = n.value
+    assert need16 > 0
+    assert L.mbq_linear_workspace(dp, 16, F32, ctypes.byref(n)) == OK
+    assert n.value > need16                      # float32 inputs keep a high and a low part
+    assert L.mbq_linear_workspace(dp, 1000, BF16, ctypes.byref(n)) == OK and n.value == 0
+    assert L.mbq_linear_workspace(dp, -1, BF16, ctypes.byref(n)) == SHAPE
+    assert L.mbq_linear_workspace(dp, 1, BF16, None) == ARG
+    args = lambda **kw: dict(dict(desc=dp, packed=f, t=16, x=f, xd=BF16, perm=f, off=f, y=f,
+                                  yd=BF16, ws=f, wsb=need16, s=None), **kw)
+    call = lambda a: L.mbq_linear(a["desc"], a["packed"], a["t"], a["x"], a["xd"], a["perm"],
+                                  a["off"], a["y"], a["yd"], a["ws"], a["wsb"], a["s"])
+    assert call(args(desc=None)) == ARG
+    assert call(args(packed=None)) == ARG
+    assert call(args(packed=P(FAKE + 64))) == ARG
+    assert call(args(x=P(FAKE + 8))) == ARG
+    assert call(args(y=None)) == ARG
+    assert call(args(yd=3)) == ARG
+    assert call(args(t=-1)) == SHAPE
+    assert call(args(ws=None)) == WS
+    assert call(args(wsb=need16 - 1)) == WS
+    assert call(args(t=0, ws=None, wsb=0)) == OK          # nothing to do, nothing launched

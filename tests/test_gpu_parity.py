@@ -1,0 +1,324 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: packed codes and params bit-exact; routes bit-exact given identical logits;
+regroup bit-exact; outputs within max_n |y - yref| / max_n |yref| <= 1e-2 per token
+(bf16 I/O, fp32 accumulate), and a tighter bar where the arithmetic allows it.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import mbq_oracle as O
+from token_adaptive_bit_amd import inputs
+from parity import (TOL, budget_from_perm, oracle_blob, oracle_linear_rows, say,
+                    token_errors)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def mbq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from token_adaptive_bit_amd import api
+    return api
+
+
+def to_dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device=DEV, dtype=dtype)
+
+
+def tdt(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def gpu_pack(mbq, W, group, slices, dtype):
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    p = mbq.pack(to_dev(W, tdt(dtype)), group=group, slices=slices, status=st)
+    torch.cuda.synchronize()
+    return p, int(st.item())
+
+
+# ------------------------------------------------------------------------------ pack
+PACK_CASES = [
+    # N, K, G, S, dtype, seed, outliers
+    (512, 256, 64, 3, "f32", 1, 4),       # the tiny workload's shape
+    (200, 640, 128, 3, "bf16", 2, 3),     # ragged rows (not /16) and inputs (not /256)
+    (33, 512, 256, 4, "bf16", 3, 0),
+    (64, 256, 64, 1, "f32", 4, 2),
+    (48, 768, 128, 2, "bf16", 5, 1),
+    (17, 320, 64, 3, "f32", 6, 0),        # K = 320: 5 groups, one padded tile
+]
+
+
+@pytest.mark.parametrize("N,K,G,S,dtype,seed,outl", PACK_CASES)
+def test_pack_bitexact(mbq, N, K, G, S, dtype, seed, outl):
+    say(f"pack N={N} K={K} G={G} S={S} {dtype}")
+    d = inputs.make_linear(seed, N, K, 1, group=G, slices=S, dtype=dtype, n_outliers=outl,
+                           outlier_scale=20.0)
+    want, _ = oracle_blob(d["W"], G, S)
+    p, st = gpu_pack(mbq, d["W"], G, S, dtype)
+    assert st == 0
+    got = p.blob.cpu().numpy()
+    assert got.shape == want.shape
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+
+
+def test_pack_edge_groups(mbq):
+    """Constant groups, exact grids, f16-subnormal steps, signed zeros, huge dynamic range."""
+    rng = np.random.default_rng(7)
+    W = (rng.standard_normal((32, 512)).astype(np.float32) * np.float32(0.02))
+    W[0, :64] = 0.125                                       # constant
+    W[1, :64] = np.float32(-0.375) + np.float32(0.125) * (np.arange(64) % 4)  # exact grid
+    W[2, :64] = rng.standard_normal(64).astype(np.float32) * np.float32(1e-6)  # subnormal step
+    W[3, :64] = 0.0
+    W[3, 5] = -0.0
+    W[3, 64:128] = -0.0                                     # signed-zero minimum
+    W[3, 70] = 1.0
+    W[4, :64] = rng.standard_normal(64).astype(np.float32) * np.float32(3e3)  # large
+    W[5, 64:128] = np.float32(1e-30)                        # float32 tiny, half zero
+    want, _ = oracle_blob(W, 64, 3)
+    p, st = gpu_pack(mbq, W, 64, 3, "f32")
+    assert st == 0
+    got = p.blob.cpu().numpy()
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} bytes differ"
+
+
+def test_pack_status_flags(mbq):
+    W = np.zeros((16, 256), np.float32)
+    W[3, 7] = np.inf
+    _, st = gpu_pack(mbq, W, 64, 2, "f32")
+    assert st & 1
+    W = np.zeros((16, 256), np.float32)
+    W[1, 1] = 3.0e5
+    _, st = gpu_pack(mbq, W, 64, 1, "f32")
+    assert st & 2
+    assert O.pack(W, 64, 1)["flags"] & 2
+
+
+def test_pack_full_decode_workload(mbq):
+    """The 18944 x 3584 bf16 decode weight with outlier columns, all three slices."""
+    say("pack full 18944x3584")
+    d = inputs.make_config(2)
+    want, _ = oracle_blob(d["W"], 128, 3)
+    p, st = gpu_pack(mbq, d["W"], 128, 3, "bf16")
+    assert st == 0
+    got = p.blob.cpu().numpy()
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} bytes differ"
+
+
+# ------------------------------------------------------------------------------ route
+@pytest.mark.parametrize("T,S", [(2048, 3), (1, 3), (37, 4), (5000, 2), (1025, 1)])
+def test_route_from_logits_bitexact(mbq, T, S):
+    say(f"route logits-in T={T} S={S}")
+    rng = np.random.default_rng(T + S)
+    L = np.round(rng.standard_normal((T, S)) * 2).astype(np.float32)   # many exact ties
+    b, perm, off = mbq.route_from_logits(to_dev(L, torch.float32))
+    torch.cuda.synchronize()
+    wb = O.route_from_logits(L)
+    wp, wo = O.regroup(wb, S)
+    assert np.array_equal(b.cpu().numpy(), wb)
+    assert np.array_equal(perm.cpu().numpy(), wp)
+    assert np.array_equal(off.cpu().numpy(), wo)
+
+
+def test_route_empty(mbq):
+    L = torch.zeros((0, 3), dtype=torch.float32, device=DEV)
+    b, perm, off = mbq.route_from_logits(L)
+    torch.cuda.synchronize()
+    assert off.cpu().tolist() == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("cfg_dtype,T,K", [("f32", 16, 256), ("bf16", 64, 5120), ("bf16", 300, 4096)])
+def test_route_with_router(mbq, cfg_dtype, T, K):
+    say(f"route x T={T} K={K} {cfg_dtype}")
+    d = inputs.make_linear(31, 8, K, T, dtype=cfg_dtype)
+    logits, b, perm, off = mbq.route(to_dev(d["X"], tdt(cfg_dtype)), to_dev(d["Wr"], torch.float32))
+    torch.cuda.synchronize()
+    Lg = logits.cpu().numpy()
+    Lref = O.router_logits(d["X"], d["Wr"])
+    assert np.abs(Lg - Lref).max() <= 1e-5 * np.abs(Lref).max()
+    # bit-exact given identical logits
+    wb = O.route_from_logits(Lg)
+    wp, wo = O.regroup(wb, 3)
+    assert np.array_equal(b.cpu().numpy(), wb)
+    assert np.array_equal(perm.cpu().numpy(), wp)
+    assert np.array_equal(off.cpu().numpy(), wo)
+    # against float64 logits: a flip is allowed only at a near tie
+    b64 = O.route_from_logits(Lref)
+    flips = np.nonzero(b64 != wb)[0]
+    for t in flips:
+        top2 = np.sort(Lref[t])[-2:]
+        assert top2[1] - top2[0] < 1e-4 * np.abs(Lref[t]).max()
+
+
+def test_regroup_forced_mix(mbq):
+    d = inputs.make_linear(3, 4, 64, 2048, forced_counts=inputs.forced_mix(2048, [0.3, 0.5, 0.2]))
+    perm, off = mbq.regroup(to_dev(d["budget"], torch.int32), 3)
+    torch.cuda.synchronize()
+    wp, wo = O.regroup(d["budget"], 3)
+    assert wo.tolist() == [0, 614, 1638, 2048]
+    assert np.array_equal(perm.cpu().numpy(), wp)
+    assert np.array_equal(off.cpu().numpy(), wo)
+
+
+# ------------------------------------------------------------------------------ linear
+def run_linear(mbq, d, budget=None, out_dtype=None, rows=None):
+    """GPU pack + route/regroup + linear; returns (y_gpu, y_ref [T, rows], budget)."""
+    G, S, dt = d["group"], d["slices"], d["dtype"]
+    p, st = gpu_pack(mbq, d["W"], G, S, dt)
+    assert st == 0
+    x = to_dev(d["X"], tdt(dt))
+    if budget is None:
+        _, _, perm, off = mbq.route(x, to_dev(d["Wr"], torch.float32))
+    else:
+        perm, off = mbq.regroup(to_dev(budget, torch.int32), S)
+    y = mbq.linear(p, x, perm, off, out_dtype=out_dtype or tdt(dt))
+    torch.cuda.synchronize()
+    b = budget_from_perm(perm.cpu().numpy(), off.cpu().numpy())
+    if budget is not None:
+        assert np.array_equal(b, budget)
+    yref = oracle_linear_rows(d["W"], d["X"], b, G, S, rows)
+    yg = y.float().cpu().numpy()
+    if rows is not None:
+        yg = yg[:, rows]
+    return yg, yref, b
+
+
+LINEAR_CASES = [
+    # N, K, G, S, T, dtype, budget mode
+    (512, 256, 64, 3, 16, "f32", "router"),     # the tiny workload
+    (200, 640, 128, 3, 1, "bf16", "router"),
+    (200, 640, 128, 3, 5, "bf16", "mix"),
+    (200, 640, 128, 3, 17, "bf16", "mix"),
+    (130, 768, 256, 4, 33, "bf16", "mix"),
+    (96, 512, 64, 2, 64, "bf16", "mix"),
+    (96, 512, 64, 3, 64, "bf16", "all1"),
+    (96, 512, 64, 3, 40, "bf16", "allS"),
+    (77, 384, 128, 1, 9, "f32", "allS"),
+    (200, 640, 128, 3, 65, "bf16", "mix"),      # smallest prefill
+    (200, 640, 128, 3, 300, "bf16", "mix"),
+    (300, 1024, 128, 3, 257, "bf16", "router"),
+    (130, 768, 256, 4, 200, "bf16", "mix"),
+    (96, 512, 64, 2, 129, "f32", "mix"),
+    (64, 256, 64, 3, 100, "bf16", "all1"),
+]
+
+
+def budgets_for(mode, T, S, seed):
+    rng = np.random.default_rng(seed)
+    if mode == "mix":
+        return rng.integers(1, S + 1, T).astype(np.int32)
+    if mode == "all1":
+        return np.ones(T, np.int32)
+    if mode == "allS":
+        return np.full(T, S, np.int32)
+    return None
+
+
+@pytest.mark.parametrize("N,K,G,S,T,dtype,mode", LINEAR_CASES)
+def test_linear_parity(mbq, N, K, G, S, T, dtype, mode):
+    say(f"linear N={N} K={K} G={G} S={S} T={T} {dtype} {mode}")
+    d = inputs.make_linear(100 + T, N, K, T, group=G, slices=S, dtype=dtype, n_outliers=2,
+                           outlier_scale=10.0)
+    yg, yref, _ = run_linear(mbq, d, budgets_for(mode, T, S, T))
+    err = token_errors(yg, yref)
+    say(f"  max token error {err.max():.3e}")
+    assert err.max() <= TOL
+    if dtype == "f32" and T <= 64:
+        assert err.max() <= 1e-4     # exact codes, split activations, float32 accumulate
+
+
+def test_linear_fp32_output_from_bf16(mbq):
+    d = inputs.make_linear(5, 160, 512, 12, dtype="bf16")
+    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", 12, 3, 1), out_dtype=torch.float32)
+    assert token_errors(yg, yref).max() <= 1e-4
+
+
+def test_linear_deterministic(mbq):
+    for T in (16, 200):
+        d = inputs.make_linear(9, 256, 1024, T)
+        p, _ = gpu_pack(mbq, d["W"], 128, 3, "bf16")
+        x = to_dev(d["X"], torch.bfloat16)
+        _, _, perm, off = mbq.route(x, to_dev(d["Wr"], torch.float32))
+        y1 = mbq.linear(p, x, perm, off).clone()
+        y2 = mbq.linear(p, x, perm, off)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_linear_empty_batch(mbq):
+    d = inputs.make_linear(9, 64, 256, 1)
+    p, _ = gpu_pack(mbq, d["W"], 128, 3, "bf16")
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
+    perm = torch.zeros(0, dtype=torch.int32, device=DEV)
+    off = torch.zeros(4, dtype=torch.int32, device=DEV)
+    y = mbq.linear(p, x, perm, off)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+
+
+# ------------------------------------------------------------------------------ full sizes
+def sample_rows(N, seed, k=48):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.choice(N, k, replace=False), [0, N - 1]]))
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_full_decode_workload(mbq, T):
+    say(f"full decode 18944x3584 T={T}")
+    d = inputs.make_config(2)
+    d = dict(d, X=d["X"][:T], T=T)
+    rows = sample_rows(d["N"], T)
+    yg, yref, _ = run_linear(mbq, d, None, rows=rows)
+    err = token_errors(yg, yref)
+    say(f"  max token error {err.max():.3e}")
+    assert err.max() <= TOL
+
+
+def test_full_prefill_workload(mbq):
+    say("full prefill 11008x4096 T=2048 mix 614/1024/410")
+    d = inputs.make_config(3)
+    rows = sample_rows(d["N"], 3, k=24)
+    yg, yref, _ = run_linear(mbq, d, d["budget"], rows=rows)
+    err = token_errors(yg, yref)
+    say(f"  max token error {err.max():.3e}")
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("T,mode", [(32, "all1"), (32, "router"), (1024, "allS"), (1024, "router")])
+def test_full_sweep_workload(mbq, T, mode):
+    say(f"full sweep 14336x4096 T={T} {mode}")
+    d = inputs.make_config(5)
+    d = dict(d, X=d["X"][:T], T=T)
+    rows = sample_rows(d["N"], T, k=24)
+    yg, yref, _ = run_linear(mbq, d, budgets_for(mode, T, 3, 0), rows=rows)
+    err = token_errors(yg, yref)
+    say(f"  max token error {err.max():.3e}")
+    assert err.max() <= TOL
+
+
+def test_full_layer14b_workload(mbq):
+    """Seven linears of the 14B-like layer, one router on the layer input, T = 64."""
+    cfg = inputs.make_config(4)
+    x0 = to_dev(cfg["X_layer"], torch.bfloat16)
+    _, _, perm, off = mbq.route(x0, to_dev(cfg["Wr"], torch.float32))
+    torch.cuda.synchronize()
+    b = budget_from_perm(perm.cpu().numpy(), off.cpu().numpy())
+    for lin in cfg["linears"]:
+        say(f"full layer14b {lin['name']} {lin['W'].shape}")
+        W = lin["W"]
+        p, st = gpu_pack(mbq, W, 128, 3, "bf16")
+        assert st == 0
+        y = mbq.linear(p, to_dev(lin["X"], torch.bfloat16), perm, off)
+        torch.cuda.synchronize()
+        rows = sample_rows(W.shape[0], 4, k=16)
+        yref = oracle_linear_rows(W, lin["X"], b, 128, 3, rows)
+        err = token_errors(y.float().cpu().numpy()[:, rows], yref)
+        assert err.max() <= TOL
+        del p

@@ -323,3 +323,12 @@ def test_blob_roundtrip_and_fast_writer():
     np.testing.assert_array_equal(c, p["codes"])
     np.testing.assert_array_equal(s.view(np.uint16), p["scale"].view(np.uint16))
     np.testing.assert_array_equal(z.view(np.uint16), p["zero"].view(np.uint16))
+
+
+def test_signed_zero_minimum_stored_as_plus_zero():
+    W = np.zeros((1, 64), np.float32)
+    W[0, 3] = -0.0
+    W[0, 9] = 1.5
+    p = O.pack(W, 64, 1)
+    assert p["zero"].view(np.uint16)[0, 0] == 0
+    assert p["codes"][0, 0, 9] == 3 and p["codes"][0, 0, 3] == 0

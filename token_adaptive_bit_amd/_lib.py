@@ -1,0 +1,89 @@
+"""ctypes binding of libmbq.so (the C ABI declared in include/mbq.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  If the shared library is
+missing the import of this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmbq.so")
+
+MBQ_F32, MBQ_BF16 = 0, 1
+ABI_VERSION = 1
+
+STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANGE",
+          -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}
+
+EXPORTS = ("mbq_describe", "mbq_pack", "mbq_route", "mbq_regroup", "mbq_linear_workspace",
+           "mbq_linear", "mbq_status_str", "mbq_abi_version")
+
+
+class MbqDesc(ctypes.Structure):
+    _fields_ = [("abi", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("slices", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("row_blocks", ctypes.c_int32), ("k_tiles", ctypes.c_int32),
+                ("groups_padded", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("codes_bytes", ctypes.c_uint64), ("params_bytes", ctypes.c_uint64),
+                ("params_offset", ctypes.c_uint64), ("slice_stride", ctypes.c_uint64),
+                ("total_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class MbqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_str(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m token_adaptive_bit_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, U64, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
+    D = P(MbqDesc)
+    lib.mbq_describe.argtypes = [I32, I32, I32, I32, D]
+    lib.mbq_pack.argtypes = [D, VP, I32, VP, VP, VP]
+    lib.mbq_route.argtypes = [I32, I32, I32, VP, I32, VP, VP, VP, VP, VP, VP]
+    lib.mbq_regroup.argtypes = [I32, I32, VP, VP, VP, VP]
+    lib.mbq_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
+    lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, VP]
+    lib.mbq_status_str.argtypes = [I32]
+    lib.mbq_status_str.restype = ctypes.c_char_p
+    lib.mbq_abi_version.argtypes = []
+    for name in EXPORTS:
+        if name not in ("mbq_status_str",):
+            getattr(lib, name).restype = I32
+    if lib.mbq_abi_version() != ABI_VERSION:
+        raise ImportError("libmbq ABI version mismatch")
+    return lib
+
+
+LIB = _load()
+
+
+def _str(status: int) -> str:
+    return LIB.mbq_status_str(status).decode()
+
+
+def check(status: int, what: str) -> None:
+    if status != 0:
+        raise MbqError(status, what)
+
+
+def describe(n: int, k: int, group: int, slices: int) -> MbqDesc:
+    d = MbqDesc()
+    check(LIB.mbq_describe(n, k, group, slices, ctypes.byref(d)), "mbq_describe")
+    return d
+
+
+def workspace_bytes(desc: MbqDesc, t: int, x_dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    check(LIB.mbq_linear_workspace(ctypes.byref(desc), t, x_dtype, ctypes.byref(n)),
+          "mbq_linear_workspace")
+    return int(n.value)

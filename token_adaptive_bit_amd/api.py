@@ -1,0 +1,141 @@
+"""PyTorch-facing wrappers over the C ABI (include/mbq.h).
+
+Tensors are plain CUDA (HIP) tensors; each call passes their device pointers and the
+current stream to libmbq and returns without synchronizing.  No arithmetic happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import MBQ_BF16, MBQ_F32, MbqDesc, MbqError, check, describe
+
+__all__ = ["PackedLinear", "pack", "route", "route_from_logits", "regroup", "linear",
+           "linear_workspace", "describe", "MbqError"]
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MBQ_F32
+    if t.dtype == torch.bfloat16:
+        return MBQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _p(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class PackedLinear:
+    """One packed weight: geometry plus the slice-major blob (uint8 device tensor)."""
+    desc: MbqDesc
+    blob: torch.Tensor
+
+    @property
+    def n(self): return self.desc.n
+
+    @property
+    def k(self): return self.desc.k
+
+    @property
+    def group(self): return self.desc.group
+
+    @property
+    def slices(self): return self.desc.slices
+
+    def slice_bytes(self) -> int:
+        return int(self.desc.slice_stride)
+
+
+def pack(w: torch.Tensor, group: int = 128, slices: int = 3, status: torch.Tensor | None = None,
+         out: torch.Tensor | None = None) -> PackedLinear:
+    """MoBiSlice pack of W [n, k] (float32 or bfloat16) into a new or given blob."""
+    _dev(w, "w")
+    n, k = w.shape
+    d = describe(n, k, group, slices)
+    if out is None:
+        out = torch.empty(int(d.total_bytes), dtype=torch.uint8, device=w.device)
+    if out.numel() < d.total_bytes:
+        raise ValueError("out is smaller than the packed size")
+    check(_lib.LIB.mbq_pack(ctypes.byref(d), _p(w), _dtype(w), _p(out), _p(status), _stream()),
+          "mbq_pack")
+    return PackedLinear(d, out)
+
+
+def route(x: torch.Tensor, wr: torch.Tensor, logits=None, budget=None, perm=None, offsets=None):
+    """Router logits x . wr (float32), budgets 1 + first argmax, stable regroup."""
+    _dev(x, "x")
+    _dev(wr, "wr")
+    t, k = x.shape
+    s = wr.shape[1]
+    dev = x.device
+    logits = torch.empty((t, s), dtype=torch.float32, device=dev) if logits is None else logits
+    budget = torch.empty(t, dtype=torch.int32, device=dev) if budget is None else budget
+    perm = torch.empty(t, dtype=torch.int32, device=dev) if perm is None else perm
+    offsets = torch.empty(s + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    check(_lib.LIB.mbq_route(t, k, s, _p(x), _dtype(x), _p(wr), _p(logits), _p(budget), _p(perm),
+                             _p(offsets), _stream()), "mbq_route")
+    return logits, budget, perm, offsets
+
+
+def route_from_logits(logits: torch.Tensor):
+    """Route from given float32 logits [t, s] (the bit-exact route contract)."""
+    _dev(logits, "logits")
+    t, s = logits.shape
+    dev = logits.device
+    budget = torch.empty(t, dtype=torch.int32, device=dev)
+    perm = torch.empty(t, dtype=torch.int32, device=dev)
+    offsets = torch.empty(s + 1, dtype=torch.int32, device=dev)
+    check(_lib.LIB.mbq_route(t, 0, s, None, MBQ_F32, None, _p(logits), _p(budget), _p(perm),
+                             _p(offsets), _stream()), "mbq_route")
+    return budget, perm, offsets
+
+
+def regroup(budget: torch.Tensor, slices: int, perm=None, offsets=None):
+    """Stable regroup of tokens with given budgets (int32 [t], values in 1..slices)."""
+    _dev(budget, "budget")
+    t = budget.shape[0]
+    dev = budget.device
+    perm = torch.empty(t, dtype=torch.int32, device=dev) if perm is None else perm
+    offsets = torch.empty(slices + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    check(_lib.LIB.mbq_regroup(t, slices, _p(budget), _p(perm), _p(offsets), _stream()),
+          "mbq_regroup")
+    return perm, offsets
+
+
+def linear_workspace(p: PackedLinear, t: int, x_dtype=torch.bfloat16) -> int:
+    return _lib.workspace_bytes(p.desc, t, MBQ_BF16 if x_dtype == torch.bfloat16 else MBQ_F32)
+
+
+def linear(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor,
+           out_dtype: torch.dtype | None = None, y: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed linear y = x . W^(b(t))^T, original token order."""
+    _dev(x, "x")
+    t = x.shape[0]
+    out_dtype = out_dtype or x.dtype
+    if y is None:
+        y = torch.empty((t, p.n), dtype=out_dtype, device=x.device)
+    need = linear_workspace(p, t, x.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    check(_lib.LIB.mbq_linear(ctypes.byref(p.desc), _p(p.blob), t, _p(x), _dtype(x), _p(perm),
+                              _p(offsets), _p(y), _dtype(y), _p(workspace), ws_bytes, _stream()),
+          "mbq_linear")
+    return y

@@ -1,0 +1,147 @@
+// Host side of the C ABI: validation, geometry, dispatch.  No device work happens here
+// until every argument has been checked, so all error paths run without a GPU.
+#include "mbq_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+bool valid_dtype(mbq_dtype t) { return t == MBQ_F32 || t == MBQ_BF16; }
+
+mbq_status check_desc(const mbq_desc* d) {
+  if (!d) return MBQ_ERR_ARG;
+  if (d->abi != MBQ_ABI_VERSION || d->bits != 2) return MBQ_ERR_UNSUPPORTED;
+  mbq_desc ref;
+  mbq_status st = mbq_describe(d->n, d->k, d->group, d->slices, &ref);
+  if (st != MBQ_OK) return st;
+  if (ref.total_bytes != d->total_bytes || ref.slice_stride != d->slice_stride ||
+      ref.params_offset != d->params_offset || ref.row_blocks != d->row_blocks ||
+      ref.k_tiles != d->k_tiles || ref.groups_padded != d->groups_padded)
+    return MBQ_ERR_SHAPE;
+  return MBQ_OK;
+}
+
+mbq_status launched(hipError_t e) {
+  if (e != hipSuccess) return MBQ_ERR_DEVICE;
+  return hipGetLastError() == hipSuccess ? MBQ_OK : MBQ_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mbq_abi_version(void) { return MBQ_ABI_VERSION; }
+
+const char* mbq_status_str(mbq_status s) {
+  switch (s) {
+    case MBQ_OK: return "ok";
+    case MBQ_ERR_ARG: return "invalid argument (NULL or misaligned pointer, unknown dtype)";
+    case MBQ_ERR_SHAPE: return "invalid shape";
+    case MBQ_ERR_RANGE: return "value out of range";
+    case MBQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MBQ_ERR_DEVICE: return "HIP launch failed";
+    case MBQ_ERR_UNSUPPORTED: return "unsupported group, slice count, bit width or ABI version";
+  }
+  return "unknown status";
+}
+
+mbq_status mbq_describe(int32_t n, int32_t k, int32_t group, int32_t slices, mbq_desc* out) {
+  if (!out) return MBQ_ERR_ARG;
+  if (group != 64 && group != 128 && group != 256) return MBQ_ERR_UNSUPPORTED;
+  if (slices < 1 || slices > 4) return MBQ_ERR_UNSUPPORTED;
+  if (n < 1 || k < group || (k % group) != 0) return MBQ_ERR_SHAPE;
+  if (n > (1 << 28) || k > (1 << 28)) return MBQ_ERR_SHAPE;
+  mbq_desc d{};
+  d.abi = MBQ_ABI_VERSION;
+  d.n = n;
+  d.k = k;
+  d.group = group;
+  d.slices = slices;
+  d.bits = 2;
+  d.row_blocks = (n + mbq::kRowBlock - 1) / mbq::kRowBlock;
+  d.k_tiles = (k + mbq::kKTile - 1) / mbq::kKTile;
+  d.groups_padded = d.k_tiles * mbq::kKTile / group;
+  d.codes_bytes = uint64_t(d.row_blocks) * d.k_tiles * mbq::kTileBytes;
+  d.params_bytes = uint64_t(d.row_blocks) * d.groups_padded * 64;
+  d.params_offset = align256(d.codes_bytes);
+  d.slice_stride = d.params_offset + align256(d.params_bytes);
+  d.total_bytes = d.slice_stride * uint64_t(slices);
+  *out = d;
+  return MBQ_OK;
+}
+
+mbq_status mbq_pack(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void* packed,
+                    int32_t* dev_status, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (!valid_dtype(w_dtype) || !w || !packed) return MBQ_ERR_ARG;
+  if (!aligned(packed, 256) || !aligned(w, w_dtype == MBQ_F32 ? 4 : 2)) return MBQ_ERR_ARG;
+  if (dev_status && !aligned(dev_status, 4)) return MBQ_ERR_ARG;
+  return launched(mbq::launch_pack(*desc, w, w_dtype == MBQ_BF16, packed, dev_status, stream));
+}
+
+mbq_status mbq_route(int32_t t, int32_t k, int32_t s, const void* x, mbq_dtype x_dtype,
+                     const float* wr, float* logits, int32_t* budget, int32_t* perm,
+                     int32_t* offsets, hipStream_t stream) {
+  if (s < 1 || s > 4) return MBQ_ERR_UNSUPPORTED;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (!logits || !budget || !perm || !offsets) return MBQ_ERR_ARG;
+  if (x) {
+    if (k < 1) return MBQ_ERR_SHAPE;
+    if (!valid_dtype(x_dtype) || !wr) return MBQ_ERR_ARG;
+    if (!aligned(x, x_dtype == MBQ_F32 ? 4 : 2) || !aligned(wr, 4)) return MBQ_ERR_ARG;
+  }
+  if (!aligned(logits, 4) || !aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4))
+    return MBQ_ERR_ARG;
+  return launched(mbq::launch_route(t, k, s, x, x_dtype == MBQ_BF16, wr, logits, nullptr,
+                                    budget, perm, offsets, stream));
+}
+
+mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* perm,
+                       int32_t* offsets, hipStream_t stream) {
+  if (s < 1 || s > 4) return MBQ_ERR_UNSUPPORTED;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (!budget || !perm || !offsets) return MBQ_ERR_ARG;
+  if (!aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4)) return MBQ_ERR_ARG;
+  return launched(mbq::launch_route(t, 0, s, nullptr, false, nullptr, nullptr, budget,
+                                    nullptr, perm, offsets, stream));
+}
+
+mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
+                                size_t* bytes) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (!bytes || !valid_dtype(x_dtype)) return MBQ_ERR_ARG;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  *bytes = (t >= 1 && t <= 64) ? mbq::decode_workspace(*desc, t, x_dtype == MBQ_BF16) : 0;
+  return MBQ_OK;
+}
+
+mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                      mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
+                      void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
+                      hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
+  if (!packed || !x || !perm || !offsets || !y) return MBQ_ERR_ARG;
+  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(perm, 4) ||
+      !aligned(offsets, 4))
+    return MBQ_ERR_ARG;
+  size_t need = 0;
+  st = mbq_linear_workspace(desc, t, x_dtype, &need);
+  if (st != MBQ_OK) return st;
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
+    return MBQ_ERR_WORKSPACE;
+  if (t == 0) return MBQ_OK;
+  const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16;
+  if (t <= 64)
+    return launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb,
+                                       workspace, stream));
+  return launched(mbq::launch_prefill(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
+}
+
+}  // extern "C"

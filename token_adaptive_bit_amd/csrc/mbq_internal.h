@@ -1,0 +1,50 @@
+// Internal declarations of libmbq: kernel launchers and small device helpers.
+// Everything here is gfx950 (CDNA4, wave64) code; nothing is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/mbq.h"
+
+namespace mbq {
+
+constexpr int kWave = 64;
+constexpr int kRowBlock = 16;    // rows per packed tile
+constexpr int kKTile = 256;      // inputs per packed tile
+constexpr int kTileBytes = 1024; // 16 rows x 256 inputs x 2 bits
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// bfloat16 bits of a float, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float load_x(const void* p, size_t idx, bool is_bf16) {
+  if (is_bf16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p)[idx]);
+  return reinterpret_cast<const float*>(p)[idx];
+}
+
+// Host-side launchers (one per translation unit).
+hipError_t launch_pack(const mbq_desc& d, const void* w, bool w_bf16, void* packed,
+                       int32_t* dev_status, hipStream_t stream);
+hipError_t launch_route(int32_t t, int32_t k, int32_t s, const void* x, bool x_bf16,
+                        const float* wr, float* logits, const int32_t* budget_in,
+                        int32_t* budget, int32_t* perm, int32_t* offsets, hipStream_t stream);
+size_t decode_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
+hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const void* x,
+                         bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
+                         bool y_bf16, void* ws, hipStream_t stream);
+hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, const void* x,
+                          bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
+                          bool y_bf16, hipStream_t stream);
+
+}  // namespace mbq

@@ -1,0 +1,131 @@
+// MoBiSlice pack: recursive 2-bit residual quantization into the slice-major blob.
+//
+// MoBiQuant explainer (gist.science, English), section 2.A: the first slice quantizes W,
+// each later slice quantizes the residual left by the previous ones, and a precision of
+// b slices is the sum of the first b.  The quantizer is the 2-bit asymmetric min/max
+// round-to-nearest reading documented in mbq.h.
+//
+// One wave per packed tile (16 rows x 256 inputs).  Lane l = 16c + r owns row r of the
+// tile and inputs 64i + 16c + e (i = 0..3, e = 0..15): exactly the 64 codes it stores as
+// one 16-byte vector, so the codes of every slice leave the kernel as one coalesced
+// 1 KiB store per wave.  A group of G inputs of one row is spread over the 4 lanes
+// r, r+16, r+32, r+48 (G/64 words each), so its min and max need two cross-lane steps.
+// The residual of all 64 inputs stays in registers across the slices.
+//
+// Bit-exactness: every float32 operation is rounded on its own (this file is built with
+// -ffp-contract=off and uses the _rn intrinsics), division is IEEE, rint rounds half to
+// even and float->half rounds to nearest even with subnormals.
+#include "mbq_internal.h"
+
+namespace mbq {
+namespace {
+
+template <int G, bool BF16>
+__global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, int N, int K,
+                                                  int S, int KB, int NG, uint64_t slice_stride,
+                                                  uint64_t params_offset,
+                                                  uint8_t* __restrict__ packed,
+                                                  int32_t* __restrict__ status) {
+  constexpr int kWordsPerGroup = G / 64;
+  constexpr int kGroupsPerTile = 256 / G;
+  const int kb = blockIdx.x, nb = blockIdx.y;
+  const int lane = threadIdx.x, r = lane & 15, c = lane >> 4;
+  const int n = nb * 16 + r;
+
+  float R[4][16];
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int k = kb * 256 + 64 * i + 16 * c + e;
+      float v = 0.f;
+      if (n < N && k < K) v = load_x(w, size_t(n) * K + k, BF16);
+      if (!__builtin_isfinite(v)) bad |= 1;
+      R[i][e] = v;
+    }
+  }
+
+  for (int j = 0; j < S; ++j) {
+    uint8_t* slice = packed + uint64_t(j) * slice_stride;
+    uint32_t word[4];
+#pragma unroll
+    for (int gi = 0; gi < kGroupsPerTile; ++gi) {
+      float lo = R[gi * kWordsPerGroup][0], hi = lo;
+#pragma unroll
+      for (int ii = 0; ii < kWordsPerGroup; ++ii) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          lo = fminf(lo, R[gi * kWordsPerGroup + ii][e]);
+          hi = fmaxf(hi, R[gi * kWordsPerGroup + ii][e]);
+        }
+      }
+      lo = fminf(lo, __shfl_xor(lo, 16));
+      hi = fmaxf(hi, __shfl_xor(hi, 16));
+      lo = fminf(lo, __shfl_xor(lo, 32));
+      hi = fmaxf(hi, __shfl_xor(hi, 32));
+      lo = __fadd_rn(lo, 0.0f);  // a signed-zero minimum is stored as +0
+      const float span = __fsub_rn(hi, lo);
+      const float step = __fdiv_rn(span, 3.0f);
+      // float -> half rounds to infinity from 65520 on (round to nearest even)
+      if (!(fabsf(step) < 65520.f) || !(fabsf(lo) < 65520.f)) bad |= 2;
+      const __half hs = __float2half_rn(step);
+      const __half hz = __float2half_rn(lo);
+      const float sf = __half2float(hs);
+      const float zf = __half2float(hz);
+#pragma unroll
+      for (int ii = 0; ii < kWordsPerGroup; ++ii) {
+        const int i = gi * kWordsPerGroup + ii;
+        uint32_t wd = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float rv = R[i][e];
+          float q = 0.f;
+          if (sf != 0.f) {
+            const float u = __fdiv_rn(__fsub_rn(rv, zf), sf);
+            q = fminf(fmaxf(rintf(u), 0.f), 3.f);
+          }
+          wd |= uint32_t(q) << (2 * e);
+          const float dq = __fadd_rn(zf, __fmul_rn(q, sf));
+          R[i][e] = __fsub_rn(rv, dq);
+        }
+        word[i] = wd;
+      }
+      if (c == 0) {
+        const uint32_t pv = uint32_t(__half_as_ushort(hs)) | (uint32_t(__half_as_ushort(hz)) << 16);
+        const size_t g = size_t(kb) * kGroupsPerTile + gi;
+        *reinterpret_cast<uint32_t*>(slice + params_offset + ((size_t(nb) * NG + g) * 16 + r) * 4) = pv;
+      }
+    }
+    u32x4_t v = {word[0], word[1], word[2], word[3]};
+    *reinterpret_cast<u32x4_t*>(slice + (size_t(nb) * KB + kb) * kTileBytes + 16 * lane) = v;
+  }
+  if (bad && status) atomicOr(status, bad);
+}
+
+template <int G>
+hipError_t launch_g(const mbq_desc& d, const void* w, bool w_bf16, void* packed,
+                    int32_t* st, hipStream_t stream) {
+  dim3 grid(d.k_tiles, d.row_blocks), block(64);
+  auto* out = static_cast<uint8_t*>(packed);
+  if (w_bf16)
+    hipLaunchKernelGGL((pack_kernel<G, true>), grid, block, 0, stream, w, d.n, d.k, d.slices,
+                       d.k_tiles, d.groups_padded, d.slice_stride, d.params_offset, out, st);
+  else
+    hipLaunchKernelGGL((pack_kernel<G, false>), grid, block, 0, stream, w, d.n, d.k, d.slices,
+                       d.k_tiles, d.groups_padded, d.slice_stride, d.params_offset, out, st);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack(const mbq_desc& d, const void* w, bool w_bf16, void* packed,
+                       int32_t* st, hipStream_t stream) {
+  switch (d.group) {
+    case 64: return launch_g<64>(d, w, w_bf16, packed, st, stream);
+    case 128: return launch_g<128>(d, w, w_bf16, packed, st, stream);
+    default: return launch_g<256>(d, w, w_bf16, packed, st, stream);
+  }
+}
+
+}  // namespace mbq
