@@ -44,6 +44,14 @@ class MbqError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m token_adaptive_bit_amd.build`")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7, and libmbq must
+    # bind to that one (same SONAME) rather than load the system copy next to it, or the
+    # two HSA runtimes fight over the device.  Importing torch first makes the dynamic
+    # linker reuse torch's runtime for libmbq.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, U64, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
     D = P(MbqDesc)

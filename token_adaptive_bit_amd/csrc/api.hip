@@ -1,5 +1,8 @@
 // Host side of the C ABI: validation, geometry, dispatch.  No device work happens here
 // until every argument has been checked, so all error paths run without a GPU.
+#include <cstdio>
+#include <cstdlib>
+
 #include "mbq_internal.h"
 
 namespace {
@@ -23,9 +26,12 @@ mbq_status check_desc(const mbq_desc* d) {
   return MBQ_OK;
 }
 
+// With MBQ_DEBUG set in the environment, a failed launch also prints the HIP error.
 mbq_status launched(hipError_t e) {
-  if (e != hipSuccess) return MBQ_ERR_DEVICE;
-  return hipGetLastError() == hipSuccess ? MBQ_OK : MBQ_ERR_DEVICE;
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e == hipSuccess) return MBQ_OK;
+  if (std::getenv("MBQ_DEBUG")) std::fprintf(stderr, "libmbq: launch failed: %s (%d)\n", hipGetErrorString(e), int(e));
+  return MBQ_ERR_DEVICE;
 }
 
 }  // namespace
