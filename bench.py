@@ -1,0 +1,288 @@
+"""Benchmark of the routed bit-sliced linear on one MI355X.
+
+Prints one JSON line.  A step is one pass of the per-batch hot path on the decode
+workload (Qwen2.5-7B-like up-projection, W 18944 x 3584 bf16 with 0.5% outlier columns,
+G = 128, 3 slices, a batch of 16 bf16 tokens): router logits + argmax + stable regroup
+(mbq_route) and the routed decode linear (mbq_linear).  Packing is an offline, once-per-
+weight step and is timed separately (reported under "extra").
+
+value = tokens / s over the timed steps (inputs resident in HBM).  The roofline object
+is for the dominant kernel (the routed decode GEMV): algorithmic bytes per launch (the
+slices the batch needs, plus activations and outputs) over its average duration measured
+with HIP events on the launch stream inside the timed region.  The packed weight is
+rotated over enough copies (> 512 MiB) that neither L2 nor the 256 MiB Infinity Cache
+can serve a repeat.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed bit-sliced linear: tokens/s + effective weight GB/s (decode), TFLOP/s (prefill)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--tokens", type=int, default=16, help="decode batch (1, 4 or 16)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer"], default=None,
+                    help="run one workload only (for profiling); prints its own JSON line")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def copies_for(nbytes: int) -> int:
+    return max(2, math.ceil(ROTATE_BYTES / nbytes))
+
+
+def make_blobs(api, torch, W, group, slices, dev):
+    p = api.pack(W, group=group, slices=slices)
+    n = copies_for(p.blob.numel())
+    blobs = [p] + [api.PackedLinear(p.desc, p.blob.clone()) for _ in range(n - 1)]
+    torch.cuda.synchronize()
+    return blobs
+
+
+def decode_bytes(p, T, jmax):
+    """Algorithmic bytes of one routed decode launch: needed slices + x + y + routing."""
+    d = p.desc
+    return jmax * int(d.slice_stride) + T * d.k * 2 + T * d.n * 2 + T * 4 + (d.slices + 1) * 4
+
+
+def weight_bytes(p, jmax):
+    return jmax * int(p.desc.slice_stride)
+
+
+def time_events(torch, fn, iters):
+    """Average duration (s) of fn() on the current stream, bracketed by HIP events."""
+    s = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        s[i].record()
+        fn(i)
+        e[i].record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in zip(s, e)) / iters / 1e3
+
+
+def traffic_from_profile(kernel_src: str, name: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = open(os.path.join(ROOT, "token_adaptive_bit_amd", "csrc", kernel_src), "rb").read()
+    if vals.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_decode(api, torch, inputs, T, steps, warmup, dev):
+    d = inputs.make_config(2)
+    W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
+    X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
+    Wr = torch.from_numpy(d["Wr"]).to(dev, torch.float32)
+    blobs = make_blobs(api, torch, W, 128, 3, dev)
+    del W
+    nb = len(blobs)
+    logits = torch.empty((T, 3), dtype=torch.float32, device=dev)
+    budget = torch.empty(T, dtype=torch.int32, device=dev)
+    perm = torch.empty(T, dtype=torch.int32, device=dev)
+    off = torch.empty(4, dtype=torch.int32, device=dev)
+    y = torch.empty((T, d["N"]), dtype=torch.bfloat16, device=dev)
+    ws_n = api.linear_workspace(blobs[0], T)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        api.route(X, Wr, logits, budget, perm, off)
+        api.linear(blobs[i % nb], X, perm, off, y=y, workspace=ws if ws_n else None)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps; events bracket the routed linear of each step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        api.route(X, Wr, logits, budget, perm, off)
+        ev[i][0].record()
+        api.linear(blobs[i % nb], X, perm, off, y=y, workspace=ws if ws_n else None)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lin_s = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    jmax = int((off[:3] < T).sum().item())      # slices with at least one token
+    counts = torch.diff(off).cpu().tolist()
+    return {"T": T, "step_s": (t1 - t0) / steps, "linear_s": lin_s, "jmax": jmax,
+            "budget_counts": counts, "bytes": decode_bytes(blobs[0], T, jmax),
+            "weight_bytes": weight_bytes(blobs[0], jmax), "copies": nb,
+            "blob_bytes": int(blobs[0].blob.numel()), "N": d["N"], "K": d["K"]}
+
+
+def bench_pack(api, torch, inputs, dev):
+    d = inputs.make_config(2)
+    W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
+    out = torch.empty(int(api.describe(d["N"], d["K"], 128, 3).total_bytes), dtype=torch.uint8, device=dev)
+    api.pack(W, 128, 3, out=out)
+    torch.cuda.synchronize()
+    return time_events(torch, lambda i: api.pack(W, 128, 3, out=out), 5)
+
+
+def bench_prefill(api, torch, inputs, dev, iters=20):
+    d = inputs.make_config(3)
+    W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
+    X = torch.from_numpy(d["X"]).to(dev, torch.bfloat16)
+    budget = torch.from_numpy(d["budget"]).to(dev)
+    blobs = make_blobs(api, torch, W, 128, 3, dev)[:4]
+    perm, off = api.regroup(budget, 3)
+    y = torch.empty((d["T"], d["N"]), dtype=torch.bfloat16, device=dev)
+    for i in range(3):
+        api.linear(blobs[i % 4], X, perm, off, y=y)
+    torch.cuda.synchronize()
+    s = time_events(torch, lambda i: api.linear(blobs[i % 4], X, perm, off, y=y), iters)
+    flops = 2.0 * d["T"] * d["N"] * d["K"]
+    return {"T": d["T"], "linear_s": s, "tflops": flops / s / 1e12,
+            "mfma_frac": flops / s / 1e12 / BF16_PEAK_TFLOPS, "budget_counts": torch.diff(off).cpu().tolist()}
+
+
+def bench_copy(torch, dev, nbytes=1 << 30):
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s = time_events(torch, lambda i: b.copy_(a), 10)
+    return 2 * nbytes / s / 1e9
+
+
+def cpu_baseline(inputs, T):
+    """The oracle as it stands, timed on the host on a bounded sample of the same step:
+    route + regroup + routed linear for the same T tokens against a row slice of W."""
+    import numpy as np
+    from oracle import mbq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    d = inputs.make_config(2)
+    rows = 4736                                  # a quarter of the 18944 output rows
+    p = O.pack(d["W"][:rows], 128, 3)
+    X = d["X"][:T]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 128)
+        b = O.route_from_logits(O.router_logits(X, d["Wr"]))
+        O.regroup(b, 3)
+        O.linear(X, deq, b)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    s = (time.perf_counter() - t0) / reps
+    # scale to the full step: the sample is a quarter of the rows
+    full_step_s = s * d["N"] / rows
+    return {"value": T / full_step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} oracle steps (route + regroup + float64 dequant and linear) for "
+                      f"{T} tokens on {rows} of {d['N']} rows, scaled by {d['N'] / rows:.0f}x; "
+                      f"{s:.2f} s per sample step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path.  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from token_adaptive_bit_amd import api, inputs
+    dev = "cuda:0"
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.only == "prefill":
+        r = bench_prefill(api, torch, inputs, dev, iters=max(args.steps, 1))
+        print(json.dumps({"workload": "prefill", **r}))
+        return
+
+    log(f"decode T={args.tokens}: {args.warmup} warmup + {args.steps} timed steps")
+    r = bench_decode(api, torch, inputs, args.tokens, args.steps, args.warmup, dev)
+    achieved = r["bytes"] / r["linear_s"] / 1e9
+    traffic = traffic_from_profile("decode.hip", f"decode_gemv_18944x3584_t{args.tokens}_traffic.txt")
+    out = {
+        "metric": METRIC,
+        "value": args.tokens / r["step_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["step_s"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV 18944x3584 (Qwen2.5-7B-like up-proj), G128, S3, "
+                               f"bf16, T{args.tokens}, router argmax",
+                   "N": r["N"], "K": r["K"], "group": 128, "slices": 3, "tokens": args.tokens,
+                   "budget_counts": r["budget_counts"], "slices_read": r["jmax"],
+                   "weight_copies_rotated": r["copies"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "effective_weight_gbs": r["weight_bytes"] / r["linear_s"] / 1e9,
+        "linear_us": r["linear_s"] * 1e6,
+    }
+    if not args.no_extra and args.only is None:
+        extra = {}
+        for T in (1, 4):
+            if T != args.tokens:
+                log(f"decode T={T}")
+                q = bench_decode(api, torch, inputs, T, 100, 10, dev)
+                extra[f"decode_t{T}"] = {"tokens_per_s": T / q["step_s"], "linear_us": q["linear_s"] * 1e6,
+                                         "slices_read": q["jmax"],
+                                         "hbm_frac": q["bytes"] / q["linear_s"] / 1e9 / HBM_PEAK_GBS,
+                                         "effective_weight_gbs": q["weight_bytes"] / q["linear_s"] / 1e9}
+        log("prefill 11008x4096 T=2048")
+        pf = bench_prefill(api, torch, inputs, dev)
+        extra["prefill_11008x4096_t2048"] = {"tflops": pf["tflops"], "mfma_frac": pf["mfma_frac"],
+                                             "linear_us": pf["linear_s"] * 1e6,
+                                             "budget_counts": pf["budget_counts"]}
+        log("pack")
+        extra["pack_18944x3584_s3_us"] = bench_pack(api, torch, inputs, dev) * 1e6
+        extra["copy_kernel_gbs"] = bench_copy(torch, dev)
+        out["extra"] = extra
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(inputs, args.tokens)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -31,7 +31,8 @@
  *     negative mbq_status and launch nothing.  A failed launch returns MBQ_ERR_DEVICE.
  *   - Alignment: the packed blob 256 bytes, x / y / workspace 16 bytes, others 4 bytes.
  *   - Supported: bits == 2, 1 <= slices <= 4, group in {64, 128, 256}, K % group == 0,
- *     N >= 1, K >= group, T >= 0 (T == 0 launches nothing).
+ *     N >= 1, K >= group, T >= 0.  With T == 0 nothing is launched except that
+ *     mbq_route / mbq_regroup still write offsets; T-sized pointers may then be NULL.
  */
 #ifndef MBQ_H
 #define MBQ_H
@@ -69,7 +70,9 @@ typedef enum { MBQ_F32 = 0, MBQ_BF16 = 1 } mbq_dtype;
  *                                lane l = 16*c + r owns 16 bytes at 16*l = four 32-bit
  *                                little-endian words; word i holds the 2-bit codes of
  *                                row 16*nb + r at inputs 256*kb + 64*i + 16*c + e,
- *                                e = 0..15, code e in bits [2e, 2e+1].
+ *                                e = 0..15; code e in bits [p, p+1] with
+ *                                p = 16*(e & 1) + 2*(e >> 1) (even inputs in the low
+ *                                half-word, odd inputs in the high half-word).
  *     params at +params_offset:  entry (nb, g, r) is 4 bytes at
  *                                ((nb*groups_padded + g)*16 + r)*4: half scale in
  *                                bits 0..15, half zero in bits 16..31.

@@ -198,11 +198,18 @@ def linear(X: np.ndarray, deq: np.ndarray, budget: np.ndarray) -> np.ndarray:
 #   * Codes: tile (nb, kb) is 1024 bytes at (nb*KB + kb)*1024; inside it, lane
 #     l = 16*c + r (r = row in block, c = 0..3) owns 16 bytes at 16*l: four little-endian
 #     32-bit words, word i holding the 16 codes of row 16*nb + r at inputs
-#     k = 256*kb + 64*i + 16*c + e, e = 0..15, code e in bits 2e..2e+1.
+#     k = 256*kb + 64*i + 16*c + e, e = 0..15; code e sits in bits p..p+1 with
+#     p = 16*(e % 2) + 2*(e // 2): even inputs fill the low 16 bits, odd inputs the high
+#     16 bits, two bits each in input order.
 #   * Params: entry (nb, g, r) is 4 bytes at ((nb*NG + g)*16 + r)*4: half scale in the
 #     low 16 bits, half zero in the high 16 bits.
 #   * Padding rows and padding inputs hold code 0 and params (0, 0).
 # ----------------------------------------------------------------------------------------
+def code_bit(e: int) -> int:
+    """Bit position of code e (0..15) inside its 32-bit word."""
+    return 16 * (e % 2) + 2 * (e // 2)
+
+
 def blob_geometry(N: int, K: int, group: int, slices: int) -> dict:
     nb = -(-N // 16)
     kb = -(-K // 256)
@@ -236,7 +243,7 @@ def to_blob(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray, group: int) 
                 c = c16 // 16
                 w = 0
                 for e in range(16):
-                    w |= int(codes[j, n, k0 + e]) << (2 * e)
+                    w |= int(codes[j, n, k0 + e]) << code_bit(e)
                 lane = 16 * c + r
                 off = base + (nb * KB + kb) * 1024 + 16 * lane + 4 * i
                 words[off // 4] = w
@@ -269,7 +276,7 @@ def to_blob_fast(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray, group: 
         c = c.reshape(Np, Kp // 16, 16)
         w = np.zeros((Np, Kp // 16), np.uint32)
         for e in range(16):
-            w |= c[:, :, e] << np.uint32(2 * e)
+            w |= c[:, :, e] << np.uint32(code_bit(e))
         # (nb, r, kb, i, c) -> tile (nb, kb), lane 16c + r, word i
         w = w.reshape(NB, 16, KB, 4, 4)            # nb, r, kb, i, c
         w = w.transpose(0, 2, 4, 1, 3)             # nb, kb, c, r, i
@@ -302,7 +309,7 @@ def from_blob(blob: np.ndarray, N: int, K: int, group: int, slices: int):
                 i, rem2 = divmod(rem, 64)
                 c, e = divmod(rem2, 16)
                 off = base + (nb * KB + kb) * 1024 + 16 * (16 * c + r) + 4 * i
-                codes[j, n, k] = (int(words[off // 4]) >> (2 * e)) & 3
+                codes[j, n, k] = (int(words[off // 4]) >> code_bit(e)) & 3
         pbase = base + geo["params_offset"]
         for n in range(N):
             nb, r = divmod(n, 16)

@@ -285,16 +285,18 @@ def test_blob_word_placement():
     codes[0, 0, 64] = 3           # row 0, k 64: tile 0, lane 0, word 1
     codes[0, 0, 16] = 1           # row 0, k 16: tile 0, lane 16, word 0
     codes[0, 2, 256 + 200] = 3    # row 2, k 456: tile 1, rem 200 = 3*64 + 8 -> lane 2, word 3, e 8
+    codes[0, 5, 3] = 1            # row 5, k 3: lane 5, word 0, odd e 3 -> high half, bits 18-19
     sc = np.zeros((1, N, K // 128), np.float16)
     sc[0, 3, 2] = np.float16(1.0)
     blob = O.to_blob(codes, sc, sc, 128)
     w = blob[:2048].view(np.uint32)
     assert w[0] == 1
-    assert w[4] == 2 << 30
+    assert w[4] == 2 << 30        # e = 15: high half, last slot
     assert w[1] == 3
     assert w[64] == 1             # lane 16 starts at byte 256
-    assert w[256 + 2 * 4 + 3] == 3 << 16
-    assert np.count_nonzero(w) == 5
+    assert w[256 + 2 * 4 + 3] == 3 << 8    # e = 8: low half, slot 4
+    assert w[5 * 4] == 1 << 18
+    assert np.count_nonzero(w) == 6
     geo = O.blob_geometry(N, K, 128, 1)
     h = blob[geo["params_offset"]:].view(np.uint16)
     # (nb 0, g 2, r 3) -> ((0*4 + 2)*16 + 3)*4 bytes = 140 bytes -> halves 70, 71
@@ -302,13 +304,14 @@ def test_blob_word_placement():
 
 
 def test_blob_patterned_words():
-    """codes[n, k] = (n + k) % 4 gives the four repeating byte patterns 0xE4, 0x39, 0x4E, 0x93."""
+    """codes[n, k] = (n + k) % 4: even inputs (low half) and odd inputs (high half) give
+    the repeating half-words 0x8888/0xDDDD, 0xDDDD/0x2222, 0x2222/0x7777, 0x7777/0x8888."""
     N, K = 16, 256
     n, k = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
     codes = ((n + k) % 4).astype(np.uint8)[None]
     sc = np.zeros((1, N, 2), np.float16)
     w = O.to_blob(codes, sc, sc, 128)[:1024].view(np.uint32).reshape(64, 4)
-    pat = [0xE4E4E4E4, 0x39393939, 0x4E4E4E4E, 0x93939393]
+    pat = [0xDDDD8888, 0x2222DDDD, 0x77772222, 0x88887777]
     for lane in range(64):
         assert all(int(x) == pat[(lane % 16) % 4] for x in w[lane])
 

@@ -26,6 +26,7 @@ SOURCES = {
     "pack.hip": ["-ffp-contract=off"],
     "route.hip": [],
     "decode.hip": [],
+    "decode_stream.hip": [],
     "prefill.hip": [],
 }
 

@@ -93,8 +93,9 @@ mbq_status mbq_route(int32_t t, int32_t k, int32_t s, const void* x, mbq_dtype x
                      int32_t* offsets, hipStream_t stream) {
   if (s < 1 || s > 4) return MBQ_ERR_UNSUPPORTED;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
-  if (!logits || !budget || !perm || !offsets) return MBQ_ERR_ARG;
-  if (x) {
+  if (!offsets) return MBQ_ERR_ARG;
+  if (t > 0 && (!logits || !budget || !perm)) return MBQ_ERR_ARG;  // may be NULL when t == 0
+  if (x && t > 0) {
     if (k < 1) return MBQ_ERR_SHAPE;
     if (!valid_dtype(x_dtype) || !wr) return MBQ_ERR_ARG;
     if (!aligned(x, x_dtype == MBQ_F32 ? 4 : 2) || !aligned(wr, 4)) return MBQ_ERR_ARG;
@@ -109,7 +110,7 @@ mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* per
                        int32_t* offsets, hipStream_t stream) {
   if (s < 1 || s > 4) return MBQ_ERR_UNSUPPORTED;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
-  if (!budget || !perm || !offsets) return MBQ_ERR_ARG;
+  if (!offsets || (t > 0 && (!budget || !perm))) return MBQ_ERR_ARG;
   if (!aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4)) return MBQ_ERR_ARG;
   return launched(mbq::launch_route(t, 0, s, nullptr, false, nullptr, nullptr, budget,
                                     nullptr, perm, offsets, stream));
@@ -133,6 +134,7 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
   if (st != MBQ_OK) return st;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
+  if (t == 0) return MBQ_OK;  // nothing to compute; t-sized pointers may be NULL
   if (!packed || !x || !perm || !offsets || !y) return MBQ_ERR_ARG;
   if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(perm, 4) ||
       !aligned(offsets, 4))
@@ -142,8 +144,9 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
   if (st != MBQ_OK) return st;
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
     return MBQ_ERR_WORKSPACE;
-  if (t == 0) return MBQ_OK;
   const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16;
+  if (mbq::decode_stream_supported(*desc, t))
+    return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
   if (t <= 64)
     return launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb,
                                        workspace, stream));

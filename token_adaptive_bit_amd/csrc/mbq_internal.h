@@ -7,6 +7,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/mbq.h"
 
 namespace mbq {
@@ -43,6 +45,10 @@ size_t decode_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
 hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                          bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                          bool y_bf16, void* ws, hipStream_t stream);
+bool decode_stream_supported(const mbq_desc& d, int32_t t);
+hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
+                                bool x_bf16, const int32_t* perm, const int32_t* offsets,
+                                void* y, bool y_bf16, hipStream_t stream);
 hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                           bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                           bool y_bf16, hipStream_t stream);

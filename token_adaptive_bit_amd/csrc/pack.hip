@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
             const float u = __fdiv_rn(__fsub_rn(rv, zf), sf);
             q = fminf(fmaxf(rintf(u), 0.f), 3.f);
           }
-          wd |= uint32_t(q) << (2 * e);
+          wd |= uint32_t(q) << (16 * (e & 1) + 2 * (e >> 1));  // even e: low half, odd e: high half
           const float dq = __fadd_rn(zf, __fmul_rn(q, sf));
           R[i][e] = __fsub_rn(rv, dq);
         }
@@ -99,6 +99,14 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
     }
     u32x4_t v = {word[0], word[1], word[2], word[3]};
     *reinterpret_cast<u32x4_t*>(slice + (size_t(nb) * KB + kb) * kTileBytes + 16 * lane) = v;
+  }
+  // The first wave also clears each slice's alignment gap after its params, so that the
+  // whole blob is defined.
+  if (kb == 0 && nb == 0) {
+    const uint64_t used = params_offset + uint64_t(gridDim.y) * NG * 64;
+    for (int j = 0; j < S; ++j)
+      for (uint64_t off = used + 4 * lane; off < slice_stride; off += 256)
+        *reinterpret_cast<uint32_t*>(packed + uint64_t(j) * slice_stride + off) = 0u;
   }
   if (bad && status) atomicOr(status, bad);
 }

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             const float s = __half2float(__ushort_as_half(uint16_t(pv & 0xFFFFu)));
             const float z = __half2float(__ushort_as_half(uint16_t(pv >> 16)));
 #pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] += fmaf(s, float((w >> (2 * e)) & 3u), z);
+            for (int e = 0; e < 16; ++e) v[e] += fmaf(s, float((w >> (16 * (e & 1) + 2 * (e >> 1))) & 3u), z);
           }
         }
         uint32_t pk[8];

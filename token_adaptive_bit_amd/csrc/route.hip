@@ -6,32 +6,99 @@
 // largest logit.  Tokens are then regrouped by a stable ascending sort on b(t) so that
 // the linear kernels see runs of tokens with one budget (the pages leave the regroup
 // open; the English page, section 5, names irregular access as the cost it avoids).
+//
+// The logits kernel runs one workgroup per token (coalesced loads, fixed-order sums, so
+// logits and routes are identical from run to run).  The sort runs in one wave with
+// ballot ranks for T <= 64 (decode) and in one 1024-thread workgroup otherwise.
 #include "mbq_internal.h"
 
 namespace mbq {
 namespace {
 
-// One wave per token: lanes stride over K, then a butterfly sum.  Deterministic.
+constexpr int kSmallT = 64;
+
+// sum over the wave, fixed butterfly order
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Partial dot products of one token row against Wr: thread i takes inputs i, i + stride,
+// ...; consecutive threads read consecutive activations and consecutive Wr rows, so every
+// load instruction is coalesced.
 template <bool BF16>
-__global__ __launch_bounds__(256) void logits_kernel(const void* __restrict__ x, int T, int K,
+__device__ __forceinline__ void dot_row(const void* __restrict__ x, size_t row, int K, int S,
+                                        const float* __restrict__ wr, int i0, int stride,
+                                        float (&acc)[4]) {
+  constexpr int U = 8;  // independent loads in flight per thread
+  for (int k0 = i0; k0 < K; k0 += U * stride) {
+    float xk[U], w[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u * stride;
+      const bool in = k < K;
+      xk[u] = in ? load_x(x, row * K + k, BF16) : 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) w[u][s] = (in && s < S) ? wr[size_t(k) * S + s] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[s] = fmaf(xk[u], w[u][s], acc[s]);
+  }
+}
+
+__device__ __forceinline__ int argmax_first(const float* l, int S) {
+  float best = l[0];
+  int arg = 0;
+  for (int j = 1; j < S; ++j)
+    if (l[j] > best) { best = l[j]; arg = j; }
+  return arg + 1;
+}
+
+// T <= 64: budgets, perm and offsets from the logits in one wave (ballot ranks).
+__global__ __launch_bounds__(64) void route_small_kernel(int T, int S, const float* __restrict__ logits,
+                                                         int32_t* __restrict__ budget,
+                                                         int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ offsets) {
+  const int lane = threadIdx.x;
+  const int b = lane < T ? argmax_first(logits + size_t(lane) * S, S) : 0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int base = 0, pos = 0;
+  if (lane == 0) offsets[0] = 0;
+  for (int v = 1; v <= S; ++v) {
+    const uint64_t m = __ballot(b == v);
+    if (b == v) pos = base + __popcll(m & lt);
+    base += __popcll(m);
+    if (lane == 0) offsets[v] = base;
+  }
+  if (lane < T) {
+    perm[pos] = lane;
+    budget[lane] = b;
+  }
+}
+
+// One workgroup (512 threads) per token.
+template <bool BF16>
+__global__ __launch_bounds__(512) void logits_kernel(const void* __restrict__ x, int T, int K,
                                                      int S, const float* __restrict__ wr,
                                                      float* __restrict__ logits) {
-  const int t = blockIdx.x * 4 + threadIdx.x / 64;
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;  // whole waves exit together
+  __shared__ float part[8][4];
+  const int t = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k = lane; k < K; k += 64) {
-    const float xv = load_x(x, size_t(t) * K + k, BF16);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      if (s < S) acc[s] = fmaf(xv, wr[size_t(k) * S + s], acc[s]);
-  }
+  dot_row<BF16>(x, size_t(t), K, S, wr, threadIdx.x, 512, acc);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    float v = acc[s];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if (s < S && lane == 0) logits[size_t(t) * S + s] = v;
+    const float v = wave_sum(acc[s]);
+    if (lane == 0) part[wave][s] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < S) {
+    const int s = threadIdx.x;
+    logits[size_t(t) * S + s] = ((part[0][s] + part[1][s]) + (part[2][s] + part[3][s])) +
+                                ((part[4][s] + part[5][s]) + (part[6][s] + part[7][s]));
   }
 }
 
@@ -52,12 +119,7 @@ __global__ __launch_bounds__(1024) void route_kernel(int T, int S, const float* 
       int b = budget_in[t];
       return b < 1 ? 1 : (b > S ? S : b);  // out-of-contract values are clamped, never used as addresses
     }
-    const float* l = logits + size_t(t) * S;
-    float best = l[0];
-    int arg = 0;
-    for (int j = 1; j < S; ++j)
-      if (l[j] > best) { best = l[j]; arg = j; }
-    return arg + 1;
+    return argmax_first(logits + size_t(t) * S, S);
   };
 
   if (tid < 5) cnt[tid] = 0;
@@ -109,16 +171,19 @@ hipError_t launch_route(int32_t t, int32_t k, int32_t s, const void* x, bool x_b
                         const float* wr, float* logits, const int32_t* budget_in,
                         int32_t* budget, int32_t* perm, int32_t* offsets, hipStream_t stream) {
   if (x && t > 0) {
-    dim3 grid((t + 3) / 4), block(256);
     if (x_bf16)
-      hipLaunchKernelGGL(logits_kernel<true>, grid, block, 0, stream, x, t, k, s, wr, logits);
+      hipLaunchKernelGGL(logits_kernel<true>, dim3(t), dim3(512), 0, stream, x, t, k, s, wr, logits);
     else
-      hipLaunchKernelGGL(logits_kernel<false>, grid, block, 0, stream, x, t, k, s, wr, logits);
+      hipLaunchKernelGGL(logits_kernel<false>, dim3(t), dim3(512), 0, stream, x, t, k, s, wr, logits);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, stream, t, s,
-                     budget_in ? nullptr : logits, budget_in, budget, perm, offsets);
+  if (!budget_in && t <= kSmallT)
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(64), 0, stream, t, s, logits, budget,
+                       perm, offsets);
+  else
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, stream, t, s,
+                       budget_in ? nullptr : logits, budget_in, budget, perm, offsets);
   return hipGetLastError();
 }
 
