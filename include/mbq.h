@@ -132,7 +132,9 @@ mbq_status mbq_route(int32_t t, int32_t k, int32_t s, const void* x, mbq_dtype x
 mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* perm,
                        int32_t* offsets, hipStream_t stream);
 
-/* Host only: bytes of device workspace mbq_linear needs for t tokens (may be 0). */
+/* Host only: bytes of device workspace mbq_linear needs for t tokens.  Every kernel of
+ * this version works without scratch memory, so this reports 0; callers that pass the
+ * reported size stay correct if a later version needs some. */
 mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                 size_t* bytes);
 
