@@ -207,6 +207,14 @@ LINEAR_CASES = [
     (130, 768, 256, 4, 200, "bf16", "mix"),
     (96, 512, 64, 2, 129, "f32", "mix"),
     (64, 256, 64, 3, 100, "bf16", "all1"),
+    # MFMA prefill edges: one chunk of 64 inputs, odd chunk counts, several token tiles
+    # per budget group, four slices at group 64, float32 activations over several tiles
+    (40, 64, 64, 2, 70, "bf16", "mix"),
+    (300, 192, 64, 3, 90, "bf16", "mix"),
+    (272, 320, 64, 4, 700, "bf16", "mix"),
+    (17, 448, 64, 1, 600, "bf16", "allS"),
+    (520, 512, 128, 3, 530, "bf16", "all1"),
+    (130, 640, 128, 4, 333, "f32", "mix"),
 ]
 
 
@@ -238,6 +246,34 @@ def test_linear_fp32_output_from_bf16(mbq):
     d = inputs.make_linear(5, 160, 512, 12, dtype="bf16")
     yg, yref, _ = run_linear(mbq, d, budgets_for("mix", 12, 3, 1), out_dtype=torch.float32)
     assert token_errors(yg, yref).max() <= 1e-4
+
+
+def test_prefill_fp32_output(mbq):
+    d = inputs.make_linear(6, 300, 512, 150, dtype="bf16")
+    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", 150, 3, 2), out_dtype=torch.float32)
+    assert token_errors(yg, yref).max() <= TOL
+
+
+def test_prefill_generic_kernel(mbq, monkeypatch):
+    """The plain LDS prefill kernel (kept for activations or slices of 4 GiB and more)."""
+    monkeypatch.setenv("MBQ_GENERIC_PREFILL", "1")
+    d = inputs.make_linear(7, 200, 640, 300, dtype="bf16", n_outliers=2, outlier_scale=10.0)
+    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", 300, 3, 3))
+    assert token_errors(yg, yref).max() <= TOL
+
+
+@pytest.mark.parametrize("T", [16, 200])
+def test_linear_subnormal_scales(mbq, T):
+    """Weights ~1e-5: the residual slices' float16 scales are subnormal and must count."""
+    d = inputs.make_linear(8, 128, 512, T, dtype="bf16")
+    d = dict(d, W=inputs.round_bf16(d["W"] * np.float32(1e-3)))
+    p, _ = gpu_pack(mbq, d["W"], 128, 3, "bf16")
+    s = O.pack(d["W"], 128, 3)["scale"]
+    assert np.any((s[2] > 0) & (s[2] < np.float32(6.1e-5)))   # subnormal scales present
+    yg, yref, _ = run_linear(mbq, d, budgets_for("allS", T, 3, 0), out_dtype=torch.float32)
+    err = token_errors(yg, yref)
+    say(f"  subnormal scales T={T}: max token error {err.max():.3e}")
+    assert err.max() <= TOL
 
 
 def test_linear_deterministic(mbq):

@@ -28,6 +28,7 @@ SOURCES = {
     "decode.hip": [],
     "decode_stream.hip": [],
     "prefill.hip": [],
+    "prefill_mfma.hip": [],
 }
 
 COMMON = [

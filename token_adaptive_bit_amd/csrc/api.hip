@@ -150,6 +150,10 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
   if (t <= 64)
     return launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb,
                                        workspace, stream));
+  // MBQ_GENERIC_PREFILL forces the plain LDS kernel (kept for activations of 4 GiB and more
+  // or slices of 4 GiB and more, which the MFMA kernel's 32-bit buffer offsets cannot reach)
+  if (mbq::prefill_mfma_supported(*desc, t, x, xb) && !std::getenv("MBQ_GENERIC_PREFILL"))
+    return launched(mbq::launch_prefill_mfma(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
   return launched(mbq::launch_prefill(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
 }
 

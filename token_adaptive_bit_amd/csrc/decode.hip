@@ -267,7 +267,8 @@ __global__ __launch_bounds__(512) void decode_kernel(
   for (int tb = 0; tb < TB; ++tb) {
     const int p = 16 * tb + r;
     xlive[tb] = p < T;
-    const int src = xlive[tb] ? perm[p] : 0;
+    const int pp = xlive[tb] ? perm[p] : 0;
+    const int src = (pp >= 0 && pp < T) ? pp : 0;  // out-of-contract entries never address memory
     xrow[tb] = static_cast<const char*>(x) + size_t(src) * K * (XF32 ? 4 : 2);
   }
 
@@ -321,8 +322,9 @@ __global__ __launch_bounds__(512) void decode_kernel(
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int p = 16 * tb + 4 * (ln >> 4) + v;
-      if (p < T && n < N) {
-        const size_t idx = size_t(perm[p]) * N + n;
+      const int tok = p < T ? perm[p] : -1;
+      if (tok >= 0 && tok < T && n < N) {
+        const size_t idx = size_t(tok) * N + n;
         if (y_bf16)
           reinterpret_cast<uint16_t*>(y)[idx] = uint16_t(bf16_bits_rne(o[v]));
         else

@@ -52,5 +52,9 @@ hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t
 hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                           bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                           bool y_bf16, hipStream_t stream);
+bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_bf16);
+hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t, const void* x,
+                               bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
+                               bool y_bf16, hipStream_t stream);
 
 }  // namespace mbq

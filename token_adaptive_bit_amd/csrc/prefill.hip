@@ -36,7 +36,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   // Which budget group and which tokens this M tile covers.
   int m = blockIdx.y, b = 0, start = 0, rows = 0;
   for (int bb = 1; bb <= S; ++bb) {
-    const int lo = offsets[bb - 1], hi = offsets[bb];
+    // offsets out of contract are clamped into [0, T] so no tile reaches past perm
+    const int lo = min(max(offsets[bb - 1], 0), T), hi = min(max(offsets[bb], lo), T);
     const int nt = (hi - lo + BM - 1) / BM;
     if (m < nt) {
       b = bb;
@@ -54,7 +55,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
   // A staging: thread -> (row tid/2, 32 inputs at 32*(tid%2))
   const int arow = tid >> 1, acol = (tid & 1) * 32;
-  const int src = arow < rows ? perm[start + arow] : -1;
+  const int pa = arow < rows ? perm[start + arow] : -1;
+  const int src = (pa >= 0 && pa < T) ? pa : -1;
   // B staging: thread -> row block tid/32 of the tile, tile lanes 2*(tid%32) + {0, 1}
   const int brb = tid >> 5;
   const int bnb = n0 / 16 + brb;
@@ -151,7 +153,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int v = 0; v < 4; ++v) {
       const int row = 64 * wm + 16 * mi + 4 * (lane >> 4) + v;
       if (row >= rows) continue;
-      const size_t ybase = size_t(perm[start + row]) * N;
+      const int tok = perm[start + row];
+      if (tok < 0 || tok >= T) continue;
+      const size_t ybase = size_t(tok) * N;
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
         const int n = n0 + 64 * wn + 16 * ni + (lane & 15);
