@@ -40,8 +40,10 @@ def parse():
     ap.add_argument("--tokens", type=int, default=16, help="decode batch (1, 4 or 16)")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer"], default=None,
-                    help="run one workload only (for profiling); prints its own JSON line")
+    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer", "traffic"], default=None,
+                    help="run one workload only (for profiling); prints its own JSON line.  "
+                         "'traffic' runs a copy kernel of known size and then the decode linear, "
+                         "for the FETCH_SIZE / WRITE_SIZE counter passes")
     return ap.parse_args()
 
 
@@ -180,6 +182,95 @@ def bench_copy(torch, dev, nbytes=1 << 30):
     return 2 * nbytes / s / 1e9
 
 
+def bench_sweep(api, torch, inputs, dev, iters=20):
+    """Elasticity sweep, W 14336 x 4096: T in {32, 1024}, budgets forced to 1, 2, 3 and
+    router-mixed; bytes of weight read and throughput for each."""
+    d = inputs.make_config(5)
+    W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
+    blobs = make_blobs(api, torch, W, 128, 3, dev)
+    del W
+    nb = len(blobs)
+    Wr = torch.from_numpy(d["Wr"]).to(dev, torch.float32)
+    out = {}
+    for T in (32, 1024):
+        X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
+        y = torch.empty((T, d["N"]), dtype=torch.bfloat16, device=dev)
+        for mode in ("b1", "b2", "b3", "router"):
+            if mode == "router":
+                _, _, perm, off = api.route(X, Wr)
+            else:
+                perm, off = api.regroup(torch.full((T,), int(mode[1]), dtype=torch.int32, device=dev), 3)
+            for i in range(3):
+                api.linear(blobs[i % nb], X, perm, off, y=y)
+            torch.cuda.synchronize()
+            s = time_events(torch, lambda i: api.linear(blobs[i % nb], X, perm, off, y=y), iters)
+            counts = torch.diff(off).cpu().tolist()
+            jmax = max(j + 1 for j in range(3) if counts[j] > 0)
+            r = {"us": s * 1e6, "tokens_per_s": T / s, "budget_counts": counts,
+                 "weight_bytes_read": weight_bytes(blobs[0], jmax)}
+            if T <= 64:
+                r["hbm_frac"] = decode_bytes(blobs[0], T, jmax) / s / 1e9 / HBM_PEAK_GBS
+            else:
+                r["tflops"] = 2.0 * T * d["N"] * d["K"] / s / 1e12
+            out[f"t{T}_{mode}"] = r
+    return out
+
+
+def bench_layer(api, torch, inputs, dev, iters=20):
+    """Seven linears of a 14B-like decoder layer at T = 64 with one router on the layer
+    input: total time of route + 7 routed linears, and HBM fraction of the linears."""
+    cfg = inputs.make_config(4)
+    T = cfg["T"]
+    x0 = torch.from_numpy(cfg["X_layer"]).to(dev, torch.bfloat16)
+    Wr = torch.from_numpy(cfg["Wr"]).to(dev, torch.float32)
+    packs, xs, ys = [], [], []
+    for lin in cfg["linears"]:
+        W = torch.from_numpy(lin["W"]).to(dev, torch.bfloat16)
+        packs.append(api.pack(W, 128, 3))
+        xs.append(torch.from_numpy(lin["X"]).to(dev, torch.bfloat16))
+        ys.append(torch.empty((T, W.shape[0]), dtype=torch.bfloat16, device=dev))
+        del W
+    torch.cuda.synchronize()
+    _, _, perm, off = api.route(x0, Wr)
+
+    def step(i):
+        api.route(x0, Wr, perm=perm, offsets=off)
+        for p, x, y in zip(packs, xs, ys):
+            api.linear(p, x, perm, off, y=y)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    s = time_events(torch, step, iters)
+    counts = torch.diff(off).cpu().tolist()
+    jmax = max(j + 1 for j in range(3) if counts[j] > 0)
+    nbytes = sum(decode_bytes(p, T, jmax) for p in packs)
+    return {"T": T, "us": s * 1e6, "tokens_per_s": T / s, "budget_counts": counts,
+            "hbm_frac_incl_route": nbytes / s / 1e9 / HBM_PEAK_GBS,
+            "note": "weights are not rotated: the 7 packed linears (267 MB) exceed the 256 MiB cache"}
+
+
+def run_traffic(api, torch, inputs, dev, T, launches=20):
+    """For the counter passes: 3 copies of 1 GiB (known bytes), then `launches` decode
+    linears over rotated weight copies."""
+    bench_copy(torch, dev)
+    d = inputs.make_config(2)
+    W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
+    X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
+    Wr = torch.from_numpy(d["Wr"]).to(dev, torch.float32)
+    blobs = make_blobs(api, torch, W, 128, 3, dev)
+    del W
+    _, _, perm, off = api.route(X, Wr)
+    y = torch.empty((T, d["N"]), dtype=torch.bfloat16, device=dev)
+    for i in range(launches):
+        api.linear(blobs[i % len(blobs)], X, perm, off, y=y)
+    torch.cuda.synchronize()
+    counts = torch.diff(off).cpu().tolist()
+    jmax = max(j + 1 for j in range(3) if counts[j] > 0)
+    return {"workload": "traffic", "copy_bytes": 2 * (1 << 30), "decode_bytes": decode_bytes(blobs[0], T, jmax),
+            "launches": launches}
+
+
 def cpu_baseline(inputs, T):
     """The oracle as it stands, timed on the host on a bounded sample of the same step:
     route + regroup + routed linear for the same T tokens against a row slice of W."""
@@ -230,11 +321,20 @@ def main():
         r = bench_prefill(api, torch, inputs, dev, iters=max(args.steps, 1))
         print(json.dumps({"workload": "prefill", **r}))
         return
+    if args.only == "sweep":
+        print(json.dumps({"workload": "sweep", **bench_sweep(api, torch, inputs, dev)}))
+        return
+    if args.only == "layer":
+        print(json.dumps({"workload": "layer", **bench_layer(api, torch, inputs, dev)}))
+        return
+    if args.only == "traffic":
+        print(json.dumps(run_traffic(api, torch, inputs, dev, args.tokens, launches=max(args.steps, 1))))
+        return
 
     log(f"decode T={args.tokens}: {args.warmup} warmup + {args.steps} timed steps")
     r = bench_decode(api, torch, inputs, args.tokens, args.steps, args.warmup, dev)
     achieved = r["bytes"] / r["linear_s"] / 1e9
-    traffic = traffic_from_profile("decode.hip", f"decode_gemv_18944x3584_t{args.tokens}_traffic.txt")
+    traffic = traffic_from_profile("decode_stream.hip", f"decode_stream_18944x3584_t{args.tokens}_traffic.txt")
     out = {
         "metric": METRIC,
         "value": args.tokens / r["step_s"],
@@ -259,7 +359,7 @@ def main():
         "effective_weight_gbs": r["weight_bytes"] / r["linear_s"] / 1e9,
         "linear_us": r["linear_s"] * 1e6,
     }
-    if not args.no_extra and args.only is None:
+    if not args.no_extra and args.only is None:  # (--only decode prints the headline line alone)
         extra = {}
         for T in (1, 4):
             if T != args.tokens:
@@ -273,7 +373,13 @@ def main():
         pf = bench_prefill(api, torch, inputs, dev)
         extra["prefill_11008x4096_t2048"] = {"tflops": pf["tflops"], "mfma_frac": pf["mfma_frac"],
                                              "linear_us": pf["linear_s"] * 1e6,
-                                             "budget_counts": pf["budget_counts"]}
+                                             "budget_counts": pf["budget_counts"],
+                                             "hbm_traffic_bytes": traffic_from_profile(
+                                                 "prefill_mfma.hip", "prefill_mfma_11008x4096_t2048_traffic.txt")}
+        log("elasticity sweep 14336x4096")
+        extra["sweep_14336x4096"] = bench_sweep(api, torch, inputs, dev)
+        log("14B-like layer, T=64")
+        extra["layer14b_t64"] = bench_layer(api, torch, inputs, dev)
         log("pack")
         extra["pack_18944x3584_s3_us"] = bench_pack(api, torch, inputs, dev) * 1e6
         extra["copy_kernel_gbs"] = bench_copy(torch, dev)
