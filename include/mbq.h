@@ -151,8 +151,10 @@ mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dty
  *            is written.  Accumulation is float32; bfloat16 output is rounded once.
  *   workspace: at least mbq_linear_workspace() bytes; contents are scratch.
  * Decode (t <= 64) runs a streaming kernel that reads each needed slice once; prefill
- * (t > 64) dequantizes the summed slices to bfloat16 in LDS and runs an MFMA GEMM per
- * budget group.
+ * (t > 64) runs an MFMA GEMM over tiles of one budget group each: the summed slices are
+ * dequantized to bfloat16 MFMA operands once per 256-token tile and shared between the
+ * two waves of a SIMD through LDS.  Rows whose perm entry is outside [0, t) are not
+ * written; offsets outside [0, t] are clamped (no access outside x, y, perm).
  */
 mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                       mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
