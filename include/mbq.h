@@ -132,9 +132,11 @@ mbq_status mbq_route(int32_t t, int32_t k, int32_t s, const void* x, mbq_dtype x
 mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* perm,
                        int32_t* offsets, hipStream_t stream);
 
-/* Host only: bytes of device workspace mbq_linear needs for t tokens.  Every kernel of
- * this version works without scratch memory, so this reports 0; callers that pass the
- * reported size stay correct if a later version needs some. */
+/* Host only: bytes of device workspace mbq_linear needs for t tokens (0 when none).
+ * Decode (1 <= t <= 64) over more k tiles of 256 inputs than one workgroup holds (8 waves
+ * of 1 or 2 tiles each, 2 when the group / slices / x dtype variant fits its registers)
+ * splits K into c equal chunks and needs c * t * n * 4 bytes of float32 partials;
+ * prefill needs none.  The size depends only on desc, t and x_dtype. */
 mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                 size_t* bytes);
 
@@ -149,8 +151,12 @@ mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dty
  *            budget b with offsets[b-1] <= i < offsets[b]).
  *   y:       [t x n] row-major, float32 or bfloat16, original token order; every element
  *            is written.  Accumulation is float32; bfloat16 output is rounded once.
- *   workspace: at least mbq_linear_workspace() bytes; contents are scratch.
- * Decode (t <= 64) runs a streaming kernel that reads each needed slice once; prefill
+ *   workspace: at least mbq_linear_workspace() bytes (16-byte aligned; may be NULL when
+ *            that is 0); contents are scratch, overwritten by every call that uses it, so
+ *            calls that overlap in time must not share one.
+ * Decode (t <= 64) runs a streaming kernel that reads each needed slice once (a slice no
+ * token uses is not read at all), in 16-token blocks, with K split into chunks whose
+ * partials a second small kernel sums in a fixed order when K is long; prefill
  * (t > 64) runs an MFMA GEMM over tiles of one budget group each: the summed slices are
  * dequantized to bfloat16 MFMA operands once per 256-token tile and shared between the
  * two waves of a SIMD through LDS.  Rows whose perm entry is outside [0, t) are not

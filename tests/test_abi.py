@@ -110,7 +110,7 @@ def test_linear_validation_and_workspace():
     dp = ctypes.byref(d)
     f = P(FAKE)
     n = ctypes.c_size_t(123)
-    # no kernel of this library needs device scratch today: the query reports 0 bytes
+    # K = 640 fits one workgroup (3 k tiles): no k split, no scratch; prefill needs none
     for t, dt in ((16, BF16), (16, F32), (64, BF16), (1000, BF16), (0, F32)):
         assert L.mbq_linear_workspace(dp, t, dt, ctypes.byref(n)) == OK and n.value == 0
     assert L.mbq_linear_workspace(dp, -1, BF16, ctypes.byref(n)) == SHAPE
@@ -135,3 +135,26 @@ def test_linear_validation_and_workspace():
     assert call(args(desc=ctypes.byref(bad))) == SHAPE
     # nothing to do: every t-sized pointer may be NULL and nothing is launched
     assert call(args(t=0, x=None, perm=None, off=None, y=None, packed=None)) == OK
+
+
+@pytest.mark.parametrize("N,K,G,S,t,dt,chunks", [
+    (18944, 3584, 128, 3, 16, BF16, 1),   # 14 k tiles: two per wave, one workgroup
+    (18944, 3584, 128, 3, 16, F32, 2),    # float32 activations: one tile per wave, 7 + 7
+    (5120, 5120, 128, 3, 64, BF16, 2),    # 20 tiles: 10 + 10
+    (5120, 13824, 128, 3, 64, BF16, 4),   # 54 tiles: 14 + 14 + 14 + 12
+    (150, 2304, 64, 4, 48, F32, 2),       # 9 tiles, one per wave: 5 + 4
+    (150, 2304, 64, 1, 48, BF16, 1),      # 9 tiles, two per wave
+    (5120, 13824, 128, 3, 65, BF16, 0),   # prefill: no workspace
+])
+def test_decode_split_k_workspace(N, K, G, S, t, dt, chunks):
+    """Decode over more k tiles than one workgroup holds (8 waves x 1 or 2 tiles) splits K
+    into equal chunks whose float32 partials [chunks, t, N] live in the workspace."""
+    st, d = desc(N, K, G, S)
+    assert st == OK
+    n = ctypes.c_size_t(123)
+    assert L.mbq_linear_workspace(ctypes.byref(d), t, dt, ctypes.byref(n)) == OK
+    assert n.value == (chunks * t * N * 4 if chunks > 1 else 0)
+    if chunks > 1:  # a missing or short workspace is refused before any launch
+        f = P(FAKE)
+        for ws, wsb in ((None, 0), (f, n.value - 1)):
+            assert L.mbq_linear(ctypes.byref(d), f, t, f, dt, f, f, f, BF16, ws, wsb, None) == WS

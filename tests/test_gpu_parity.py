@@ -201,6 +201,15 @@ LINEAR_CASES = [
     (96, 512, 64, 3, 64, "bf16", "all1"),
     (96, 512, 64, 3, 40, "bf16", "allS"),
     (77, 384, 128, 1, 9, "f32", "allS"),
+    # streaming decode with several 16-token blocks: 16 k tiles (two per wave), float32
+    # activations (split into two bf16 operands), four slices at group 64
+    (100, 4096, 128, 3, 64, "bf16", "mix"),
+    (200, 640, 128, 3, 50, "f32", "mix"),
+    (150, 2304, 64, 4, 48, "f32", "mix"),
+    # decode with K split over several workgroups (float32 partials in the workspace)
+    (100, 5120, 128, 3, 64, "bf16", "mix"),
+    (60, 13824, 128, 3, 20, "bf16", "mix"),
+    (70, 2560, 64, 3, 7, "bf16", "allS"),
     (200, 640, 128, 3, 65, "bf16", "mix"),      # smallest prefill
     (200, 640, 128, 3, 300, "bf16", "mix"),
     (300, 1024, 128, 3, 257, "bf16", "router"),
@@ -262,6 +271,16 @@ def test_prefill_generic_kernel(mbq, monkeypatch):
     assert token_errors(yg, yref).max() <= TOL
 
 
+@pytest.mark.parametrize("T,K,dtype", [(16, 640, "bf16"), (40, 5120, "bf16"), (9, 2304, "f32")])
+def test_decode_generic_kernel(mbq, monkeypatch, T, K, dtype):
+    """The generic decode kernel (kept for slices of 4 GiB and more) against the oracle."""
+    monkeypatch.setenv("MBQ_GENERIC_DECODE", "1")
+    say(f"generic decode N=120 K={K} T={T} {dtype}")
+    d = inputs.make_linear(7 + T, 120, K, T, group=128, slices=3, dtype=dtype)
+    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", T, 3, T))
+    assert token_errors(yg, yref).max() <= TOL
+
+
 @pytest.mark.parametrize("T", [16, 200])
 def test_linear_subnormal_scales(mbq, T):
     """Weights ~1e-5: the residual slices' float16 scales are subnormal and must count."""
@@ -305,7 +324,7 @@ def sample_rows(N, seed, k=48):
     return np.unique(np.concatenate([rng.choice(N, k, replace=False), [0, N - 1]]))
 
 
-@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("T", [1, 4, 16, 17, 64])
 def test_full_decode_workload(mbq, T):
     say(f"full decode 18944x3584 T={T}")
     d = inputs.make_config(2)

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -31,6 +32,12 @@ SOURCES = {
     "prefill_mfma.hip": [],
 }
 
+# Translation units whose kernels must not spill registers: their load pipelines rely on
+# exact waits on the in-order memory counter, which spill traffic (scratch loads and
+# stores) would stall, and the variants a launcher can pick are chosen to fit.  The build
+# reads the compiler's resource-usage remarks and fails on any spill to scratch memory.
+SPILL_FREE = ("decode_stream.hip", "prefill_mfma.hip")
+
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -47,14 +54,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmbq)")
 
 
+def _spills(remarks: str) -> list:
+    """(kernel, vgpr spills, sgpr spills, scratch bytes) of every kernel that spills to memory."""
+    out, name = [], None
+    vals = {}
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name, vals = m.group(1), {}
+            continue
+        for key in ("VGPRs Spill", "SGPRs Spill", "ScratchSize \\[bytes/lane\\]"):
+            m = re.search(" " + key + r": (\d+)", line)
+            if m:
+                vals[key[:5]] = int(m.group(1))
+        if name and len(vals) == 3:
+            if vals["VGPRs"] or vals["Scrat"]:  # SGPR spills into VGPR lanes touch no memory
+                out.append((name, vals["VGPRs"], vals["SGPRs"], vals["Scrat"]))
+            name = None
+    return out
+
+
 def _compile(src: str, extra: list, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-    cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    check = src in SPILL_FREE
+    remarks = ["-Rpass-analysis=kernel-resource-usage"] if check else []
+    cmd = [hipcc(), *COMMON, *extra, *remarks, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+    if check:
+        bad = _spills(res.stderr)
+        if bad:
+            lines = "\n".join(f"  {n}: {v} VGPR / {s} SGPR spills, {b} B scratch" for n, v, s, b in bad)
+            raise RuntimeError(f"{src}: kernels spill registers:\n{lines}")
     return obj
 
 

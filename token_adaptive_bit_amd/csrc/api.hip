@@ -122,7 +122,13 @@ mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dty
   if (st != MBQ_OK) return st;
   if (!bytes || !valid_dtype(x_dtype)) return MBQ_ERR_ARG;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
-  *bytes = (t >= 1 && t <= 64) ? mbq::decode_workspace(*desc, t, x_dtype == MBQ_BF16) : 0;
+  const bool xb = x_dtype == MBQ_BF16;
+  *bytes = 0;
+  if (t >= 1 && t <= 64) {  // enough for either decode kernel
+    *bytes = mbq::decode_workspace(*desc, t, xb);
+    if (mbq::decode_stream_supported(*desc, t))
+      *bytes = std::max(*bytes, mbq::decode_stream_workspace(*desc, t, xb));
+  }
   return MBQ_OK;
 }
 
@@ -145,8 +151,11 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
     return MBQ_ERR_WORKSPACE;
   const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16;
-  if (mbq::decode_stream_supported(*desc, t))
-    return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
+  // MBQ_GENERIC_DECODE forces the generic decode kernel (kept for slices of 4 GiB and more,
+  // which the streaming kernel's 32-bit buffer offsets cannot reach)
+  if (mbq::decode_stream_supported(*desc, t) && !std::getenv("MBQ_GENERIC_DECODE"))
+    return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb,
+                                              workspace, stream));
   if (t <= 64)
     return launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb,
                                        workspace, stream));

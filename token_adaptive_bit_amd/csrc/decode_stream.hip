@@ -1,4 +1,4 @@
-// Routed decode linear for small batches (T <= 16) -- the HBM-streaming kernel.
+// Routed decode linear for small batches (T <= 64) -- the HBM-streaming kernel.
 //
 // Same arithmetic as decode.hip (MoBiQuant explainer, gist.science English page, sections
 // 2.A and 3: each token sums its own slices; only slices some token uses are fetched):
@@ -7,16 +7,17 @@
 //   and the accumulator seeded with -sum_k x_k o_k.
 //
 // Organisation (one persistent workgroup per CU):
-//   * wave w owns k tiles w, w + NW, ... (TPW of them): their slice of x (the A operand)
-//     and the per-group seeds -sum x*o and sum x are computed once and stay in registers
-//     for the whole kernel.  With at most 16 tokens there is a single MFMA token block, so
-//     rows stay in the tokens' original order: x is read with no dependence on perm, and
-//     perm / offsets only decide which slices count for which row;
+//   * tokens come in blocks of 16 (workgroup row blockIdx.y, at most 4 for T <= 64), one
+//     MFMA token block each; rows stay in the tokens' original order, so x is read with no
+//     dependence on perm, and perm / offsets only decide which slices count for which row;
+//   * wave w owns k tiles w, w + NW, ... (TPW of them): their slice of its token block's x
+//     (the A operand) and the per-group seeds -sum x*o and sum x are computed once and stay
+//     in registers for the whole kernel;
 //   * the workgroup walks row blocks nb = blockIdx.x, + gridDim.x, ...; for each, every
 //     wave multiplies its k tiles of every needed slice while the next two row blocks'
 //     codes and params are already loading (three register buffers with fixed roles,
-//     every load unconditional: an unused slice or a past-the-end row block re-reads
-//     cached lines);
+//     every load unconditional: a past-the-end row block re-reads cached lines, a slice no
+//     token of the batch uses has an empty buffer range and reads nothing);
 //   * the waves' partial 16x16 tiles are summed in LDS (double-buffered, one barrier per
 //     row block) and written out with per-token slice masks already applied.
 // Token perm[i] (sorted position i) has budget b with offsets[b-1] <= i < offsets[b].
@@ -26,6 +27,7 @@ namespace mbq {
 namespace {
 
 constexpr int kMaxWaves = 8;
+constexpr int kMaxTokens = 64;  // tokens per launch (16 per workgroup row)
 constexpr uint32_t kNeg128 = 0xC300C300u, kNeg32 = 0xC200C200u, kNeg8 = 0xC100C100u;
 constexpr uint32_t kOnes = 0x3F803F80u;
 
@@ -103,7 +105,8 @@ template <int G, int S, int NA, int TPW>
 __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, uint64_t ss,
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ offsets, void* __restrict__ y, int y_bf16) {
+    const int32_t* __restrict__ offsets, void* __restrict__ y, int y_bf16, int kchunk,
+    float* __restrict__ part) {
   constexpr int GPT = 256 / G, WPG = G / 64;
   __shared__ f32x4_t red[2][kMaxWaves][64];
   const int NW = blockDim.x >> 6;
@@ -112,18 +115,36 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   const int r = lane & 15, c = lane >> 4;
   const int step = gridDim.x;
 
+  // k tiles [kb0, kend) of this workgroup's k chunk (blockIdx.z)
+  const int kb0 = blockIdx.z * kchunk, kend = min(KB, kb0 + kchunk);
   int kt[TPW];
   bool live[TPW];
 #pragma unroll
   for (int tp = 0; tp < TPW; ++tp) {
-    const int t = wave + NW * tp;
-    live[tp] = t < KB;
-    kt[tp] = live[tp] ? t : 0;
+    const int t = kb0 + wave + NW * tp;
+    live[tp] = t < kend;
+    kt[tp] = live[tp] ? t : kb0;
   }
 
-  // ---- 1. loads that depend on nothing: this wave's activations (row r = token r; rows
-  // past T repeat the last token and are never stored).
-  const int xr = min(r, T - 1);
+  // ---- 1. routing.  The number of slices read (jmax) comes from offsets alone, through
+  // the scalar cache: 1 + #{j >= 1 : offsets[j] < T} (every slice some token of the batch
+  // uses).  Per-token budgets come from perm: lane i of wave 0 takes sorted position i
+  // (T <= 64) and later publishes that token's budget in an LDS table.  The perm load is
+  // issued first, so waiting for it never waits for the activation loads behind it.
+  int off[S + 1];
+#pragma unroll
+  for (int j = 0; j <= S; ++j) off[j] = offsets[j];
+  int jmax = 1;
+#pragma unroll
+  for (int j = 1; j < S; ++j)
+    if (off[j] <= T - 1) jmax = j + 1;
+  const int pi = (wave == 0 && lane < T) ? perm[lane] : -1;
+
+  // ---- 2. this wave's activations.  Workgroup row blockIdx.y takes tokens 16 blockIdx.y
+  // .. + 15 (row r = token tb0 + r; rows past T repeat the block's last token and are never
+  // stored).
+  const int tb0 = 16 * blockIdx.y, Tb = min(16, T - tb0);
+  const int xr = tb0 + min(r, Tb - 1);
   u32x4_t Araw[TPW][4][2][NA];
 #pragma unroll
   for (int tp = 0; tp < TPW; ++tp)
@@ -138,40 +159,29 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           Araw[tp][i][h][q] = ldg16(p);
         }
     }
-  Codes<G, S, TPW> c0, c1, c2;
   u32x4_t A[TPW][4][2][NA];
 
-  // ---- 2. routing data through the scalar cache (uniform addresses; its own counter, so
-  // nothing here waits on the vector loads above): slices any token needs (jmax) and, per
-  // row of this lane, its budget.
-  int off[S + 1];
+  // Budgets of this block's tokens, published in LDS right before the first row block is
+  // multiplied (by then every wave has its first three row blocks in flight): wave 0 clears
+  // the table and writes the budget of each token of the block that it holds (in order
+  // within the wave, so one barrier suffices).  A token that perm does not name keeps
+  // budget 0, so its row is written as zero.  The epilogue reads the table back.
+  __shared__ __align__(16) int budT[16];
+  auto route_budgets = [&]() {
+    if (wave == 0) {
+      int pv = pi;
+      asm volatile("" : "+v"(pv));  // keep the use of perm (and its wait) here
+      int b = 1;
 #pragma unroll
-  for (int j = 0; j <= S; ++j) off[j] = offsets[j];
-  int pm[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) pm[i] = perm[min(i, T - 1)];
-  int jmax = 1;
-#pragma unroll
-  for (int j = 1; j < S; ++j)
-    if (off[j] <= T - 1) jmax = j + 1;
-  // one buffer resource per slice; a slice no token needs points at slice 0 (cached)
-  __amdgpu_buffer_rsrc_t rs[S];
-#pragma unroll
-  for (int j = 0; j < S; ++j) rs[j] = slice_rsrc(packed + uint64_t(j < jmax ? j : 0) * ss, uint32_t(ss));
+      for (int j = 1; j < S; ++j)
+        if (off[j] <= lane) b = j + 1;
+      const int rr = pv - tb0;
+      if (lane < 16) budT[lane] = 0;
+      if (rr >= 0 && rr < Tb) budT[rr] = b;
+    }
+    __syncthreads();
+  };
   const uint32_t lane_code = 16u * lane, lane_par = 4u * (lane & 15);
-  int bud[4] = {0, 0, 0, 0};  // budget of token 4c + v
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tok = pm[i];
-    int b = 1;
-#pragma unroll
-    for (int j = 1; j < S; ++j)
-      if (off[j] <= i) b = j + 1;
-    if (i >= T) b = 0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (tok == 4 * c + v && b > 0) bud[v] = b;
-  }
 
   // ---- 3. A operands (float32 inputs split into bf16 high and low parts) and the seeds
   // -sum x*o, sum x per group.  Computed inside the streaming loop, after the first weight
@@ -228,8 +238,14 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       }
   };
 
-  // ---- stream the row blocks
+  // ---- stream the row blocks.  One buffer resource per slice; a slice no token needs
+  // gets an empty range, so its loads return zeros without any memory traffic (and its
+  // MFMAs and epilogues are skipped).
   const Magic mg{0x43004300u, 0x42004200u, 0x41004100u};
+  __amdgpu_buffer_rsrc_t rs[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) rs[j] = slice_rsrc(packed + uint64_t(j) * ss, j < jmax ? uint32_t(ss) : 0u);
+  Codes<G, S, TPW> c0, c1, c2;
   auto process = [&](const Codes<G, S, TPW>& C, int nb, int buf) {
     // Per group, the (slice, tile) MFMA chains are independent: issue them interleaved so
     // the matrix pipeline never waits on one chain, then run all their epilogues.
@@ -278,12 +294,15 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
         }
       }
     }
+    const int4 bud = *reinterpret_cast<const int4*>(&budT[4 * c]);  // tokens tb0 + 4c + v
     f32x4_t out{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < S; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (j < bud[v]) out[v] += acc[j][v];
+    for (int j = 0; j < S; ++j) {
+      out[0] += j < bud.x ? acc[j][0] : 0.f;
+      out[1] += j < bud.y ? acc[j][1] : 0.f;
+      out[2] += j < bud.z ? acc[j][2] : 0.f;
+      out[3] += j < bud.w ? acc[j][3] : 0.f;
+    }
     red[buf][wave][lane] = out;
     __syncthreads();
     // one output per thread of the first four waves (the workgroup has at least four), so
@@ -295,9 +314,11 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       float sum = 0.f;
       for (int w = 0; w < NW; ++w) sum += red[buf][w][ln][v];
       const int n = nb * 16 + n16;
-      if (p < T && n < N) {
-        const size_t idx = size_t(p) * N + n;
-        if (y_bf16)
+      if (p < Tb && n < N) {
+        const size_t idx = size_t(tb0 + p) * N + n;
+        if (part)  // one k chunk of several: a float32 partial, summed by splitk_reduce
+          part[size_t(blockIdx.z) * T * N + idx] = sum;
+        else if (y_bf16)
           reinterpret_cast<uint16_t*>(y)[idx] = uint16_t(bf16_bits_rne(sum));
         else
           reinterpret_cast<float*>(y)[idx] = sum;
@@ -334,9 +355,24 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       if (rb0 + (m0 + 2) * step >= NB) break;
     }
     load_codes(c2, rs, nbl(m0 + 4), kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    if (m0 < 0) route_budgets();
     process(c0, rb0 + (m0 + 2) * step, buf);
     buf ^= 1;
     if (rb0 + (m0 + 3) * step >= NB) break;
+  }
+}
+
+// Sums the k chunks' float32 partials in a fixed order (deterministic) and writes y.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ks,
+                                                            size_t tn, void* __restrict__ y,
+                                                            int y_bf16) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < tn; i += size_t(gridDim.x) * 256) {
+    float sum = part[i];
+    for (int z = 1; z < ks; ++z) sum += part[size_t(z) * tn + i];
+    if (y_bf16)
+      reinterpret_cast<uint16_t*>(y)[i] = uint16_t(bf16_bits_rne(sum));
+    else
+      reinterpret_cast<float*>(y)[i] = sum;
   }
 }
 
@@ -348,58 +384,109 @@ int cu_count() {
   return n;
 }
 
+// Whether a wave can hold two k tiles (their activations, seeds and three buffers of codes
+// and params) in its 256 registers without spilling.  A spill would wait on the in-order
+// load counter behind the prefetched weights; the build checks that every instantiated
+// variant is spill-free.
+constexpr bool two_tiles_fit(int G, int S, int NA) {
+  return NA == 1 ? (G == 64 ? S <= 1 : S <= 3) : (G == 128 ? S <= 1 : (G == 256 && S <= 2));
+}
+
+// How a launch covers the k tiles: one workgroup holds up to 8 waves x TPW tiles; a longer
+// K is cut into ks equal chunks (grid z) whose float32 partials go to the workspace.
+struct Plan {
+  int tpw, kchunk, ks, nw;
+};
+
+Plan make_plan(const mbq_desc& d, bool x_bf16) {
+  const int tmax = two_tiles_fit(d.group, d.slices, x_bf16 ? 1 : 2) ? 2 : 1;
+  const int kb = d.k_tiles;
+  int ks = (kb + kMaxWaves * tmax - 1) / (kMaxWaves * tmax);
+  const int kchunk = (kb + ks - 1) / ks;
+  ks = (kb + kchunk - 1) / kchunk;
+  const int tpw = kchunk > kMaxWaves ? 2 : 1;
+  const int nw = std::max(4, (kchunk + tpw - 1) / tpw);  // >= 4 waves: see the store step
+  return Plan{tpw, kchunk, ks, nw};
+}
+
 template <int G, int S, int NA, int TPW>
-hipError_t launch_gsn(const mbq_desc& d, const void* packed, int32_t t, const void* x,
-                      const int32_t* perm, const int32_t* offsets, void* y, bool y_bf16,
-                      hipStream_t stream) {
-  const int nw = std::max(4, (d.k_tiles + TPW - 1) / TPW);  // >= 4 waves: see the store step
-  const int grid = std::min(d.row_blocks, cu_count());
-  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW>), dim3(grid), dim3(64 * nw), 0, stream,
-                     static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles, d.groups_padded,
-                     d.row_blocks, d.slice_stride, d.params_offset, x, t, perm, offsets, y,
-                     int(y_bf16));
+hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
+                      const void* x, const int32_t* perm, const int32_t* offsets, void* y,
+                      bool y_bf16, float* part, hipStream_t stream) {
+  // One workgroup per CU.  The token blocks and k chunks of a launch share the CUs, so
+  // they all run at once: with gridDim.x a multiple of 8, workgroups (x, y, z) of every
+  // y and z sit on XCD x % 8, and the token blocks of one k chunk walk the same row blocks
+  // at the same pace, so each weight line comes from HBM once and is served to the other
+  // token blocks by that XCD's L2.
+  const int ty = (t + 15) / 16;
+  const int grid = std::min(d.row_blocks, std::max(8, (cu_count() / (ty * pl.ks)) & ~7));
+  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
+                     0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
+                     d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
+                     offsets, y, int(y_bf16), pl.kchunk, part);
   return hipGetLastError();
 }
 
-template <int G, int NA, int TPW>
-hipError_t launch_gn(const mbq_desc& d, const void* packed, int32_t t, const void* x,
-                     const int32_t* perm, const int32_t* offsets, void* y, bool y_bf16,
-                     hipStream_t stream) {
+template <int G, int S, int NA>
+hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
+                     const void* x, const int32_t* perm, const int32_t* offsets, void* y,
+                     bool y_bf16, float* part, hipStream_t stream) {
+  if constexpr (two_tiles_fit(G, S, NA)) {
+    if (pl.tpw == 2)
+      return launch_gsn<G, S, NA, 2>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+  }
+  return launch_gsn<G, S, NA, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+}
+
+template <int G, int NA>
+hipError_t launch_gn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
+                     const void* x, const int32_t* perm, const int32_t* offsets, void* y,
+                     bool y_bf16, float* part, hipStream_t stream) {
   switch (d.slices) {
-    case 1: return launch_gsn<G, 1, NA, TPW>(d, packed, t, x, perm, offsets, y, y_bf16, stream);
-    case 2: return launch_gsn<G, 2, NA, TPW>(d, packed, t, x, perm, offsets, y, y_bf16, stream);
-    case 3: return launch_gsn<G, 3, NA, TPW>(d, packed, t, x, perm, offsets, y, y_bf16, stream);
-    default: return launch_gsn<G, 4, NA, TPW>(d, packed, t, x, perm, offsets, y, y_bf16, stream);
+    case 1: return launch_gs<G, 1, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+    case 2: return launch_gs<G, 2, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+    case 3: return launch_gs<G, 3, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+    default: return launch_gs<G, 4, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
   }
 }
 
 template <int G>
-hipError_t launch_g(const mbq_desc& d, const void* packed, int32_t t, const void* x, bool x_bf16,
-                    const int32_t* perm, const int32_t* offsets, void* y, bool y_bf16,
-                    hipStream_t stream) {
-  const bool two = d.k_tiles > kMaxWaves;  // 9..16 tiles: two per wave
-  if (x_bf16)
-    return two ? launch_gn<G, 1, 2>(d, packed, t, x, perm, offsets, y, y_bf16, stream)
-               : launch_gn<G, 1, 1>(d, packed, t, x, perm, offsets, y, y_bf16, stream);
-  return two ? launch_gn<G, 2, 2>(d, packed, t, x, perm, offsets, y, y_bf16, stream)
-             : launch_gn<G, 2, 1>(d, packed, t, x, perm, offsets, y, y_bf16, stream);
+hipError_t launch_g(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
+                    const void* x, bool x_bf16, const int32_t* perm, const int32_t* offsets,
+                    void* y, bool y_bf16, float* part, hipStream_t stream) {
+  if (x_bf16) return launch_gn<G, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+  return launch_gn<G, 2>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
 }
 
 }  // namespace
 
 bool decode_stream_supported(const mbq_desc& d, int32_t t) {
   // buffer offsets are 32-bit: a slice must stay below 4 GiB
-  return t >= 1 && t <= 16 && d.k_tiles <= 2 * kMaxWaves && d.slice_stride < (uint64_t(1) << 32);
+  return t >= 1 && t <= kMaxTokens && d.slice_stride < (uint64_t(1) << 32);
+}
+
+size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16) {
+  const Plan pl = make_plan(d, x_bf16);
+  return pl.ks > 1 ? size_t(pl.ks) * size_t(t) * size_t(d.n) * sizeof(float) : 0;
 }
 
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
-                                void* y, bool y_bf16, hipStream_t stream) {
+                                void* y, bool y_bf16, void* workspace, hipStream_t stream) {
+  const Plan pl = make_plan(d, x_bf16);
+  float* part = pl.ks > 1 ? static_cast<float*>(workspace) : nullptr;
+  hipError_t e;
   switch (d.group) {
-    case 64: return launch_g<64>(d, packed, t, x, x_bf16, perm, offsets, y, y_bf16, stream);
-    case 128: return launch_g<128>(d, packed, t, x, x_bf16, perm, offsets, y, y_bf16, stream);
-    default: return launch_g<256>(d, packed, t, x, x_bf16, perm, offsets, y, y_bf16, stream);
+    case 64: e = launch_g<64>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, stream); break;
+    case 128: e = launch_g<128>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, stream); break;
+    default: e = launch_g<256>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, stream); break;
   }
+  if (e != hipSuccess || !part) return e;
+  const size_t tn = size_t(t) * size_t(d.n);
+  const int blocks = int(std::min<size_t>((tn + 255) / 256, size_t(8) * cu_count()));
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, stream, part, pl.ks, tn, y,
+                     int(y_bf16));
+  return hipGetLastError();
 }
 
 }  // namespace mbq

@@ -46,9 +46,10 @@ hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const
                          bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                          bool y_bf16, void* ws, hipStream_t stream);
 bool decode_stream_supported(const mbq_desc& d, int32_t t);
+size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
-                                void* y, bool y_bf16, hipStream_t stream);
+                                void* y, bool y_bf16, void* ws, hipStream_t stream);
 hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                           bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                           bool y_bf16, hipStream_t stream);
