@@ -142,7 +142,8 @@ def test_linear_validation_and_workspace():
     (18944, 3584, 128, 3, 16, F32, 2),    # float32 activations: one tile per wave, 7 + 7
     (5120, 5120, 128, 3, 64, BF16, 2),    # 20 tiles: 10 + 10
     (5120, 13824, 128, 3, 64, BF16, 4),   # 54 tiles: 14 + 14 + 14 + 12
-    (150, 2304, 64, 4, 48, F32, 2),       # 9 tiles, one per wave: 5 + 4
+    (150, 2304, 64, 3, 48, F32, 2),       # 9 tiles, one per wave: 5 + 4
+    (150, 2304, 64, 4, 48, F32, 0),       # group 64, 4 slices, float32: generic kernel
     (150, 2304, 64, 1, 48, BF16, 1),      # 9 tiles, two per wave
     (5120, 13824, 128, 3, 65, BF16, 0),   # prefill: no workspace
 ])

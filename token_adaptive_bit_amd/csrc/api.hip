@@ -126,7 +126,7 @@ mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dty
   *bytes = 0;
   if (t >= 1 && t <= 64) {  // enough for either decode kernel
     *bytes = mbq::decode_workspace(*desc, t, xb);
-    if (mbq::decode_stream_supported(*desc, t))
+    if (mbq::decode_stream_supported(*desc, t, xb))
       *bytes = std::max(*bytes, mbq::decode_stream_workspace(*desc, t, xb));
   }
   return MBQ_OK;
@@ -153,7 +153,7 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
   const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16;
   // MBQ_GENERIC_DECODE forces the generic decode kernel (kept for slices of 4 GiB and more,
   // which the streaming kernel's 32-bit buffer offsets cannot reach)
-  if (mbq::decode_stream_supported(*desc, t) && !std::getenv("MBQ_GENERIC_DECODE"))
+  if (mbq::decode_stream_supported(*desc, t, xb) && !std::getenv("MBQ_GENERIC_DECODE"))
     return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb,
                                               workspace, stream));
   if (t <= 64)

@@ -21,6 +21,8 @@
 //   * the waves' partial 16x16 tiles are summed in LDS (double-buffered, one barrier per
 //     row block) and written out with per-token slice masks already applied.
 // Token perm[i] (sorted position i) has budget b with offsets[b-1] <= i < offsets[b].
+#include <type_traits>
+
 #include "mbq_internal.h"
 
 namespace mbq {
@@ -150,16 +152,18 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const size_t k = size_t(kt[tp]) * 256 + 64 * i + 16 * c;
+      const int k = kt[tp] * 256 + 64 * i + 16 * c;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int q = 0; q < NA; ++q) {
-          const uint8_t* p = static_cast<const uint8_t*>(x) + (size_t(xr) * K + k + 8 * h) * (2 * NA) + 16 * q;
+          // K is a multiple of 64, so these 8 inputs are all real or all padding; padding
+          // reads the row's first inputs instead (zeroed with the seeds)
+          const int kk = k + 8 * h < K ? k + 8 * h : 0;
+          const uint8_t* p = static_cast<const uint8_t*>(x) + (size_t(xr) * K + kk) * (2 * NA) + 16 * q;
           Araw[tp][i][h][q] = ldg16(p);
         }
     }
-  u32x4_t A[TPW][4][2][NA];
 
   // Budgets of this block's tokens, published in LDS right before the first row block is
   // multiplied (by then every wave has its first three row blocks in flight): wave 0 clears
@@ -189,13 +193,29 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   const u32x4_t bneg0{kNeg128, kNeg32, kNeg8, kNeg128};
   const u32x4_t bneg1{kNeg32, kNeg8, kNeg128, kNeg32};
   const u32x4_t ones{kOnes, kOnes, kOnes, kOnes};
-  f32x4_t gnb[TPW][GPT], gxs[TPW][GPT];
-  // bf16 activations are used straight from the load registers (no copy, so nothing
-  // waits on them before the loop); float32 ones are split once into A.
-  auto aop = [&](int tp, int i, int h, int pa) -> const u32x4_t& {
-    return NA == 1 ? Araw[tp][i][h][0] : A[tp][i][h][pa];
-  };
+  // Per-group activation sums X[t][g] of the wave's NE groups live in LDS (they are used
+  // once per group and row block, by the zero term z * X), token-major so that a lane
+  // reads its four tokens with one 16-byte access.
+  constexpr int NE = TPW * GPT;
+  __shared__ __align__(16) float xsT[kMaxWaves][NE][16];
+  f32x4_t gnb[TPW][GPT];
+  // The A operands live in the load registers: bf16 activations as loaded, float32 ones
+  // (8 values in two registers) split once, in place, into bf16 high and low parts.
+  auto aop = [&](int tp, int i, int h, int pa) -> const u32x4_t& { return Araw[tp][i][h][pa]; };
   auto setup_a = [&]() {
+    // inputs past K and tiles this wave does not have get zero activations, so their
+    // products and sums are exactly zero whatever the redirected loads hold
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool real = live[tp] && kt[tp] * 256 + 64 * i + 16 * c + 8 * h < K;
+#pragma unroll
+          for (int q = 0; q < NA; ++q)
+            if (!real) Araw[tp][i][h][q] = u32x4_t{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
@@ -206,6 +226,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
             // used in place
           } else {
             const u32x4_t q0 = Araw[tp][i][h][0], q1 = Araw[tp][i][h][NA - 1];
+            u32x4_t hi, lo;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
               const float v0 = __uint_as_float(d < 2 ? q0[2 * d] : q1[2 * d - 4]);
@@ -213,9 +234,11 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
               const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
               const uint32_t l0 = bf16_bits_rne(v0 - bf16_bits_to_float(h0));
               const uint32_t l1 = bf16_bits_rne(v1 - bf16_bits_to_float(h1));
-              A[tp][i][h][0][d] = h0 | (h1 << 16);
-              A[tp][i][h][NA - 1][d] = l0 | (l1 << 16);
+              hi[d] = h0 | (h1 << 16);
+              lo[d] = l0 | (l1 << 16);
             }
+            Araw[tp][i][h][0] = hi;
+            Araw[tp][i][h][NA - 1] = lo;
           }
         }
 #pragma unroll
@@ -234,8 +257,13 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
             xs4 = mfma(aop(tp, i, 1, pa), ones, xs4);
           }
         gnb[tp][gi] = nb4;
-        gxs[tp][gi] = xs4;
+        // lanes (0, c) hold X of tokens 4c + v (every row n sees the same sums)
+        if (r == 0) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xsT[wave][tp * GPT + gi][4 * c + v] = xs4[v];
+        }
       }
+
   };
 
   // ---- stream the row blocks.  One buffer resource per slice; a slice no token needs
@@ -245,59 +273,63 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   __amdgpu_buffer_rsrc_t rs[S];
 #pragma unroll
   for (int j = 0; j < S; ++j) rs[j] = slice_rsrc(packed + uint64_t(j) * ss, j < jmax ? uint32_t(ss) : 0u);
+  // Three code buffers (two row blocks in flight) unless a wave's registers cannot hold
+  // them (group 64 with 4 slices: 32 registers of codes and params per buffer and tile):
+  // then two (one row block in flight).
+  constexpr bool kThreeBuffers = !(G == 64 && S == 4);
   Codes<G, S, TPW> c0, c1, c2;
-  auto process = [&](const Codes<G, S, TPW>& C, int nb, int buf) {
-    // Per group, the (slice, tile) MFMA chains are independent: issue them interleaved so
-    // the matrix pipeline never waits on one chain, then run all their epilogues.
-    f32x4_t acc[S];
+  // Multiplies one row block.  JM, the slices processed, is a compile-time count, so the
+  // MFMA chains and epilogues of a group form one straight-line block that the compiler
+  // interleaves (a runtime test per slice or tile would split it into small blocks and
+  // expose every MFMA's latency).  JM is S, or 1 when no token of the batch uses more;
+  // slices in [jmax, JM) read zeros (empty buffer range) and so add exactly zero, and a
+  // wave without one of its tiles zeroes that tile's scales and zeros.
+  auto process = [&](auto jm, const Codes<G, S, TPW>& C, int nb, int buf, Codes<G, S, TPW>& Cn,
+                     int nbn) __attribute__((always_inline)) {
+    constexpr int JM = decltype(jm)::value;
+    // the next buffer's loads (row block nbn) go out first: two row blocks stay in flight
+    load_codes(Cn, rs, nbn, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    f32x4_t acc[JM];
 #pragma unroll
-    for (int j = 0; j < S; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JM; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // One (tile, group) unit at a time: the slices' MFMA chains are independent and are
+    // issued interleaved, then the unit's epilogue scales them into the accumulators.
 #pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) {
-      f32x4_t P[S][TPW];
+    for (int u = 0; u < NE; ++u) {
+      const int tp = u / GPT, gi = u % GPT;
+      f32x4_t P[JM];
 #pragma unroll
-      for (int j = 0; j < S; ++j)
-#pragma unroll
-        for (int tp = 0; tp < TPW; ++tp) P[j][tp] = gnb[tp][gi];
+      for (int j = 0; j < JM; ++j) P[j] = gnb[tp][gi];
 #pragma unroll
       for (int ii = 0; ii < WPG; ++ii) {
         const int i = gi * WPG + ii;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int j = 0; j < S; ++j) {
-            if (j < jmax) {
+          for (int j = 0; j < JM; ++j) {
+            u32x4_t b0, b1;
+            unpack_word(C.cw[tp][j][i], mg, b0, b1);
 #pragma unroll
-              for (int tp = 0; tp < TPW; ++tp) {
-                u32x4_t b0, b1;
-                unpack_word(C.cw[tp][j][i], mg, b0, b1);
-#pragma unroll
-                for (int pa = 0; pa < NA; ++pa) P[j][tp] = mfma(aop(tp, i, h, pa), h ? b1 : b0, P[j][tp]);
-              }
-            }
+            for (int pa = 0; pa < NA; ++pa) P[j] = mfma(aop(tp, i, h, pa), h ? b1 : b0, P[j]);
           }
         }
       }
+      // the wave wrote this table itself, so its own in-order LDS accesses suffice
+      const f32x4_t X4 = *reinterpret_cast<const f32x4_t*>(&xsT[wave][u][4 * c]);
 #pragma unroll
-      for (int j = 0; j < S; ++j) {
-        if (j < jmax) {
+      for (int j = 0; j < JM; ++j) {
+        // scale and zero converted once each, then plain fmas (no mixed-precision fma)
+        float sc = __half2float(__ushort_as_half(uint16_t(C.pv[tp][j][gi] & 0xFFFFu)));
+        float zc = __half2float(__ushort_as_half(uint16_t(C.pv[tp][j][gi] >> 16)));
+        asm volatile("" : "+v"(sc), "+v"(zc));
 #pragma unroll
-          for (int tp = 0; tp < TPW; ++tp) {
-            if (!live[tp]) continue;  // a wave without this tile (uniform); its loads were redirects
-            const uint32_t pv = C.pv[tp][j][gi];
-            const float s = __half2float(__ushort_as_half(uint16_t(pv & 0xFFFFu)));
-            const float z = __half2float(__ushort_as_half(uint16_t(pv >> 16)));
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[j][v] = fmaf(s, P[j][tp][v], fmaf(z, gxs[tp][gi][v], acc[j][v]));
-          }
-        }
+        for (int v = 0; v < 4; ++v) acc[j][v] = fmaf(sc, P[j][v], fmaf(zc, X4[v], acc[j][v]));
       }
     }
     const int4 bud = *reinterpret_cast<const int4*>(&budT[4 * c]);  // tokens tb0 + 4c + v
     f32x4_t out{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
+    for (int j = 0; j < JM; ++j) {
       out[0] += j < bud.x ? acc[j][0] : 0.f;
       out[1] += j < bud.y ? acc[j][1] : 0.f;
       out[2] += j < bud.z ? acc[j][2] : 0.f;
@@ -326,40 +358,54 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     }
   };
 
-  // Three register buffers; step m loads row block m + 2 into buffer (m + 2) % 3 and then
-  // multiplies row block m from buffer m % 3, so two row blocks are always in flight.
-  // There is no prologue: steps -2 and -1 only load, and the seeds are computed once,
-  // right after the first row block's loads are out.  Every path into the loop header therefore carries the
-  // same pending loads, which keeps the compiler's waits on the in-order load counter
-  // exact.  A load past the end re-reads the workgroup's first row block (cached), so
-  // every load is unconditional.
+  // Three register buffers with fixed roles: step m issues the loads of row block m + 2
+  // into buffer (m + 2) % 3 and then multiplies row block m from buffer m % 3, so two row
+  // blocks are always in flight.  The prologue loads row blocks 0 and 1, with
+  // the seeds and the budgets computed in between (no loads in either).  The loop is
+  // instantiated once per slice count (S, and 1 when no token of the batch uses more), so
+  // inside each copy every path into the loop header carries the same pending loads in
+  // the same order, which keeps the compiler's waits on the in-order load counter exact.
+  // A load past the end re-reads the workgroup's first row block (cached), so every load
+  // is unconditional.
   const int rb0 = blockIdx.x;
   auto nbl = [&](int m) { const int n = rb0 + m * step; return n < NB ? n : rb0; };
-  int buf = 0;
-  bool first = true;
-  for (int m0 = -2;; m0 += 3) {
-    load_codes(c0, rs, nbl(m0 + 2), kt, KB, NG, uint32_t(po), lane_code, lane_par);
-    if (first) {  // seeds while the first row block is in flight (no loads in here)
-      setup_a();
-      first = false;
-    }
-    if (m0 >= 0) {
-      process(c1, rb0 + m0 * step, buf);
-      buf ^= 1;
-      if (rb0 + (m0 + 1) * step >= NB) break;
-    }
-    load_codes(c1, rs, nbl(m0 + 3), kt, KB, NG, uint32_t(po), lane_code, lane_par);
-    if (m0 + 1 >= 0) {
-      process(c2, rb0 + (m0 + 1) * step, buf);
-      buf ^= 1;
-      if (rb0 + (m0 + 2) * step >= NB) break;
-    }
-    load_codes(c2, rs, nbl(m0 + 4), kt, KB, NG, uint32_t(po), lane_code, lane_par);
-    if (m0 < 0) route_budgets();
-    process(c0, rb0 + (m0 + 2) * step, buf);
-    buf ^= 1;
-    if (rb0 + (m0 + 3) * step >= NB) break;
+  // (scheduling fences keep the issue order perm, x, row block 0, row block 1, so each
+  // wait below covers exactly the loads it needs)
+  __builtin_amdgcn_sched_barrier(0);
+  load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+  __builtin_amdgcn_sched_barrier(0);
+  setup_a();
+  if constexpr (kThreeBuffers) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_par);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  route_budgets();
+  auto stream = [&](auto jm) __attribute__((always_inline)) {
+    int buf = 0;
+    if constexpr (kThreeBuffers) {
+      for (int m = 0;; m += 3) {
+        process(jm, c0, rb0 + m * step, buf, c2, nbl(m + 2));
+        if (rb0 + (m + 1) * step >= NB) break;
+        process(jm, c1, rb0 + (m + 1) * step, buf ^ 1, c0, nbl(m + 3));
+        if (rb0 + (m + 2) * step >= NB) break;
+        process(jm, c2, rb0 + (m + 2) * step, buf, c1, nbl(m + 4));
+        buf ^= 1;
+        if (rb0 + (m + 3) * step >= NB) break;
+      }
+    } else {  // two buffers: row block m + 1 loads while m is multiplied
+      for (int m = 0;; m += 2) {
+        process(jm, c0, rb0 + m * step, 0, c1, nbl(m + 1));
+        if (rb0 + (m + 1) * step >= NB) break;
+        process(jm, c1, rb0 + (m + 1) * step, 1, c0, nbl(m + 2));
+        if (rb0 + (m + 2) * step >= NB) break;
+      }
+    }
+  };
+  if (S > 1 && jmax == 1)
+    stream(std::integral_constant<int, 1>{});
+  else
+    stream(std::integral_constant<int, S>{});
 }
 
 // Sums the k chunks' float32 partials in a fixed order (deterministic) and writes y.
@@ -438,6 +484,10 @@ hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int3
   return launch_gsn<G, S, NA, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
 }
 
+// Group 64 with 4 slices and float32 activations does not fit a wave's registers even
+// with two buffers; the generic decode kernel serves it.
+constexpr bool stream_fits(int G, int S, int NA) { return !(G == 64 && S == 4 && NA == 2); }
+
 template <int G, int NA>
 hipError_t launch_gn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                      const void* x, const int32_t* perm, const int32_t* offsets, void* y,
@@ -446,7 +496,10 @@ hipError_t launch_gn(const mbq_desc& d, const Plan& pl, const void* packed, int3
     case 1: return launch_gs<G, 1, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
     case 2: return launch_gs<G, 2, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
     case 3: return launch_gs<G, 3, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
-    default: return launch_gs<G, 4, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+    default:
+      if constexpr (stream_fits(G, 4, NA))
+        return launch_gs<G, 4, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+      return hipErrorInvalidValue;  // excluded by decode_stream_supported
   }
 }
 
@@ -460,9 +513,10 @@ hipError_t launch_g(const mbq_desc& d, const Plan& pl, const void* packed, int32
 
 }  // namespace
 
-bool decode_stream_supported(const mbq_desc& d, int32_t t) {
+bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16) {
   // buffer offsets are 32-bit: a slice must stay below 4 GiB
-  return t >= 1 && t <= kMaxTokens && d.slice_stride < (uint64_t(1) << 32);
+  return t >= 1 && t <= kMaxTokens && d.slice_stride < (uint64_t(1) << 32) &&
+         stream_fits(d.group, d.slices, x_bf16 ? 1 : 2);
 }
 
 size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16) {

@@ -45,7 +45,7 @@ size_t decode_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
 hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                          bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                          bool y_bf16, void* ws, hipStream_t stream);
-bool decode_stream_supported(const mbq_desc& d, int32_t t);
+bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16);
 size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
