@@ -134,18 +134,15 @@ def test_route_empty(mbq):
     assert off.cpu().tolist() == [0, 0, 0, 0]
 
 
-@pytest.mark.parametrize("cfg_dtype,T,K", [("f32", 16, 256), ("bf16", 64, 5120), ("bf16", 300, 4096)])
-def test_route_with_router(mbq, cfg_dtype, T, K):
-    say(f"route x T={T} K={K} {cfg_dtype}")
-    d = inputs.make_linear(31, 8, K, T, dtype=cfg_dtype)
-    logits, b, perm, off = mbq.route(to_dev(d["X"], tdt(cfg_dtype)), to_dev(d["Wr"], torch.float32))
+def check_route(mbq, d, x, S):
+    logits, b, perm, off = mbq.route(x, to_dev(d["Wr"], torch.float32))
     torch.cuda.synchronize()
     Lg = logits.cpu().numpy()
     Lref = O.router_logits(d["X"], d["Wr"])
     assert np.abs(Lg - Lref).max() <= 1e-5 * np.abs(Lref).max()
     # bit-exact given identical logits
     wb = O.route_from_logits(Lg)
-    wp, wo = O.regroup(wb, 3)
+    wp, wo = O.regroup(wb, S)
     assert np.array_equal(b.cpu().numpy(), wb)
     assert np.array_equal(perm.cpu().numpy(), wp)
     assert np.array_equal(off.cpu().numpy(), wo)
@@ -155,6 +152,36 @@ def test_route_with_router(mbq, cfg_dtype, T, K):
     for t in flips:
         top2 = np.sort(Lref[t])[-2:]
         assert top2[1] - top2[0] < 1e-4 * np.abs(Lref[t]).max()
+
+
+# 16-byte aligned x and Wr with K % 8 == 0 take the vector logits loads, K = 100 (and the
+# unaligned case below) the scalar loop; T <= 64 sorts in one wave, larger T in a workgroup
+@pytest.mark.parametrize("cfg_dtype,T,K,S", [("f32", 16, 256, 3), ("bf16", 64, 5120, 3),
+                                             ("bf16", 300, 4096, 3), ("bf16", 1, 3584, 3),
+                                             ("bf16", 16, 3584, 1), ("f32", 33, 512, 2),
+                                             ("bf16", 7, 13824, 4), ("bf16", 5, 100, 3)])
+def test_route_with_router(mbq, cfg_dtype, T, K, S):
+    say(f"route x T={T} K={K} S={S} {cfg_dtype}")
+    d = inputs.make_linear(31, 8, K if K % 64 == 0 else 128, T, slices=S, dtype=cfg_dtype)
+    if K % 64:  # a K no group divides: only the router is used here
+        rng = np.random.default_rng(5)
+        d = dict(d, X=rng.standard_normal((T, K)).astype(np.float32),
+                 Wr=(rng.standard_normal((K, S)) * 0.1).astype(np.float32))
+        if cfg_dtype == "bf16":
+            d["X"] = torch.from_numpy(d["X"]).to(torch.bfloat16).float().numpy()
+    check_route(mbq, d, to_dev(d["X"], tdt(cfg_dtype)), S)
+
+
+@pytest.mark.parametrize("cfg_dtype", ["bf16", "f32"])
+def test_route_unaligned_x(mbq, cfg_dtype):
+    """x that is only element-aligned takes the scalar logits loop; same contract."""
+    T, K, S = 16, 512, 3
+    d = inputs.make_linear(32, 8, K, T, slices=S, dtype=cfg_dtype)
+    buf = torch.zeros(T * K + 1, dtype=tdt(cfg_dtype), device=DEV)
+    x = buf[1:].view(T, K)
+    x.copy_(to_dev(d["X"], tdt(cfg_dtype)))
+    assert x.data_ptr() % 16 != 0
+    check_route(mbq, d, x, S)
 
 
 def test_regroup_forced_mix(mbq):

@@ -10,6 +10,8 @@
 // The logits kernel runs one workgroup per token (coalesced loads, fixed-order sums, so
 // logits and routes are identical from run to run).  The sort runs in one wave with
 // ballot ranks for T <= 64 (decode) and in one 1024-thread workgroup otherwise.
+#include <type_traits>
+
 #include "mbq_internal.h"
 
 namespace mbq {
@@ -79,8 +81,49 @@ __global__ __launch_bounds__(64) void route_small_kernel(int T, int S, const flo
   }
 }
 
-// One workgroup (512 threads) per token.
-template <bool BF16>
+// One workgroup (512 threads) per token.  With 16-byte aligned x and Wr and K % 8 == 0,
+// thread i takes 8-input chunks i, i + 512, ...: one 16-byte activation load (two for
+// float32) and 2 S 16-byte Wr loads per chunk, every chunk's loads in flight at once up
+// to kVecChunks; otherwise the scalar strided loop.
+constexpr int kVecChunks = 4;
+
+template <bool BF16, int S>
+__device__ __forceinline__ void dot_row_vec(const void* __restrict__ x, size_t row, int K,
+                                            const float* __restrict__ wr, int i0,
+                                            float (&acc)[4]) {
+  constexpr int XV = BF16 ? 1 : 2;
+  const int K8 = K >> 3;
+  for (int cb = i0; cb < K8; cb += 512 * kVecChunks) {
+    u32x4_t xr[kVecChunks][XV];
+    f32x4_t wv[kVecChunks][2 * S];
+#pragma unroll
+    for (int u = 0; u < kVecChunks; ++u) {
+      const int ch = cb + 512 * u;
+      if (ch < K8) {
+        const uint8_t* px = static_cast<const uint8_t*>(x) + (row * K + size_t(ch) * 8) * (BF16 ? 2 : 4);
+#pragma unroll
+        for (int q = 0; q < XV; ++q) xr[u][q] = *reinterpret_cast<const u32x4_t*>(px + 16 * q);
+#pragma unroll
+        for (int v = 0; v < 2 * S; ++v)
+          wv[u][v] = reinterpret_cast<const f32x4_t*>(wr + size_t(ch) * 8 * S)[v];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVecChunks; ++u) {
+      if (cb + 512 * u >= K8) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xe = BF16 ? __uint_as_float((e & 1) ? (xr[u][0][e >> 1] & 0xFFFF0000u)
+                                                         : (xr[u][0][e >> 1] << 16))
+                              : __uint_as_float(xr[u][e >> 2][e & 3]);
+#pragma unroll
+        for (int q = 0; q < S; ++q) acc[q] = fmaf(xe, wv[u][(e * S + q) >> 2][(e * S + q) & 3], acc[q]);
+      }
+    }
+  }
+}
+
+template <bool BF16, int SV>
 __global__ __launch_bounds__(512) void logits_kernel(const void* __restrict__ x, int T, int K,
                                                      int S, const float* __restrict__ wr,
                                                      float* __restrict__ logits) {
@@ -88,7 +131,10 @@ __global__ __launch_bounds__(512) void logits_kernel(const void* __restrict__ x,
   const int t = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  dot_row<BF16>(x, size_t(t), K, S, wr, threadIdx.x, 512, acc);
+  if (SV > 0)
+    dot_row_vec<BF16, (SV > 0 ? SV : 1)>(x, size_t(t), K, wr, threadIdx.x, acc);
+  else
+    dot_row<BF16>(x, size_t(t), K, S, wr, threadIdx.x, 512, acc);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const float v = wave_sum(acc[s]);
@@ -171,10 +217,25 @@ hipError_t launch_route(int32_t t, int32_t k, int32_t s, const void* x, bool x_b
                         const float* wr, float* logits, const int32_t* budget_in,
                         int32_t* budget, int32_t* perm, int32_t* offsets, hipStream_t stream) {
   if (x && t > 0) {
+    const bool vec = k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(wr) & 15) == 0;
+    auto go = [&](auto bf, auto sv) {
+      hipLaunchKernelGGL((logits_kernel<decltype(bf)::value, decltype(sv)::value>), dim3(t),
+                         dim3(512), 0, stream, x, t, k, s, wr, logits);
+    };
+    auto go_s = [&](auto bf) {
+      switch (vec ? s : 0) {
+        case 1: go(bf, std::integral_constant<int, 1>{}); break;
+        case 2: go(bf, std::integral_constant<int, 2>{}); break;
+        case 3: go(bf, std::integral_constant<int, 3>{}); break;
+        case 4: go(bf, std::integral_constant<int, 4>{}); break;
+        default: go(bf, std::integral_constant<int, 0>{}); break;
+      }
+    };
     if (x_bf16)
-      hipLaunchKernelGGL(logits_kernel<true>, dim3(t), dim3(512), 0, stream, x, t, k, s, wr, logits);
+      go_s(std::true_type{});
     else
-      hipLaunchKernelGGL(logits_kernel<false>, dim3(t), dim3(512), 0, stream, x, t, k, s, wr, logits);
+      go_s(std::false_type{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
