@@ -134,9 +134,10 @@ mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* per
 
 /* Host only: bytes of device workspace mbq_linear needs for t tokens (0 when none).
  * Decode (1 <= t <= 64) over more k tiles of 256 inputs than one workgroup holds (8 waves
- * of 1 or 2 tiles each, 2 when the group / slices / x dtype variant fits its registers)
- * splits K into c equal chunks and needs c * t * n * 4 bytes of float32 partials;
- * prefill needs none.  The size depends only on desc, t and x_dtype. */
+ * of 1 or 2 tiles each: 2 when the group / slices / x dtype variant fits its registers,
+ * 1 when t > 32 and two 16-token blocks share each workgroup) splits K into c equal
+ * chunks and needs c * t * n * 4 bytes of float32 partials; prefill needs none.  The
+ * size depends only on desc, t and x_dtype. */
 mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                 size_t* bytes);
 

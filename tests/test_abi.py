@@ -140,16 +140,23 @@ def test_linear_validation_and_workspace():
 @pytest.mark.parametrize("N,K,G,S,t,dt,chunks", [
     (18944, 3584, 128, 3, 16, BF16, 1),   # 14 k tiles: two per wave, one workgroup
     (18944, 3584, 128, 3, 16, F32, 2),    # float32 activations: one tile per wave, 7 + 7
-    (5120, 5120, 128, 3, 64, BF16, 2),    # 20 tiles: 10 + 10
-    (5120, 13824, 128, 3, 64, BF16, 4),   # 54 tiles: 14 + 14 + 14 + 12
+    (5120, 5120, 128, 3, 16, BF16, 2),    # 20 tiles, two per wave: 10 + 10
+    (5120, 5120, 128, 3, 32, BF16, 2),    # up to 32 tokens: one 16-token block per workgroup
+    (5120, 5120, 128, 3, 33, BF16, 3),    # two 16-token blocks per workgroup: one tile per wave, 7 + 7 + 6
+    (5120, 5120, 128, 3, 64, BF16, 3),
+    (5120, 13824, 128, 3, 64, BF16, 7),   # 54 tiles: 8 x 6 + 6
+    (5120, 13824, 128, 4, 64, BF16, 7),   # group 128 with 4 slices: one block, one tile per wave
     (150, 2304, 64, 3, 48, F32, 2),       # 9 tiles, one per wave: 5 + 4
     (150, 2304, 64, 4, 48, F32, 0),       # group 64, 4 slices, float32: generic kernel
-    (150, 2304, 64, 1, 48, BF16, 1),      # 9 tiles, two per wave
+    (150, 2304, 64, 1, 48, BF16, 2),      # two blocks, one tile per wave: 5 + 4
+    (150, 2304, 64, 1, 32, BF16, 1),      # one block: 9 tiles, two per wave
+    (150, 2304, 64, 2, 48, BF16, 2),      # group 64, 2 slices: one block, one tile per wave
     (5120, 13824, 128, 3, 65, BF16, 0),   # prefill: no workspace
 ])
 def test_decode_split_k_workspace(N, K, G, S, t, dt, chunks):
-    """Decode over more k tiles than one workgroup holds (8 waves x 1 or 2 tiles) splits K
-    into equal chunks whose float32 partials [chunks, t, N] live in the workspace."""
+    """Decode over more k tiles than one workgroup holds (8 waves x 1 or 2 tiles; 1 when two
+    16-token blocks share a workgroup, t > 32) splits K into equal chunks whose float32
+    partials [chunks, t, N] live in the workspace."""
     st, d = desc(N, K, G, S)
     assert st == OK
     n = ctypes.c_size_t(123)

@@ -233,6 +233,9 @@ LINEAR_CASES = [
     (100, 4096, 128, 3, 64, "bf16", "mix"),
     (200, 640, 128, 3, 50, "f32", "mix"),
     (150, 2304, 64, 4, 48, "f32", "mix"),
+    # two 16-token blocks per workgroup: group 64 with one slice, a partial second group
+    (150, 2304, 64, 1, 48, "bf16", "mix"),
+    (77, 1280, 256, 2, 63, "bf16", "mix"),
     # decode with K split over several workgroups (float32 partials in the workspace)
     (100, 5120, 128, 3, 64, "bf16", "mix"),
     (60, 13824, 128, 3, 20, "bf16", "mix"),

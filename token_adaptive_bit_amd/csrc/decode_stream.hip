@@ -103,14 +103,14 @@ __device__ __forceinline__ void load_codes(Codes<G, S, TPW>& C, const __amdgpu_b
 // At most 8 waves (two per SIMD), so a wave has 256 registers: room for its stationary
 // A operand and seeds plus three buffers of codes and params without any spill (a spill
 // would wait on the in-order load counter behind the prefetched loads).
-template <int G, int S, int NA, int TPW>
+template <int G, int S, int NA, int TPW, int TB>
 __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, uint64_t ss,
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, void* __restrict__ y, int y_bf16, int kchunk,
     float* __restrict__ part) {
   constexpr int GPT = 256 / G, WPG = G / 64;
-  __shared__ f32x4_t red[2][kMaxWaves][64];
+  __shared__ f32x4_t red[2][kMaxWaves][TB][64];
   const int NW = blockDim.x >> 6;
   // the wave index is uniform: telling the compiler keeps tile addresses in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -142,35 +142,38 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     if (off[j] <= T - 1) jmax = j + 1;
   const int pi = (wave == 0 && lane < T) ? perm[lane] : -1;
 
-  // ---- 2. this wave's activations.  Workgroup row blockIdx.y takes tokens 16 blockIdx.y
-  // .. + 15 (row r = token tb0 + r; rows past T repeat the block's last token and are never
-  // stored).
-  const int tb0 = 16 * blockIdx.y, Tb = min(16, T - tb0);
-  const int xr = tb0 + min(r, Tb - 1);
-  u32x4_t Araw[TPW][4][2][NA];
+  // ---- 2. this wave's activations.  Workgroup row blockIdx.y takes the TB 16-token
+  // blocks starting at token tb0 = 16 TB blockIdx.y; in block b, MFMA row r is token
+  // tb0 + 16 b + r (rows past T repeat a real token and are never stored).
+  const int tb0 = 16 * TB * blockIdx.y, Tw = min(16 * TB, T - tb0);
+  u32x4_t Araw[TB][TPW][4][2][NA];
 #pragma unroll
-  for (int tp = 0; tp < TPW; ++tp)
+  for (int b = 0; b < TB; ++b) {
+    const int xr = tb0 + min(16 * b + r, Tw - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = kt[tp] * 256 + 64 * i + 16 * c;
+    for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int i = 0; i < 4; ++i) {
+        const int k = kt[tp] * 256 + 64 * i + 16 * c;
 #pragma unroll
-        for (int q = 0; q < NA; ++q) {
-          // K is a multiple of 64, so these 8 inputs are all real or all padding; padding
-          // reads the row's first inputs instead (zeroed with the seeds)
-          const int kk = k + 8 * h < K ? k + 8 * h : 0;
-          const uint8_t* p = static_cast<const uint8_t*>(x) + (size_t(xr) * K + kk) * (2 * NA) + 16 * q;
-          Araw[tp][i][h][q] = ldg16(p);
-        }
-    }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q = 0; q < NA; ++q) {
+            // K is a multiple of 64, so these 8 inputs are all real or all padding; padding
+            // reads the row's first inputs instead (zeroed with the seeds)
+            const int kk = k + 8 * h < K ? k + 8 * h : 0;
+            const uint8_t* p = static_cast<const uint8_t*>(x) + (size_t(xr) * K + kk) * (2 * NA) + 16 * q;
+            Araw[b][tp][i][h][q] = ldg16(p);
+          }
+      }
+  }
 
   // Budgets of this block's tokens, published in LDS right before the first row block is
   // multiplied (by then every wave has its first three row blocks in flight): wave 0 clears
   // the table and writes the budget of each token of the block that it holds (in order
   // within the wave, so one barrier suffices).  A token that perm does not name keeps
   // budget 0, so its row is written as zero.  The epilogue reads the table back.
-  __shared__ __align__(16) int budT[16];
+  __shared__ __align__(16) int budT[16 * TB];
   auto route_budgets = [&]() {
     if (wave == 0) {
       int pv = pi;
@@ -180,8 +183,8 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       for (int j = 1; j < S; ++j)
         if (off[j] <= lane) b = j + 1;
       const int rr = pv - tb0;
-      if (lane < 16) budT[lane] = 0;
-      if (rr >= 0 && rr < Tb) budT[rr] = b;
+      if (lane < 16 * TB) budT[lane] = 0;
+      if (rr >= 0 && rr < Tw) budT[rr] = b;
     }
     __syncthreads();
   };
@@ -197,73 +200,75 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // once per group and row block, by the zero term z * X), token-major so that a lane
   // reads its four tokens with one 16-byte access.
   constexpr int NE = TPW * GPT;
-  __shared__ __align__(16) float xsT[kMaxWaves][NE][16];
-  f32x4_t gnb[TPW][GPT];
+  __shared__ __align__(16) float xsT[kMaxWaves][TB][NE][16];
+  f32x4_t gnb[TB][TPW][GPT];
   // The A operands live in the load registers: bf16 activations as loaded, float32 ones
   // (8 values in two registers) split once, in place, into bf16 high and low parts.
-  auto aop = [&](int tp, int i, int h, int pa) -> const u32x4_t& { return Araw[tp][i][h][pa]; };
+  auto aop = [&](int b, int tp, int i, int h, int pa) -> const u32x4_t& { return Araw[b][tp][i][h][pa]; };
   auto setup_a = [&]() {
-    // inputs past K and tiles this wave does not have get zero activations, so their
-    // products and sums are exactly zero whatever the redirected loads hold
 #pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
+    for (int b = 0; b < TB; ++b) {
+      // inputs past K and tiles this wave does not have get zero activations, so their
+      // products and sums are exactly zero whatever the redirected loads hold
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bool real = live[tp] && kt[tp] * 256 + 64 * i + 16 * c + 8 * h < K;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int q = 0; q < NA; ++q)
-            if (!real) Araw[tp][i][h][q] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+          for (int h = 0; h < 2; ++h) {
+            const bool real = live[tp] && kt[tp] * 256 + 64 * i + 16 * c + 8 * h < K;
 #pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
+            for (int q = 0; q < NA; ++q)
+              if (!real) Araw[b][tp][i][h][q] = u32x4_t{0u, 0u, 0u, 0u};
+          }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (NA == 1) {
-            // used in place
-          } else {
-            const u32x4_t q0 = Araw[tp][i][h][0], q1 = Araw[tp][i][h][NA - 1];
-            u32x4_t hi, lo;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              const float v0 = __uint_as_float(d < 2 ? q0[2 * d] : q1[2 * d - 4]);
-              const float v1 = __uint_as_float(d < 2 ? q0[2 * d + 1] : q1[2 * d - 3]);
-              const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
-              const uint32_t l0 = bf16_bits_rne(v0 - bf16_bits_to_float(h0));
-              const uint32_t l1 = bf16_bits_rne(v1 - bf16_bits_to_float(h1));
-              hi[d] = h0 | (h1 << 16);
-              lo[d] = l0 | (l1 << 16);
+          for (int h = 0; h < 2; ++h) {
+            if (NA == 1) {
+              // used in place
+            } else {
+              const u32x4_t q0 = Araw[b][tp][i][h][0], q1 = Araw[b][tp][i][h][NA - 1];
+              u32x4_t hi, lo;
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                const float v0 = __uint_as_float(d < 2 ? q0[2 * d] : q1[2 * d - 4]);
+                const float v1 = __uint_as_float(d < 2 ? q0[2 * d + 1] : q1[2 * d - 3]);
+                const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
+                const uint32_t l0 = bf16_bits_rne(v0 - bf16_bits_to_float(h0));
+                const uint32_t l1 = bf16_bits_rne(v1 - bf16_bits_to_float(h1));
+                hi[d] = h0 | (h1 << 16);
+                lo[d] = l0 | (l1 << 16);
+              }
+              Araw[b][tp][i][h][0] = hi;
+              Araw[b][tp][i][h][NA - 1] = lo;
             }
-            Araw[tp][i][h][0] = hi;
-            Araw[tp][i][h][NA - 1] = lo;
+          }
+#pragma unroll
+      for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+        for (int gi = 0; gi < GPT; ++gi) {
+          f32x4_t nb4{0.f, 0.f, 0.f, 0.f}, xs4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ii = 0; ii < WPG; ++ii)
+#pragma unroll
+            for (int pa = 0; pa < NA; ++pa) {
+              const int i = gi * WPG + ii;
+              nb4 = mfma(aop(b, tp, i, 0, pa), bneg0, nb4);
+              nb4 = mfma(aop(b, tp, i, 1, pa), bneg1, nb4);
+              xs4 = mfma(aop(b, tp, i, 0, pa), ones, xs4);
+              xs4 = mfma(aop(b, tp, i, 1, pa), ones, xs4);
+            }
+          gnb[b][tp][gi] = nb4;
+          // lanes (0, c) hold X of tokens 4c + v (every row n sees the same sums)
+          if (r == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) xsT[wave][b][tp * GPT + gi][4 * c + v] = xs4[v];
           }
         }
-#pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
-#pragma unroll
-      for (int gi = 0; gi < GPT; ++gi) {
-        f32x4_t nb4{0.f, 0.f, 0.f, 0.f}, xs4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ii = 0; ii < WPG; ++ii)
-#pragma unroll
-          for (int pa = 0; pa < NA; ++pa) {
-            const int i = gi * WPG + ii;
-            nb4 = mfma(aop(tp, i, 0, pa), bneg0, nb4);
-            nb4 = mfma(aop(tp, i, 1, pa), bneg1, nb4);
-            xs4 = mfma(aop(tp, i, 0, pa), ones, xs4);
-            xs4 = mfma(aop(tp, i, 1, pa), ones, xs4);
-          }
-        gnb[tp][gi] = nb4;
-        // lanes (0, c) hold X of tokens 4c + v (every row n sees the same sums)
-        if (r == 0) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) xsT[wave][tp * GPT + gi][4 * c + v] = xs4[v];
-        }
-      }
-
+    }
   };
 
   // ---- stream the row blocks.  One buffer resource per slice; a slice no token needs
@@ -289,17 +294,22 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     constexpr int JM = decltype(jm)::value;
     // the next buffer's loads (row block nbn) go out first: two row blocks stay in flight
     load_codes(Cn, rs, nbn, kt, KB, NG, uint32_t(po), lane_code, lane_par);
-    f32x4_t acc[JM];
+    f32x4_t acc[TB][JM];
 #pragma unroll
-    for (int j = 0; j < JM; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // One (tile, group) unit at a time: the slices' MFMA chains are independent and are
-    // issued interleaved, then the unit's epilogue scales them into the accumulators.
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int j = 0; j < JM; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // One (tile, group) unit at a time: the slices' MFMA chains (one per token block, all
+    // fed by the same unpacked codes) are independent and are issued interleaved, then
+    // the unit's epilogue scales them into the accumulators.
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
       const int tp = u / GPT, gi = u % GPT;
-      f32x4_t P[JM];
+      f32x4_t P[TB][JM];
 #pragma unroll
-      for (int j = 0; j < JM; ++j) P[j] = gnb[tp][gi];
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int j = 0; j < JM; ++j) P[b][j] = gnb[b][tp][gi];
 #pragma unroll
       for (int ii = 0; ii < WPG; ++ii) {
         const int i = gi * WPG + ii;
@@ -310,12 +320,16 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
             u32x4_t b0, b1;
             unpack_word(C.cw[tp][j][i], mg, b0, b1);
 #pragma unroll
-            for (int pa = 0; pa < NA; ++pa) P[j] = mfma(aop(tp, i, h, pa), h ? b1 : b0, P[j]);
+            for (int b = 0; b < TB; ++b)
+#pragma unroll
+              for (int pa = 0; pa < NA; ++pa) P[b][j] = mfma(aop(b, tp, i, h, pa), h ? b1 : b0, P[b][j]);
           }
         }
       }
       // the wave wrote this table itself, so its own in-order LDS accesses suffice
-      const f32x4_t X4 = *reinterpret_cast<const f32x4_t*>(&xsT[wave][u][4 * c]);
+      f32x4_t X4[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) X4[b] = *reinterpret_cast<const f32x4_t*>(&xsT[wave][b][u][4 * c]);
 #pragma unroll
       for (int j = 0; j < JM; ++j) {
         // scale and zero converted once each, then plain fmas (no mixed-precision fma)
@@ -323,31 +337,37 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
         float zc = __half2float(__ushort_as_half(uint16_t(C.pv[tp][j][gi] >> 16)));
         asm volatile("" : "+v"(sc), "+v"(zc));
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[j][v] = fmaf(sc, P[j][v], fmaf(zc, X4[v], acc[j][v]));
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[b][j][v] = fmaf(sc, P[b][j][v], fmaf(zc, X4[b][v], acc[b][j][v]));
       }
     }
-    const int4 bud = *reinterpret_cast<const int4*>(&budT[4 * c]);  // tokens tb0 + 4c + v
-    f32x4_t out{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < JM; ++j) {
-      out[0] += j < bud.x ? acc[j][0] : 0.f;
-      out[1] += j < bud.y ? acc[j][1] : 0.f;
-      out[2] += j < bud.z ? acc[j][2] : 0.f;
-      out[3] += j < bud.w ? acc[j][3] : 0.f;
+    for (int b = 0; b < TB; ++b) {
+      const int4 bud = *reinterpret_cast<const int4*>(&budT[16 * b + 4 * c]);  // tokens 16b + 4c + v
+      f32x4_t out{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < JM; ++j) {
+        out[0] += j < bud.x ? acc[b][j][0] : 0.f;
+        out[1] += j < bud.y ? acc[b][j][1] : 0.f;
+        out[2] += j < bud.z ? acc[b][j][2] : 0.f;
+        out[3] += j < bud.w ? acc[b][j][3] : 0.f;
+      }
+      red[buf][wave][b][lane] = out;
     }
-    red[buf][wave][lane] = out;
     __syncthreads();
-    // one output per thread of the first four waves (the workgroup has at least four), so
-    // every row block issues a fixed number of stores and the load waits stay exact
-    if (threadIdx.x < 256) {
-      const int t = threadIdx.x;
+    // one output per thread of the first 4 TB waves (the workgroup has at least that
+    // many), so every row block issues a fixed number of stores and the load waits stay
+    // exact
+    if (threadIdx.x < 256 * TB) {
+      const int b = threadIdx.x >> 8, t = threadIdx.x & 255;
       const int p = t >> 4, n16 = t & 15;
       const int ln = 16 * (p >> 2) + n16, v = p & 3;
       float sum = 0.f;
-      for (int w = 0; w < NW; ++w) sum += red[buf][w][ln][v];
-      const int n = nb * 16 + n16;
-      if (p < Tb && n < N) {
-        const size_t idx = size_t(tb0 + p) * N + n;
+      for (int w = 0; w < NW; ++w) sum += red[buf][w][b][ln][v];
+      const int n = nb * 16 + n16, tok = 16 * b + p;
+      if (tok < Tw && n < N) {
+        const size_t idx = size_t(tb0 + tok) * N + n;
         if (part)  // one k chunk of several: a float32 partial, summed by splitk_reduce
           part[size_t(blockIdx.z) * T * N + idx] = sum;
         else if (y_bf16)
@@ -438,35 +458,48 @@ constexpr bool two_tiles_fit(int G, int S, int NA) {
   return NA == 1 ? (G == 64 ? S <= 1 : S <= 3) : (G == 128 ? S <= 1 : (G == 256 && S <= 2));
 }
 
-// How a launch covers the k tiles: one workgroup holds up to 8 waves x TPW tiles; a longer
-// K is cut into ks equal chunks (grid z) whose float32 partials go to the workspace.
+// Whether a wave can hold two 16-token blocks (one k tile): bf16 activations with one
+// slice at group 64, up to three at group 128 and up to four at group 256.
+constexpr bool two_blocks_fit(int G, int S, int NA) {
+  return NA == 1 && (G == 64 ? S == 1 : (G == 128 ? S <= 3 : S <= 4));
+}
+
+// How a launch covers the tokens and k tiles.  Batches of more than 32 tokens put two
+// 16-token blocks in each workgroup (TB = 2) where the registers allow, so the codes are
+// unpacked (and read from L2) once for both; a wave then holds one k tile, so K may need
+// more chunks.  Up to 32 tokens the extra chunks would cost more than the shared unpack
+// saves when few slices are read, so those batches keep one block per workgroup.  One workgroup holds up to 8
+// waves x TPW tiles; a longer K is cut into ks equal chunks (grid z) whose float32
+// partials go to the workspace.
 struct Plan {
-  int tpw, kchunk, ks, nw;
+  int tb, tpw, kchunk, ks, nw;
 };
 
-Plan make_plan(const mbq_desc& d, bool x_bf16) {
-  const int tmax = two_tiles_fit(d.group, d.slices, x_bf16 ? 1 : 2) ? 2 : 1;
+Plan make_plan(const mbq_desc& d, int32_t t, bool x_bf16) {
+  const int na = x_bf16 ? 1 : 2;
+  const int tb = (t > 32 && two_blocks_fit(d.group, d.slices, na)) ? 2 : 1;
+  const int tmax = (tb == 1 && two_tiles_fit(d.group, d.slices, na)) ? 2 : 1;
   const int kb = d.k_tiles;
   int ks = (kb + kMaxWaves * tmax - 1) / (kMaxWaves * tmax);
   const int kchunk = (kb + ks - 1) / ks;
   ks = (kb + kchunk - 1) / kchunk;
   const int tpw = kchunk > kMaxWaves ? 2 : 1;
-  const int nw = std::max(4, (kchunk + tpw - 1) / tpw);  // >= 4 waves: see the store step
-  return Plan{tpw, kchunk, ks, nw};
+  const int nw = std::max(4 * tb, (kchunk + tpw - 1) / tpw);  // >= 4 TB waves: the store step
+  return Plan{tb, tpw, kchunk, ks, nw};
 }
 
-template <int G, int S, int NA, int TPW>
+template <int G, int S, int NA, int TPW, int TB>
 hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                       const void* x, const int32_t* perm, const int32_t* offsets, void* y,
                       bool y_bf16, float* part, hipStream_t stream) {
-  // One workgroup per CU.  The token blocks and k chunks of a launch share the CUs, so
-  // they all run at once: with gridDim.x a multiple of 8, workgroups (x, y, z) of every
-  // y and z sit on XCD x % 8, and the token blocks of one k chunk walk the same row blocks
+  // One workgroup per CU.  The token-block groups and k chunks of a launch share the CUs,
+  // so they all run at once: with gridDim.x a multiple of 8, workgroups (x, y, z) of every
+  // y and z sit on XCD x % 8, and the token groups of one k chunk walk the same row blocks
   // at the same pace, so each weight line comes from HBM once and is served to the other
-  // token blocks by that XCD's L2.
-  const int ty = (t + 15) / 16;
+  // token groups by that XCD's L2.
+  const int ty = (t + 16 * TB - 1) / (16 * TB);
   const int grid = std::min(d.row_blocks, std::max(8, (cu_count() / (ty * pl.ks)) & ~7));
-  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
+  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
                      0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
                      d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
                      offsets, y, int(y_bf16), pl.kchunk, part);
@@ -477,11 +510,15 @@ template <int G, int S, int NA>
 hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                      const void* x, const int32_t* perm, const int32_t* offsets, void* y,
                      bool y_bf16, float* part, hipStream_t stream) {
+  if constexpr (two_blocks_fit(G, S, NA)) {
+    if (pl.tb == 2)
+      return launch_gsn<G, S, NA, 1, 2>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+  }
   if constexpr (two_tiles_fit(G, S, NA)) {
     if (pl.tpw == 2)
-      return launch_gsn<G, S, NA, 2>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+      return launch_gsn<G, S, NA, 2, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
   }
-  return launch_gsn<G, S, NA, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+  return launch_gsn<G, S, NA, 1, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
 }
 
 // Group 64 with 4 slices and float32 activations does not fit a wave's registers even
@@ -520,14 +557,14 @@ bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16) {
 }
 
 size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16) {
-  const Plan pl = make_plan(d, x_bf16);
+  const Plan pl = make_plan(d, t, x_bf16);
   return pl.ks > 1 ? size_t(pl.ks) * size_t(t) * size_t(d.n) * sizeof(float) : 0;
 }
 
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
                                 void* y, bool y_bf16, void* workspace, hipStream_t stream) {
-  const Plan pl = make_plan(d, x_bf16);
+  const Plan pl = make_plan(d, t, x_bf16);
   float* part = pl.ks > 1 ? static_cast<float*>(workspace) : nullptr;
   hipError_t e;
   switch (d.group) {
