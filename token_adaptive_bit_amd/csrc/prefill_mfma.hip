@@ -1,7 +1,7 @@
 // Routed prefill linear (T > 64), MFMA kernel: per budget group b,
 //   Y_b = X_b . W^(b)^T,   W^(b)[n, k] = sum_{j <= b} (z_jng + s_jng * q_jnk)
-// dequantized straight into MFMA B-operand registers as bfloat16 and multiplied on
-// 16x16x32 bf16 MFMA with float32 accumulation.
+// with the summed slices dequantized to bfloat16 once per tile and multiplied on
+// 32x32x16 bf16 MFMA with float32 accumulation.
 //
 // MoBiQuant explainer (gist.science, English), sections 2.A and 4: the summed slices are
 // the token's weight and prefill cost grows with sequence length, so this path is a dense
@@ -9,17 +9,13 @@
 // vendor's GPU; CDNA4 has no 1-bit MFMA, so the slices are summed in float32 once per
 // (tile, weight), rounded once to bfloat16 and fed to bf16 MFMA.
 //
-// Tiling.  A tile is BM tokens of one budget group x 256 outputs; wave w owns outputs
-// 64w .. 64w + 63 (four 16-row blocks of the packed layout) for all BM tokens, so every
-// weight is dequantized by exactly one wave, directly in the register layout MFMA wants
-// (no LDS round trip for weights), and the activations are the only operand shared
-// through LDS (double-buffered chunks of 64 inputs, rows padded to 144 bytes so that the
-// 16-byte MFMA operand reads are free of bank conflicts).
-//
-// k order.  Lane 16c + r of a packed tile holds, in word i, the 16 codes of row r for
-// inputs 64i + 16c + e.  The MFMA contraction index of step (chunk, h) is matched to
-// input 16c + 8h + j of the chunk for both operands, so the B operand of lane (c, r) comes
-// from its own code word and the A operand is read from LDS in natural order.
+// Tiling.  A tile is BM tokens of one budget group (256, or 128 for a group's short
+// remainder and for float32 activations) x 256 outputs, on 8 waves.  Wave w runs on SIMD
+// w % 4; the two waves of a SIMD share column block wn = w & 3 (64 outputs) and split the
+// tile's tokens (wm = w >> 2) and the block's dequantization (each dequantizes 32 of the
+// 64 outputs).  Dequantized chunks are exchanged through LDS as ready-made MFMA B
+// operands; activations are staged through LDS in chunks of 64 inputs (rows of 128 bytes,
+// 16-byte pieces swizzled so operand reads are free of bank conflicts).
 //
 // Dequantization.  Each 2-bit field is turned into a float16 pair (o + q_e, o + q_e+1) by
 // one AND-OR with an exponent pattern whose unit in the last place is the field's weight;
@@ -27,9 +23,11 @@
 // and each slice adds s_j * v_j with one mixed-precision FMA per weight (float16 inputs,
 // float32 accumulate).  (A float16 dot2 would pair two slices per instruction, but DOT
 // results need wait states before VALU reads that cost as much as it saves.)
-// Pipeline per 32-input step: the MFMAs of step s run while the VALU dequantizes step
-// s + 1; codes and params of chunk q + 2 and activations of chunk q + 2 load during chunk
-// q, so the loop has no load it waits on at once.
+//
+// Pipeline per chunk: each group of MFMAs (one 32-row block, both column halves) is
+// fenced around half of the dequantization of chunk q + 1, so one wave's VALU work runs
+// in the shadow of the other wave's MFMAs; codes, params and activations of chunk q + 2
+// load during chunk q, so the loop has no load it waits on at once.
 #include "mbq_internal.h"
 
 namespace mbq {
@@ -230,10 +228,9 @@ constexpr int lds_bytes() {
   return 2 * (XBF16 ? 256 : 128) * 128 + 65536 + 1024;
 }
 
-template <int B, bool XBF16>
+template <int B, bool XBF16, int BM>
 __device__ __forceinline__ void prefill_tile(const TileArgs& a, int start, int rows, int n0,
                                              uint8_t* lds) {
-  constexpr int BM = XBF16 ? 256 : 128;   // tokens per tile (float32 activations: half)
   constexpr int WM = BM / 2;              // tokens per wave
   constexpr int MB = WM / 32;             // 32-row MFMA blocks per wave
   constexpr int ABUF = BM * 128;
@@ -280,7 +277,7 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& a, int start, int r
   // while q + 1 is written from registers loaded during q - 1.  Rows past the tile's
   // tokens repeat its last token (never stored).
   const __amdgpu_buffer_rsrc_t xrs = rsrc(a.x, a.x_bytes);
-  constexpr int NP = 4;                          // 16-byte loads per thread and chunk
+  constexpr int NP = XBF16 ? BM / 64 : BM / 32;  // 16-byte loads per thread and chunk
   constexpr uint32_t XCH = XBF16 ? 128u : 256u;  // bytes of x per row and chunk
   uint32_t xoff[NP], soff[NP];
 #pragma unroll
@@ -432,49 +429,74 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& a, int start, int r
     store_tile<MB, WM, false>(acc, a, tokT, lds, wave, wn, wm, lane, n0);
 }
 
-// Tiles are numbered (budget group, M tile, N tile) in budget order; consecutive tiles
-// share an activation tile.  Workgroups are dealt to the eight XCDs round-robin, so the
-// block index is remapped to give each XCD a contiguous run of the tiles that exist (the
-// grid is sized for the most token tiles any budget split can need; the real count comes
-// from offsets), and the XCD's L2 holds the activation tiles its CUs share.
+// Tiles.  A budget group of R tokens takes R / BMb full tiles of BMb tokens (256; 128
+// for float32 activations); a remainder of more than half a tile takes one more full
+// tile, a smaller one (bf16 activations) a half tile of 128 tokens, so the padding stays
+// below half a tile.  All full tiles are numbered first, then the half tiles, each as
+// (M tile, N tile) with N fastest, and tile i runs on workgroup i.  Workgroups are dealt
+// to the eight XCDs round-robin and, within an XCD, dispatched in order, so every XCD
+// starts its share of full tiles and fills the tail with half tiles (a longest-first
+// schedule); the grid is sized for the most tiles any budget split can need and the real
+// count comes from offsets.  The 256 MiB last-level cache serves the activation and
+// weight tiles that several XCDs read.
 template <bool XBF16>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(TileArgs a, int S,
                                                            const int32_t* __restrict__ offsets) {
-  constexpr int BM = XBF16 ? 256 : 128;
+  constexpr int BMb = XBF16 ? 256 : 128, BMs = XBF16 ? 128 : 0;
   __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<XBF16>()];
   const int T = a.T;
-  int lo_[5], mt_[5], mtiles = 0;
-  for (int bb = 1; bb <= S; ++bb) {
+  int lo_[5] = {}, hi_[5] = {}, full_[5] = {}, half_[5] = {}, nfull = 0, nhalf = 0;
+  // (loops over the at most 4 budget groups are unrolled so the tables stay in registers)
+#pragma unroll
+  for (int bb = 1; bb <= 4; ++bb) {
+    if (bb > S) break;
     // offsets out of contract are clamped into [0, T] so no tile reaches past perm
     const int lo = min(max(offsets[bb - 1], 0), T), hi = min(max(offsets[bb], lo), T);
+    const int R = hi - lo, rem = R % BMb;
     lo_[bb] = lo;
-    mt_[bb] = (hi - lo + BM - 1) / BM;
-    mtiles += mt_[bb];
+    hi_[bb] = hi;
+    half_[bb] = (BMs > 0 && rem > 0 && rem <= BMs) ? 1 : 0;
+    full_[bb] = R / BMb + ((rem > 0 && !half_[bb]) ? 1 : 0);
+    nfull += full_[bb];
+    nhalf += half_[bb];
   }
   const int NT = (a.N + kBN - 1) / kBN;
-  const int tiles = NT * mtiles, per_xcd = (tiles + 7) / 8;
-  const int bid = blockIdx.x;
-  if ((bid >> 3) >= per_xcd) return;
-  const int lin = (bid & 7) * per_xcd + (bid >> 3);
-  if (lin >= tiles) return;
+  const int lin = blockIdx.x;
+  if (lin >= NT * (nfull + nhalf)) return;
   int m = lin / NT;
   const int n0 = (lin % NT) * kBN;
+  const bool is_half = m >= nfull;
+  if (is_half) m -= nfull;
   int b = 0, start = 0, rows = 0;
-  for (int bb = 1; bb <= S; ++bb) {
-    if (m < mt_[bb]) {
+#pragma unroll
+  for (int bb = 1; bb <= 4; ++bb) {
+    if (bb > S) break;
+    const int cnt = is_half ? half_[bb] : full_[bb];
+    if (m < cnt) {
       b = bb;
-      start = lo_[bb] + m * BM;
-      rows = min(BM, min(max(offsets[bb], lo_[bb]), T) - start);
+      start = is_half ? lo_[bb] + (full_[bb] * BMb) : lo_[bb] + m * BMb;
+      rows = min(is_half ? BMs : BMb, hi_[bb] - start);
       break;
     }
-    m -= mt_[bb];
+    m -= cnt;
   }
-  if (b == 0) return;  // uniform; unreachable for lin < tiles
+  if (b == 0) return;  // uniform; unreachable for lin below the tile count
+  if constexpr (BMs > 0) {
+    if (is_half) {
+      switch (b) {
+        case 1: prefill_tile<1, XBF16, BMs>(a, start, rows, n0, lds); break;
+        case 2: prefill_tile<2, XBF16, BMs>(a, start, rows, n0, lds); break;
+        case 3: prefill_tile<3, XBF16, BMs>(a, start, rows, n0, lds); break;
+        default: prefill_tile<4, XBF16, BMs>(a, start, rows, n0, lds); break;
+      }
+      return;
+    }
+  }
   switch (b) {
-    case 1: prefill_tile<1, XBF16>(a, start, rows, n0, lds); break;
-    case 2: prefill_tile<2, XBF16>(a, start, rows, n0, lds); break;
-    case 3: prefill_tile<3, XBF16>(a, start, rows, n0, lds); break;
-    default: prefill_tile<4, XBF16>(a, start, rows, n0, lds); break;
+    case 1: prefill_tile<1, XBF16, BMb>(a, start, rows, n0, lds); break;
+    case 2: prefill_tile<2, XBF16, BMb>(a, start, rows, n0, lds); break;
+    case 3: prefill_tile<3, XBF16, BMb>(a, start, rows, n0, lds); break;
+    default: prefill_tile<4, XBF16, BMb>(a, start, rows, n0, lds); break;
   }
 }
 
@@ -508,8 +530,9 @@ hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t,
   a.y = y;
   a.y_bf16 = int(y_bf16);
   const int NT = (d.n + kBN - 1) / kBN;
+  // at most ceil(R / BM) tiles per budget group (a half tile replaces a full one)
   const int max_tiles = NT * ((t + BM - 1) / BM + d.slices - 1);
-  dim3 grid(8 * ((max_tiles + 7) / 8)), block(512);
+  dim3 grid(max_tiles), block(512);
   if (x_bf16)
     hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, block, 0, stream, a, d.slices, offsets);
   else
