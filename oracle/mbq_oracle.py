@@ -27,6 +27,14 @@ Readings where the pages leave a step open (each one is listed in the design doc):
     group minimum of -0 is stored as +0 (the pages say nothing about signed zeros).
   * The router is linear without bias; a token's slice count is 1 + the first index of
     the largest logit.  (The pages' own router is a 2-layer MLP with a threshold.)
+  * The pages' MLP router, as built here: hidden = ReLU(x . W1^T + b1) (W1 [H, K]),
+    scores = hidden . W2 + b2, one score per residual slice (S - 1 of them; the base
+    slice is always used).  At inference the sigmoid gate passes a slice when
+    sigmoid(score) > delta, which is evaluated exactly as score > theta with
+    theta = logit(delta) rounded to float32 (delta <= 0 passes all, delta >= 1 none).
+    Residual slices refine each other, so a token uses the leading run of passing
+    slices: b = 1 + its length.  The pages name neither the activation nor the hidden
+    width; ReLU is the plainest reading.
   * Regrouping is a stable sort of tokens by ascending slice count.
   * Dot products and reconstruction are exact in float64 on the stored codes and params.
 
@@ -166,6 +174,55 @@ def regroup(budget: np.ndarray, slices: int):
     for i in range(1, slices + 1):
         offsets[i] = int(np.count_nonzero(budget <= i))
     return perm, offsets
+
+
+# ----------------------------------------------------------------------------------------
+# MoBiRoute as the pages describe it (English explainer section 2.B, Japanese section 2.2):
+# a 2-layer MLP scores each token per residual slice; a sigmoid gate with threshold delta
+# turns the scores into a binary mask at inference, and raising delta activates fewer slices
+# ----------------------------------------------------------------------------------------
+def mlp_router_scores(X, W1, b1, W2, b2) -> np.ndarray:
+    """scores [T, S-1] = ReLU(X . W1^T + b1) . W2 + b2 in float64.
+
+    X [T, K], W1 [H, K] (one row of input weights per hidden unit), b1 [H], W2 [H, S-1],
+    b2 [S-1].
+    """
+    X, W1, b1, W2, b2 = (np.asarray(a, np.float64) for a in (X, W1, b1, W2, b2))
+    hidden = np.maximum(X @ W1.T + b1, 0.0)
+    return hidden @ W2 + b2
+
+
+def gate_threshold(delta: float) -> np.float32:
+    """theta such that sigmoid(s) > delta  <=>  s > theta: logit(delta) rounded to float32.
+
+    sigmoid is increasing, so sigmoid(s) > delta exactly when s > log(delta / (1 - delta)).
+    """
+    if delta <= 0.0:
+        return np.float32(-np.inf)
+    if delta >= 1.0:
+        return np.float32(np.inf)
+    return np.float32(np.log(delta) - np.log1p(-delta))
+
+
+def budgets_from_scores(scores, theta) -> np.ndarray:
+    """b(t) = 1 + the number of leading residual slices whose score exceeds theta (int32)."""
+    scores = np.asarray(scores)
+    T, R = scores.shape
+    out = np.empty(T, np.int32)
+    for t in range(T):
+        b = 1
+        for j in range(R):
+            if scores[t, j] > theta:
+                b += 1
+            else:
+                break
+        out[t] = b
+    return out
+
+
+def average_bits(budget, bits_per_slice: int = 2) -> float:
+    """Average weight bit width over the tokens: bits_per_slice * mean(b)."""
+    return float(bits_per_slice * np.mean(np.asarray(budget, np.float64)))
 
 
 # ----------------------------------------------------------------------------------------

@@ -267,6 +267,94 @@ def test_regroup_matches_python_stable_sort():
     assert np.all(np.diff(b[perm]) >= 0)
 
 
+# ---------------------------------------------------------------- the MLP router and delta
+def test_gate_threshold_inverts_sigmoid():
+    for delta in (1e-4, 0.1, 0.3, 0.5, 0.7, 0.9, 0.999):
+        th = float(O.gate_threshold(delta))
+        assert abs(1.0 / (1.0 + np.exp(-th)) - delta) < 1e-6
+        # sigmoid(s) > delta <=> s > theta away from the float32 rounding of theta
+        s = np.linspace(th - 5, th + 5, 2001)
+        s = s[np.abs(s - th) > 1e-5]
+        assert np.array_equal(1.0 / (1.0 + np.exp(-s)) > delta, s > th)
+    assert O.gate_threshold(0.5) == 0.0
+    assert O.gate_threshold(0.0) == -np.inf and O.gate_threshold(-1.0) == -np.inf
+    assert O.gate_threshold(1.0) == np.inf and O.gate_threshold(2.0) == np.inf
+    ths = [O.gate_threshold(d) for d in np.linspace(0.01, 0.99, 99)]
+    assert np.all(np.diff(ths) > 0)
+
+
+def test_budgets_are_the_passing_prefix():
+    rng = np.random.default_rng(5)
+    sc = rng.standard_normal((400, 3))
+    for th in (-0.5, 0.0, 0.7):
+        b = O.budgets_from_scores(sc, np.float32(th))
+        passing = sc > np.float32(th)
+        # first failing residual slice, by a different route: argmin over a padded mask
+        first_fail = np.argmin(np.concatenate([passing, np.zeros((400, 1), bool)], 1), 1)
+        assert np.array_equal(b, 1 + first_fail)
+        assert b.dtype == np.int32 and b.min() >= 1 and b.max() <= 4
+    # a later passing slice does not count once an earlier one fails
+    assert O.budgets_from_scores(np.array([[-1.0, 9.0, 9.0]]), np.float32(0)).tolist() == [1]
+    assert O.budgets_from_scores(np.array([[1.0, -1.0, 9.0]]), np.float32(0)).tolist() == [2]
+    # equality does not pass (strict comparison)
+    assert O.budgets_from_scores(np.array([[0.0, 1.0]]), np.float32(0)).tolist() == [1]
+    # one-slice layers have no residual scores: every token uses the base slice
+    assert O.budgets_from_scores(np.zeros((3, 0)), np.float32(0)).tolist() == [1, 1, 1]
+
+
+def test_mlp_scores_reduce_to_selection():
+    # W1 = I, b1 = 0 and nonnegative x: the hidden layer is x itself; unit columns of W2
+    # then pick input coordinates, so the scores are x[:, i] + b2.
+    rng = np.random.default_rng(6)
+    K = 8
+    X = np.abs(rng.standard_normal((5, K)))
+    W2 = np.zeros((K, 3)); W2[2, 0] = 1; W2[5, 1] = 1; W2[7, 2] = 1
+    b2 = np.array([0.25, -0.5, 1.0])
+    sc = O.mlp_router_scores(X, np.eye(K), np.zeros(K), W2, b2)
+    np.testing.assert_array_equal(sc, X[:, [2, 5, 7]] + b2)
+    # negative pre-activations are cut by the ReLU: only the bias survives
+    sc = O.mlp_router_scores(-X, np.eye(K), np.zeros(K), W2, b2)
+    np.testing.assert_array_equal(sc, np.broadcast_to(b2, (5, 3)))
+    # b1 shifts the pre-activation before the ReLU
+    sc = O.mlp_router_scores(-X, np.eye(K), np.full(K, 10.0), W2, b2)
+    np.testing.assert_allclose(sc, 10.0 - X[:, [2, 5, 7]] + b2, rtol=0, atol=1e-12)
+
+
+def test_mlp_scores_match_loops():
+    r = inputs.make_mlp_router(7, K=12, slices=3, hidden=5)
+    X = inputs.make_linear(8, 4, 12, 3, group=4, dtype="f32")["X"]
+    sc = O.mlp_router_scores(X, r["W1"], r["b1"], r["W2"], r["b2"])
+    assert sc.shape == (3, 2)
+    for t in range(3):
+        h = [max(0.0, sum(float(X[t, k]) * float(r["W1"][u, k]) for k in range(12)) + float(r["b1"][u]))
+             for u in range(5)]
+        for j in range(2):
+            ref = sum(h[u] * float(r["W2"][u, j]) for u in range(5)) + float(r["b2"][j])
+            assert abs(sc[t, j] - ref) < 1e-12
+
+
+def test_raising_delta_never_adds_slices():
+    r = inputs.make_mlp_router(9, K=256, slices=4, hidden=64)
+    X = inputs.make_linear(10, 4, 256, 300, dtype="bf16")["X"]
+    sc = O.mlp_router_scores(X, r["W1"], r["b1"], r["W2"], r["b2"])
+    prev = None
+    bits = []
+    for delta in np.linspace(0.0, 1.0, 41):
+        b = O.budgets_from_scores(sc, O.gate_threshold(delta))
+        if prev is not None:
+            assert np.all(b <= prev)
+        prev = b
+        bits.append(O.average_bits(b))
+    assert bits[0] == 8.0 and bits[-1] == 2.0       # delta 0: every slice; delta 1: base only
+    assert len(set(bits)) > 10                      # the sweep passes through many widths
+
+
+def test_average_bits():
+    assert O.average_bits(np.array([1, 1, 1])) == 2.0
+    assert O.average_bits(np.array([1, 2, 3, 2])) == 4.0
+    assert O.average_bits(np.array([3, 3]), bits_per_slice=2) == 6.0
+
+
 # ---------------------------------------------------------------- the packed blob format
 def test_blob_sizes_match_workloads():
     # 2.25 bits per weight per slice at G=128, 2.5 at G=64 (codes + half scale and zero)

@@ -14,6 +14,10 @@ Draw order for one linear (numpy ``default_rng(seed)``):
   4. X = standard_normal((T, K), float32), rounded to bfloat16 unless float32
   5. Wr = standard_normal((K, S), float32) * 0.1
   6. forced budget mixes: rng.permutation(T) over a block-sorted budget vector
+
+The MLP router's weights have a generator of their own (``make_mlp_router``): hidden width
+256 unless stated, W1 ~ N(0, 1/K) rounded to bfloat16 (pre-activations ~ N(0, 1) on the
+activations above), b1 ~ N(0, 0.1^2), W2 ~ N(0, 2/H), b2 ~ N(0, 0.1^2), all float32.
 """
 from __future__ import annotations
 
@@ -64,6 +68,22 @@ def make_linear(seed: int, N: int, K: int, T: int, *, group: int = 128, slices: 
         budget = base[rng.permutation(T)].astype(np.int32)
     return {"W": W, "X": X, "Wr": Wr, "budget": budget, "N": N, "K": K, "T": T,
             "group": group, "slices": slices, "dtype": dtype}
+
+
+def make_mlp_router(seed: int, K: int, slices: int = 3, hidden: int = 256) -> dict:
+    """Synthetic weights of the 2-layer MLP router: one score per residual slice.
+
+    Draw order (``default_rng(seed)``): W1 [hidden, K], b1 [hidden], W2 [hidden, slices-1],
+    b2 [slices-1].  W1 holds bfloat16-representable float32 values.
+    """
+    rng = np.random.default_rng(seed)
+    W1 = rng.standard_normal((hidden, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K))
+    W1 = round_bf16(W1)
+    b1 = rng.standard_normal(hidden, dtype=np.float32) * np.float32(0.1)
+    W2 = rng.standard_normal((hidden, slices - 1), dtype=np.float32) * np.float32(np.sqrt(2.0 / hidden))
+    b2 = rng.standard_normal(slices - 1, dtype=np.float32) * np.float32(0.1)
+    return {"W1": W1, "b1": b1, "W2": W2, "b2": b2, "hidden": hidden, "K": K,
+            "slices": slices}
 
 
 def forced_mix(T: int, fractions) -> list:
