@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=16, help="decode batch (1, 4 or 16)")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer", "traffic"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer", "traffic", "route_mlp"], default=None,
                     help="run one workload only (for profiling); prints its own JSON line.  "
                          "'traffic' runs a copy kernel of known size and then the decode linear, "
                          "for the FETCH_SIZE / WRITE_SIZE counter passes")
@@ -216,6 +216,52 @@ def bench_sweep(api, torch, inputs, dev, iters=20):
     return out
 
 
+def bench_route_mlp(api, torch, inputs, dev, iters=50):
+    """The pages' MLP router (hidden 256, 3 slices, delta 0.5) on the decode (T=16, K=3584)
+    and prefill (T=2048, K=4096) layer inputs: time per call (hidden-layer MFMA kernel,
+    gate, regroup) next to the linear-argmax router, the hidden kernel's TFLOP/s, and a
+    delta sweep of the average weight bit width with the delta that lands on 3, 4, 5 bits."""
+    out = {}
+    for T, K in ((16, 3584), (2048, 4096)):
+        r = inputs.make_mlp_router(21, K, slices=3, hidden=256)
+        R = api.MlpRouter(*(torch.from_numpy(r[n]).to(dev, torch.bfloat16 if n == "W1" else torch.float32)
+                            for n in ("W1", "b1", "W2", "b2")))
+        d = inputs.make_linear(22, 16, K, T)
+        X = torch.from_numpy(d["X"]).to(dev, torch.bfloat16)
+        Wr = torch.from_numpy(d["Wr"]).to(dev, torch.float32)
+        sc, b, perm, off = api.route_mlp(X, R, 0.5)
+        ws = torch.empty(max(1, api.route_mlp_workspace(T, K, 256)), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            api.route_mlp(X, R, 0.5, sc, b, perm, off, workspace=ws)
+        torch.cuda.synchronize()
+        t_mlp = time_events(torch, lambda i: api.route_mlp(X, R, 0.5, sc, b, perm, off, workspace=ws), iters)
+        lg, lb, lp, lo = api.route(X, Wr)
+        t_lin = time_events(torch, lambda i: api.route(X, Wr, lg, lb, lp, lo), iters)
+        res = {"us": t_mlp * 1e6, "linear_router_us": t_lin * 1e6,
+               "hidden_tflops_incl_gate": 2.0 * T * K * 256 / t_mlp / 1e12,
+               "budget_counts_delta_0.5": torch.diff(off).cpu().tolist()}
+        sweep = {}
+        for delta in (0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9):
+            bb, _, _ = api.route_mlp_from_scores(sc, delta)
+            sweep[f"{delta:.1f}"] = 2.0 * bb.double().mean().item()
+        res["avg_bits_by_delta"] = sweep
+        hits = {}
+        for target in (3.0, 4.0, 5.0):
+            lo_d, hi_d = 0.0, 1.0          # average bits fall as delta rises
+            for _ in range(30):
+                mid = 0.5 * (lo_d + hi_d)
+                bb, _, _ = api.route_mlp_from_scores(sc, mid)
+                if 2.0 * bb.double().mean().item() > target:
+                    lo_d = mid
+                else:
+                    hi_d = mid
+            bb, _, _ = api.route_mlp_from_scores(sc, hi_d)
+            hits[f"{target:.0f}"] = {"delta": hi_d, "avg_bits": 2.0 * bb.double().mean().item()}
+        res["delta_for_bits"] = hits
+        out[f"t{T}_k{K}"] = res
+    return out
+
+
 def bench_layer(api, torch, inputs, dev, iters=20):
     """Seven linears of a 14B-like decoder layer at T = 64 with one router on the layer
     input: total time of route + 7 routed linears, and HBM fraction of the linears."""
@@ -327,6 +373,9 @@ def main():
     if args.only == "layer":
         print(json.dumps({"workload": "layer", **bench_layer(api, torch, inputs, dev)}))
         return
+    if args.only == "route_mlp":
+        print(json.dumps({"workload": "route_mlp", **bench_route_mlp(api, torch, inputs, dev)}))
+        return
     if args.only == "traffic":
         print(json.dumps(run_traffic(api, torch, inputs, dev, args.tokens, launches=max(args.steps, 1))))
         return
@@ -378,6 +427,8 @@ def main():
                                                  "prefill_mfma.hip", "prefill_mfma_11008x4096_t2048_traffic.txt")}
         log("elasticity sweep 14336x4096")
         extra["sweep_14336x4096"] = bench_sweep(api, torch, inputs, dev)
+        log("MLP router with threshold delta")
+        extra["route_mlp_h256_s3"] = bench_route_mlp(api, torch, inputs, dev)
         log("14B-like layer, T=64")
         extra["layer14b_t64"] = bench_layer(api, torch, inputs, dev)
         log("pack")

@@ -20,6 +20,10 @@
  *     code 0 when the stored scale is 0), deq = zero + code * scale rounded twice
  *     (float32 multiply, then float32 add; never fused).
  *   - The router is linear, no bias: logits = x . Wr, b(t) = 1 + first argmax.
+ *   - The MLP router (mbq_route_mlp): scores = ReLU(x . W1^T + b1) . W2 + b2, one score
+ *     per residual slice; the sigmoid gate passes slice j + 1 when sigmoid(score_j) >
+ *     delta, evaluated as score_j > float32(logit(delta)); b(t) = 1 + the length of the
+ *     leading run of passing slices.
  *   - Tokens are regrouped by a stable ascending sort on b(t).
  *
  * Conventions for every call:
@@ -131,6 +135,41 @@ mbq_status mbq_route(int32_t t, int32_t k, int32_t s, const void* x, mbq_dtype x
  */
 mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* perm,
                        int32_t* offsets, hipStream_t stream);
+
+/* Host only: bytes of device workspace mbq_route_mlp needs for t tokens of k inputs and
+ * `hidden` hidden units: float32 partial hidden sums, c * t * hidden * 4 bytes, where c
+ * is the number of K chunks the launch uses (c <= 64, chosen from t, k and hidden only).
+ * 0 when t == 0. */
+mbq_status mbq_route_mlp_workspace(int32_t t, int32_t k, int32_t hidden, size_t* bytes);
+
+/*
+ * MoBiRoute in the pages' own form (English page section 2.B; Japanese page section 2.2):
+ * a 2-layer MLP scores each token once per residual slice, and a sigmoid gate with
+ * threshold delta turns the scores into a binary slice mask (a larger delta activates
+ * fewer slices, so delta sets the average bit width at run time).
+ *   x:       [t x k] tokens (float32 or bfloat16), or NULL to gate the caller's `scores`
+ *            instead ("scores-in" mode; w1, b1, w2, b2 and workspace are then ignored).
+ *   w1:      [hidden x k] bfloat16 bit patterns, row-major (row u = input weights of
+ *            hidden unit u).  float32 x is multiplied as a bfloat16 hi + lo pair.
+ *   b1:      [hidden] float32, 16-byte aligned.
+ *   w2:      [hidden x (s - 1)] float32, row-major.   b2: [s - 1] float32.
+ *   delta:   gate threshold; delta <= 0 passes every slice, delta >= 1 none; NaN is
+ *            MBQ_ERR_RANGE.
+ *   scores:  [t x (s - 1)] float32; written (x != NULL) or read (x == NULL); may be NULL
+ *            when s == 1.  scores = ReLU(x . W1^T + b1) . W2 + b2, float32 accumulation
+ *            in a fixed order (identical from run to run).
+ *   budget:  [t] int32 out, b(t) = 1 + #leading j with scores[t][j] > float32(logit(delta)).
+ *   perm, offsets: as in mbq_route.
+ *   workspace: at least mbq_route_mlp_workspace() bytes, 16-byte aligned (may be NULL when
+ *            that is 0 or in scores-in mode); overwritten.
+ * hidden must be a multiple of 64 in [64, 4096]; t * k * sizeof(x) and hidden * k * 2
+ * must stay below 2^31 bytes.  NaN scores are outside the contract.  1 <= s <= 4.
+ */
+mbq_status mbq_route_mlp(int32_t t, int32_t k, int32_t s, int32_t hidden, const void* x,
+                         mbq_dtype x_dtype, const uint16_t* w1, const float* b1,
+                         const float* w2, const float* b2, double delta, float* scores,
+                         int32_t* budget, int32_t* perm, int32_t* offsets, void* workspace,
+                         size_t ws_bytes, hipStream_t stream);
 
 /* Host only: bytes of device workspace mbq_linear needs for t tokens (0 when none).
  * Decode (1 <= t <= 64) over more k tiles of 256 inputs than one workgroup holds (8 waves

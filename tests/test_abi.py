@@ -105,6 +105,56 @@ def test_route_and_regroup_validation():
     assert L.mbq_regroup(-2, 3, f, f, f, None) == SHAPE
 
 
+def mlp_ws(t, k, h):
+    n = ctypes.c_size_t(123)
+    st = L.mbq_route_mlp_workspace(t, k, h, ctypes.byref(n))
+    return st, n.value
+
+
+def test_route_mlp_validation():
+    f = P(FAKE)
+    st, need = mlp_ws(16, 3584, 256)
+    assert st == OK and need > 0
+    ws = ctypes.c_size_t(need)
+
+    def call(t=16, k=3584, s=3, h=256, x=f, xd=BF16, w1=f, b1=f, w2=f, b2=f, delta=0.5,
+             scores=f, budget=f, perm=f, offsets=f, ws_p=f, ws_b=None):
+        return L.mbq_route_mlp(t, k, s, h, x, xd, w1, b1, w2, b2, delta, scores, budget, perm,
+                               offsets, ws_p, need if ws_b is None else ws_b, None)
+
+    assert call(s=0) == UNSUP and call(s=5) == UNSUP
+    assert call(t=-1) == SHAPE and call(t=(1 << 24) + 1) == SHAPE
+    assert call(delta=float("nan")) == RANGE
+    assert call(offsets=None) == ARG
+    assert call(budget=None) == ARG and call(perm=None) == ARG and call(scores=None) == ARG
+    assert call(h=0) == SHAPE and call(h=96) == SHAPE and call(h=4160) == SHAPE
+    assert call(k=0) == SHAPE
+    assert call(xd=7) == ARG
+    for name in ("w1", "b1", "w2", "b2"):
+        assert call(**{name: None}) == ARG
+    assert call(b1=P(FAKE + 4)) == ARG           # b1 is read as float4
+    assert call(x=P(FAKE + 1)) == ARG and call(w1=P(FAKE + 1)) == ARG
+    assert call(ws_p=None) == WS and call(ws_b=need - 1) == WS and call(ws_p=P(FAKE + 4)) == WS
+    assert call(t=1 << 20, k=1 << 10, xd=F32, ws_b=1 << 40) == SHAPE   # x of 4 GiB
+    assert call(h=4096, k=1 << 18, ws_b=1 << 40) == SHAPE              # W1 of 2 GiB
+    # scores-in mode needs no weights and no workspace; s == 1 needs no scores
+    # (these would launch, so only their argument checks are exercised by a bad stream-free
+    #  field: a misaligned perm)
+    assert call(x=None, w1=None, b1=None, w2=None, b2=None, ws_p=None, perm=P(FAKE + 2)) == ARG
+    assert call(s=1, scores=None, ws_p=None, perm=P(FAKE + 2)) == ARG
+
+
+@pytest.mark.parametrize("t,k,h,chunks", [
+    (16, 3584, 256, 14), (1, 3584, 256, 14), (64, 5120, 256, 16), (65, 5120, 256, 16),
+    (2048, 3584, 256, 8), (2048, 4096, 512, 4), (17, 100, 64, 1), (5, 256, 128, 1),
+    (300, 64, 64, 1), (1024, 13824, 192, 16)])
+def test_route_mlp_workspace(t, k, h, chunks):
+    st, n = mlp_ws(t, k, h)
+    assert st == OK and n == chunks * t * h * 4
+    assert mlp_ws(0, k, h) == (OK, 0)
+    assert mlp_ws(t, k, 100)[0] == SHAPE
+
+
 def test_linear_validation_and_workspace():
     st, d = desc(200, 640, 128, 3)
     dp = ctypes.byref(d)

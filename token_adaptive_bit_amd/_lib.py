@@ -18,8 +18,9 @@ ABI_VERSION = 1
 STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANGE",
           -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}
 
-EXPORTS = ("mbq_describe", "mbq_pack", "mbq_route", "mbq_regroup", "mbq_linear_workspace",
-           "mbq_linear", "mbq_status_str", "mbq_abi_version")
+EXPORTS = ("mbq_describe", "mbq_pack", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
+           "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_status_str",
+           "mbq_abi_version")
 
 
 class MbqDesc(ctypes.Structure):
@@ -59,6 +60,9 @@ def _load() -> ctypes.CDLL:
     lib.mbq_pack.argtypes = [D, VP, I32, VP, VP, VP]
     lib.mbq_route.argtypes = [I32, I32, I32, VP, I32, VP, VP, VP, VP, VP, VP]
     lib.mbq_regroup.argtypes = [I32, I32, VP, VP, VP, VP]
+    lib.mbq_route_mlp_workspace.argtypes = [I32, I32, I32, P(ctypes.c_size_t)]
+    lib.mbq_route_mlp.argtypes = [I32, I32, I32, I32, VP, I32, VP, VP, VP, VP, ctypes.c_double,
+                                  VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
     lib.mbq_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
     lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, VP]
     lib.mbq_status_str.argtypes = [I32]
@@ -94,4 +98,10 @@ def workspace_bytes(desc: MbqDesc, t: int, x_dtype: int) -> int:
     n = ctypes.c_size_t(0)
     check(LIB.mbq_linear_workspace(ctypes.byref(desc), t, x_dtype, ctypes.byref(n)),
           "mbq_linear_workspace")
+    return int(n.value)
+
+
+def route_mlp_workspace_bytes(t: int, k: int, hidden: int) -> int:
+    n = ctypes.c_size_t(0)
+    check(LIB.mbq_route_mlp_workspace(t, k, hidden, ctypes.byref(n)), "mbq_route_mlp_workspace")
     return int(n.value)

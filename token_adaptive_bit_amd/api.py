@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import MBQ_BF16, MBQ_F32, MbqDesc, MbqError, check, describe
 
 __all__ = ["PackedLinear", "pack", "route", "route_from_logits", "regroup", "linear",
-           "linear_workspace", "describe", "MbqError"]
+           "linear_workspace", "describe", "MbqError", "MlpRouter", "route_mlp",
+           "route_mlp_from_scores", "route_mlp_workspace"]
 
 
 def _stream() -> ctypes.c_void_p:
@@ -116,6 +117,75 @@ def regroup(budget: torch.Tensor, slices: int, perm=None, offsets=None):
     check(_lib.LIB.mbq_regroup(t, slices, _p(budget), _p(perm), _p(offsets), _stream()),
           "mbq_regroup")
     return perm, offsets
+
+
+@dataclass
+class MlpRouter:
+    """Weights of the 2-layer MLP router on the device.
+
+    w1 [hidden, k] bfloat16, b1 [hidden] float32, w2 [hidden, slices - 1] float32,
+    b2 [slices - 1] float32.
+    """
+    w1: torch.Tensor
+    b1: torch.Tensor
+    w2: torch.Tensor
+    b2: torch.Tensor
+
+    @property
+    def hidden(self): return self.w1.shape[0]
+
+    @property
+    def k(self): return self.w1.shape[1]
+
+    @property
+    def slices(self): return self.w2.shape[1] + 1
+
+
+def route_mlp_workspace(t: int, k: int, hidden: int) -> int:
+    return _lib.route_mlp_workspace_bytes(t, k, hidden)
+
+
+def _mlp_outputs(t, s, dev, scores, budget, perm, offsets):
+    scores = torch.empty((t, s - 1), dtype=torch.float32, device=dev) if scores is None else scores
+    budget = torch.empty(t, dtype=torch.int32, device=dev) if budget is None else budget
+    perm = torch.empty(t, dtype=torch.int32, device=dev) if perm is None else perm
+    offsets = torch.empty(s + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    return scores, budget, perm, offsets
+
+
+def route_mlp(x: torch.Tensor, r: MlpRouter, delta: float, scores=None, budget=None, perm=None,
+              offsets=None, workspace: torch.Tensor | None = None):
+    """MLP router scores, threshold-delta budgets and the stable regroup."""
+    _dev(x, "x")
+    for name in ("w1", "b1", "w2", "b2"):
+        _dev(getattr(r, name), name)
+    if r.w1.dtype != torch.bfloat16:
+        raise TypeError("w1 must be bfloat16")
+    t, k = x.shape
+    s = r.slices
+    scores, budget, perm, offsets = _mlp_outputs(t, s, x.device, scores, budget, perm, offsets)
+    need = route_mlp_workspace(t, k, r.hidden)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    check(_lib.LIB.mbq_route_mlp(t, k, s, r.hidden, _p(x), _dtype(x), _p(r.w1), _p(r.b1),
+                                 _p(r.w2), _p(r.b2), float(delta), _p(scores), _p(budget),
+                                 _p(perm), _p(offsets), _p(workspace), ws_bytes, _stream()),
+          "mbq_route_mlp")
+    return scores, budget, perm, offsets
+
+
+def route_mlp_from_scores(scores: torch.Tensor, delta: float, budget=None, perm=None,
+                          offsets=None):
+    """Threshold-delta budgets and regroup from given float32 scores [t, slices - 1]."""
+    _dev(scores, "scores")
+    t, r = scores.shape
+    s = r + 1
+    _, budget, perm, offsets = _mlp_outputs(t, s, scores.device, scores, budget, perm, offsets)
+    check(_lib.LIB.mbq_route_mlp(t, 0, s, 0, None, MBQ_F32, None, None, None, None, float(delta),
+                                 _p(scores), _p(budget), _p(perm), _p(offsets), None, 0,
+                                 _stream()), "mbq_route_mlp")
+    return budget, perm, offsets
 
 
 def linear_workspace(p: PackedLinear, t: int, x_dtype=torch.bfloat16) -> int:

@@ -26,6 +26,7 @@ SOURCES = {
     "api.hip": [],
     "pack.hip": ["-ffp-contract=off"],
     "route.hip": [],
+    "route_mlp.hip": [],
     "decode.hip": [],
     "decode_stream.hip": [],
     "prefill.hip": [],
@@ -36,7 +37,7 @@ SOURCES = {
 # exact waits on the in-order memory counter, which spill traffic (scratch loads and
 # stores) would stall, and the variants a launcher can pick are chosen to fit.  The build
 # reads the compiler's resource-usage remarks and fails on any spill to scratch memory.
-SPILL_FREE = ("decode_stream.hip", "prefill_mfma.hip")
+SPILL_FREE = ("decode_stream.hip", "prefill_mfma.hip", "route_mlp.hip")
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -1,5 +1,6 @@
 // Host side of the C ABI: validation, geometry, dispatch.  No device work happens here
 // until every argument has been checked, so all error paths run without a GPU.
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 
@@ -114,6 +115,58 @@ mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* per
   if (!aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4)) return MBQ_ERR_ARG;
   return launched(mbq::launch_route(t, 0, s, nullptr, false, nullptr, nullptr, budget,
                                     nullptr, perm, offsets, stream));
+}
+
+namespace {
+bool mlp_shape_ok(int32_t t, int32_t k, int32_t hidden) {
+  return t >= 0 && t <= (1 << 24) && k >= 1 && hidden >= 64 && hidden <= 4096 && hidden % 64 == 0;
+}
+}  // namespace
+
+mbq_status mbq_route_mlp_workspace(int32_t t, int32_t k, int32_t hidden, size_t* bytes) {
+  if (!bytes) return MBQ_ERR_ARG;
+  if (!mlp_shape_ok(t, k, hidden)) return MBQ_ERR_SHAPE;
+  *bytes = mbq::route_mlp_workspace(t, k, hidden);
+  return MBQ_OK;
+}
+
+mbq_status mbq_route_mlp(int32_t t, int32_t k, int32_t s, int32_t hidden, const void* x,
+                         mbq_dtype x_dtype, const uint16_t* w1, const float* b1,
+                         const float* w2, const float* b2, double delta, float* scores,
+                         int32_t* budget, int32_t* perm, int32_t* offsets, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (s < 1 || s > 4) return MBQ_ERR_UNSUPPORTED;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (std::isnan(delta)) return MBQ_ERR_RANGE;
+  if (!offsets) return MBQ_ERR_ARG;
+  if (t > 0 && (!budget || !perm || (s > 1 && !scores))) return MBQ_ERR_ARG;
+  if (!aligned(scores, 4) || !aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4))
+    return MBQ_ERR_ARG;
+  const bool compute = x && t > 0 && s > 1;
+  if (compute) {
+    if (!mlp_shape_ok(t, k, hidden)) return MBQ_ERR_SHAPE;
+    if (!valid_dtype(x_dtype) || !w1 || !b1 || !w2 || !b2) return MBQ_ERR_ARG;
+    const size_t esz = x_dtype == MBQ_F32 ? 4 : 2;
+    if (!aligned(x, esz) || !aligned(w1, 2) || !aligned(b1, 16) || !aligned(w2, 4) ||
+        !aligned(b2, 4))
+      return MBQ_ERR_ARG;
+    if (size_t(t) * size_t(k) * esz >= (size_t(1) << 31) ||
+        size_t(hidden) * size_t(k) * 2 >= (size_t(1) << 31))
+      return MBQ_ERR_SHAPE;
+    const size_t need = mbq::route_mlp_workspace(t, k, hidden);
+    if (need && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MBQ_ERR_WORKSPACE;
+  }
+  // theta = logit(delta): sigmoid(score) > delta exactly when score > theta
+  double th;
+  if (delta <= 0.0)
+    th = -HUGE_VAL;
+  else if (delta >= 1.0)
+    th = HUGE_VAL;
+  else
+    th = std::log(delta) - std::log1p(-delta);
+  return launched(mbq::launch_route_mlp(t, k, s, hidden, compute ? x : nullptr,
+                                        x_dtype == MBQ_BF16, w1, b1, w2, b2, float(th), scores,
+                                        budget, perm, offsets, workspace, stream));
 }
 
 mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,

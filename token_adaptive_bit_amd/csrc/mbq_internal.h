@@ -41,6 +41,11 @@ hipError_t launch_pack(const mbq_desc& d, const void* w, bool w_bf16, void* pack
 hipError_t launch_route(int32_t t, int32_t k, int32_t s, const void* x, bool x_bf16,
                         const float* wr, float* logits, const int32_t* budget_in,
                         int32_t* budget, int32_t* perm, int32_t* offsets, hipStream_t stream);
+size_t route_mlp_workspace(int32_t t, int32_t k, int32_t h);
+hipError_t launch_route_mlp(int32_t t, int32_t k, int32_t s, int32_t h, const void* x, bool x_bf16,
+                            const uint16_t* w1, const float* b1, const float* w2, const float* b2,
+                            float theta, float* scores, int32_t* budget, int32_t* perm,
+                            int32_t* offsets, void* ws, hipStream_t stream);
 size_t decode_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
 hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                          bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
