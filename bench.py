@@ -85,6 +85,30 @@ def time_events(torch, fn, iters):
     return sum(a.elapsed_time(b) for a, b in zip(s, e)) / iters / 1e3
 
 
+def graph_time(torch, fn, calls=10, replays=5):
+    """Average device time (s) of fn() from replays of a HIP graph holding `calls` calls
+    (no host launch overhead between kernels)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                      # first use on the capture stream, outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / (calls * replays)
+
+
 def traffic_from_profile(kernel_src: str, name: str):
     """HBM bytes per launch from committed rocprofv3 counters, if the kernel is unchanged."""
     path = os.path.join(ROOT, "profiles", name)
@@ -234,11 +258,19 @@ def bench_route_mlp(api, torch, inputs, dev, iters=50):
         for _ in range(3):
             api.route_mlp(X, R, 0.5, sc, b, perm, off, workspace=ws)
         torch.cuda.synchronize()
-        t_mlp = time_events(torch, lambda i: api.route_mlp(X, R, 0.5, sc, b, perm, off, workspace=ws), iters)
+        b_eager = b.clone()
         lg, lb, lp, lo = api.route(X, Wr)
+        torch.cuda.synchronize()
+        t_mlp = time_events(torch, lambda i: api.route_mlp(X, R, 0.5, sc, b, perm, off, workspace=ws), iters)
         t_lin = time_events(torch, lambda i: api.route(X, Wr, lg, lb, lp, lo), iters)
-        res = {"us": t_mlp * 1e6, "linear_router_us": t_lin * 1e6,
-               "hidden_tflops_incl_gate": 2.0 * T * K * 256 / t_mlp / 1e12,
+        # device time without host launch overhead: 10 calls captured in a HIP graph
+        g_mlp = graph_time(torch, lambda: api.route_mlp(X, R, 0.5, sc, b, perm, off, workspace=ws))
+        ok = bool(torch.equal(b, b_eager))
+        g_lin = graph_time(torch, lambda: api.route(X, Wr, lg, lb, lp, lo))
+        res = {"us_per_call_eager": t_mlp * 1e6, "us_per_call_graph": g_mlp * 1e6,
+               "linear_router_us_eager": t_lin * 1e6, "linear_router_us_graph": g_lin * 1e6,
+               "graph_replay_matches_eager": ok,
+               "hidden_tflops_graph": 2.0 * T * K * 256 / g_mlp / 1e12,
                "budget_counts_delta_0.5": torch.diff(off).cpu().tolist()}
         sweep = {}
         for delta in (0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9):

@@ -350,22 +350,21 @@ __device__ __forceinline__ int token_budget(int t, int T, int H, int KS, const f
 #pragma unroll
     for (int r = 0; r < R; ++r) sc[r] = 0.f;
     for (int h = 4 * lane; h < H; h += 256) {
-      // chunk partials in a fixed order; eight loads are issued before the first add
-      auto ld = [&](int ks) {
-        return *reinterpret_cast<const float4*>(part + (size_t(ks) * T + t) * H + h);
-      };
-      float4 a = ld(0);
-      int ks = 1;
-      for (; ks + 8 <= KS; ks += 8) {
-        float4 p[8];
+      // Chunk partials summed in chunk order.  Sixteen loads are issued before the first
+      // add; past the last chunk the index is clamped and the term weighted by 0, which
+      // leaves the sum unchanged (a + 1 * p rounds like a + p; a + 0 * p is a).
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k0 = 0; k0 < KS; k0 += 16) {
+        float4 p[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = ld(ks + i);
+        for (int i = 0; i < 16; ++i)
+          p[i] = *reinterpret_cast<const float4*>(part + (size_t(min(k0 + i, KS - 1)) * T + t) * H + h);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { a.x += p[i].x; a.y += p[i].y; a.z += p[i].z; a.w += p[i].w; }
-      }
-      for (; ks < KS; ++ks) {
-        const float4 p = ld(ks);
-        a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
+        for (int i = 0; i < 16; ++i) {
+          const float m = k0 + i < KS ? 1.f : 0.f;
+          a.x = fmaf(p[i].x, m, a.x); a.y = fmaf(p[i].y, m, a.y);
+          a.z = fmaf(p[i].z, m, a.z); a.w = fmaf(p[i].w, m, a.w);
+        }
       }
       const float4 bb = *reinterpret_cast<const float4*>(b1 + h);
       const float hv[4] = {fmaxf(a.x + bb.x, 0.f), fmaxf(a.y + bb.y, 0.f), fmaxf(a.z + bb.z, 0.f),
