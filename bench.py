@@ -296,36 +296,51 @@ def bench_route_mlp(api, torch, inputs, dev, iters=50):
 
 def bench_layer(api, torch, inputs, dev, iters=20):
     """Seven linears of a 14B-like decoder layer at T = 64 with one router on the layer
-    input: total time of route + 7 routed linears, and HBM fraction of the linears."""
+    input: total time of route + 7 routed linears, and HBM fraction of the linears; then
+    the same layer with q/k/v and gate/up fused (one blob and one launch per shared input):
+    route + 4 routed linears."""
     cfg = inputs.make_config(4)
     T = cfg["T"]
     x0 = torch.from_numpy(cfg["X_layer"]).to(dev, torch.bfloat16)
     Wr = torch.from_numpy(cfg["Wr"]).to(dev, torch.float32)
-    packs, xs, ys = [], [], []
-    for lin in cfg["linears"]:
-        W = torch.from_numpy(lin["W"]).to(dev, torch.bfloat16)
-        packs.append(api.pack(W, 128, 3))
-        xs.append(torch.from_numpy(lin["X"]).to(dev, torch.bfloat16))
-        ys.append(torch.empty((T, W.shape[0]), dtype=torch.bfloat16, device=dev))
-        del W
-    torch.cuda.synchronize()
+    lin = {l["name"]: l for l in cfg["linears"]}
+    Wd = {n: torch.from_numpy(l["W"]).to(dev, torch.bfloat16) for n, l in lin.items()}
+    Xd = {n: torch.from_numpy(l["X"]).to(dev, torch.bfloat16) for n, l in lin.items()}
     _, _, perm, off = api.route(x0, Wr)
 
-    def step(i):
-        api.route(x0, Wr, perm=perm, offsets=off)
-        for p, x, y in zip(packs, xs, ys):
-            api.linear(p, x, perm, off, y=y)
+    def run(groups):
+        # groups: (weight names, activation name) sharing one blob and one launch
+        packs, xs, ys = [], [], []
+        for names, xn in groups:
+            p, _ = api.pack_concat([Wd[n] for n in names], 128, 3)
+            packs.append(p)
+            xs.append(x0 if xn == "layer" else Xd[xn])
+            ys.append(torch.empty((T, p.n), dtype=torch.bfloat16, device=dev))
+        torch.cuda.synchronize()
 
-    for i in range(3):
-        step(i)
-    torch.cuda.synchronize()
-    s = time_events(torch, step, iters)
-    counts = torch.diff(off).cpu().tolist()
-    jmax = max(j + 1 for j in range(3) if counts[j] > 0)
-    nbytes = sum(decode_bytes(p, T, jmax) for p in packs)
-    return {"T": T, "us": s * 1e6, "tokens_per_s": T / s, "budget_counts": counts,
-            "hbm_frac_incl_route": nbytes / s / 1e9 / HBM_PEAK_GBS,
-            "note": "weights are not rotated: the 7 packed linears (267 MB) exceed the 256 MiB cache"}
+        def step(i):
+            api.route(x0, Wr, perm=perm, offsets=off)
+            for p, x, y in zip(packs, xs, ys):
+                api.linear(p, x, perm, off, y=y)
+
+        for i in range(3):
+            step(i)
+        torch.cuda.synchronize()
+        s = time_events(torch, step, iters)
+        counts = torch.diff(off).cpu().tolist()
+        jmax = max(j + 1 for j in range(3) if counts[j] > 0)
+        nbytes = sum(decode_bytes(p, T, jmax) for p in packs)
+        return {"us": s * 1e6, "tokens_per_s": T / s, "launches": 1 + len(packs),
+                "budget_counts": counts, "hbm_frac_incl_route": nbytes / s / 1e9 / HBM_PEAK_GBS}
+
+    out = {"T": T}
+    out["separate"] = run([([n], "layer" if n == "q" else n) for n in lin])
+    out["fused_qkv_gateup"] = run([(["q", "k", "v"], "layer"), (["o"], "o"), (["gate", "up"], "gate"),
+                                   (["down"], "down")])
+    out["note"] = ("weights are not rotated: the 7 packed linears (267 MB) exceed the 256 MiB cache; "
+                   "router logits are not fused into the previous op (norm and residual lie outside "
+                   "this path)")
+    return out
 
 
 def run_traffic(api, torch, inputs, dev, T, launches=20):

@@ -115,6 +115,22 @@ mbq_status mbq_pack(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void
                     int32_t* dev_status, hipStream_t stream);
 
 /*
+ * MoBiSlice pack of a row range: W_part [rows x k] becomes rows row0 .. row0 + rows - 1 of
+ * the blob described by desc (desc->n rows in all).  Quantization groups lie within one
+ * row, so the codes and params of those rows are exactly what mbq_pack of the whole
+ * weight would write.  This lets weights that read the same activations (q/k/v, gate/up)
+ * share one blob and one routed linear launch (English page section 4: the kernels'
+ * efficiency at decoder-layer sizes).
+ *   row0:   multiple of 16; rows >= 1; row0 + rows <= desc->n; rows is a multiple of 16
+ *           unless the part ends the blob (MBQ_ERR_SHAPE otherwise).
+ *   The blob is fully defined once parts cover rows 0 .. desc->n - 1; the part holding
+ *   the last row also writes the blob's trailing alignment bytes.  Parts write disjoint
+ *   bytes and may run concurrently.  w, dev_status: as in mbq_pack.
+ */
+mbq_status mbq_pack_rows(const mbq_desc* desc, int32_t row0, int32_t rows, const void* w,
+                         mbq_dtype w_dtype, void* packed, int32_t* dev_status, hipStream_t stream);
+
+/*
  * MoBiRoute (English page section 2.B; Japanese page section 2.2), linear-argmax form.
  *   x:       [t x k] tokens (float32 or bfloat16), or NULL to route from the caller's
  *            `logits` instead ("logits-in" mode).

@@ -90,6 +90,20 @@ def test_pack_validation():
     assert L.mbq_pack(ctypes.byref(bad), P(FAKE), F32, P(FAKE), None, None) == SHAPE
 
 
+def test_pack_rows_validation():
+    st, d = desc(100, 512, 128, 3)
+    dp, f = ctypes.byref(d), P(FAKE)
+    assert L.mbq_pack_rows(dp, 8, 16, f, F32, f, None, None) == SHAPE      # row0 not on a block
+    assert L.mbq_pack_rows(dp, 0, 0, f, F32, f, None, None) == SHAPE       # no rows
+    assert L.mbq_pack_rows(dp, -16, 16, f, F32, f, None, None) == SHAPE
+    assert L.mbq_pack_rows(dp, 96, 16, f, F32, f, None, None) == SHAPE     # past n
+    assert L.mbq_pack_rows(dp, 0, 40, f, F32, f, None, None) == SHAPE      # partial block mid-blob
+    assert L.mbq_pack_rows(dp, 0, 16, None, F32, f, None, None) == ARG
+    assert L.mbq_pack_rows(dp, 0, 16, f, 5, f, None, None) == ARG
+    assert L.mbq_pack_rows(dp, 0, 16, f, F32, P(FAKE + 16), None, None) == ARG
+    assert L.mbq_pack_rows(None, 0, 16, f, F32, f, None, None) == ARG
+
+
 def test_route_and_regroup_validation():
     f = P(FAKE)
     assert L.mbq_route(4, 16, 0, f, F32, f, f, f, f, f, None) == UNSUP

@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import MBQ_BF16, MBQ_F32, MbqDesc, MbqError, check, describe
 
-__all__ = ["PackedLinear", "pack", "route", "route_from_logits", "regroup", "linear",
+__all__ = ["PackedLinear", "pack", "pack_concat", "route", "route_from_logits", "regroup", "linear",
            "linear_workspace", "describe", "MbqError", "MlpRouter", "route_mlp",
            "route_mlp_from_scores", "route_mlp_workspace"]
 
@@ -76,6 +76,26 @@ def pack(w: torch.Tensor, group: int = 128, slices: int = 3, status: torch.Tenso
     check(_lib.LIB.mbq_pack(ctypes.byref(d), _p(w), _dtype(w), _p(out), _p(status), _stream()),
           "mbq_pack")
     return PackedLinear(d, out)
+
+
+def pack_concat(ws, group: int = 128, slices: int = 3, status: torch.Tensor | None = None):
+    """One blob for weights that read the same activations: W_i [n_i, k] packed as the row
+    concatenation (every n_i but the last a multiple of 16).  Returns the PackedLinear and
+    the first output column of each weight in the fused output."""
+    k = ws[0].shape[1]
+    n = sum(w.shape[0] for w in ws)
+    d = describe(n, k, group, slices)
+    out = torch.empty(int(d.total_bytes), dtype=torch.uint8, device=ws[0].device)
+    starts, row0 = [], 0
+    for w in ws:
+        _dev(w, "w")
+        if w.shape[1] != k:
+            raise ValueError("all weights must have the same number of inputs")
+        check(_lib.LIB.mbq_pack_rows(ctypes.byref(d), row0, w.shape[0], _p(w), _dtype(w), _p(out),
+                                     _p(status), _stream()), "mbq_pack_rows")
+        starts.append(row0)
+        row0 += w.shape[0]
+    return PackedLinear(d, out), starts
 
 
 def route(x: torch.Tensor, wr: torch.Tensor, logits=None, budget=None, perm=None, offsets=None):

@@ -86,7 +86,22 @@ mbq_status mbq_pack(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void
   if (!valid_dtype(w_dtype) || !w || !packed) return MBQ_ERR_ARG;
   if (!aligned(packed, 256) || !aligned(w, w_dtype == MBQ_F32 ? 4 : 2)) return MBQ_ERR_ARG;
   if (dev_status && !aligned(dev_status, 4)) return MBQ_ERR_ARG;
-  return launched(mbq::launch_pack(*desc, w, w_dtype == MBQ_BF16, packed, dev_status, stream));
+  return launched(mbq::launch_pack(*desc, 0, desc->n, w, w_dtype == MBQ_BF16, packed, dev_status,
+                                   stream));
+}
+
+mbq_status mbq_pack_rows(const mbq_desc* desc, int32_t row0, int32_t rows, const void* w,
+                         mbq_dtype w_dtype, void* packed, int32_t* dev_status, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (!valid_dtype(w_dtype) || !w || !packed) return MBQ_ERR_ARG;
+  if (!aligned(packed, 256) || !aligned(w, w_dtype == MBQ_F32 ? 4 : 2)) return MBQ_ERR_ARG;
+  if (dev_status && !aligned(dev_status, 4)) return MBQ_ERR_ARG;
+  // whole row blocks only: a part starts on a block and fills its blocks unless it ends the blob
+  if (row0 < 0 || rows < 1 || row0 % 16 != 0 || int64_t(row0) + rows > desc->n) return MBQ_ERR_SHAPE;
+  if (rows % 16 != 0 && row0 + rows != desc->n) return MBQ_ERR_SHAPE;
+  return launched(mbq::launch_pack(*desc, row0, rows, w, w_dtype == MBQ_BF16, packed, dev_status,
+                                   stream));
 }
 
 mbq_status mbq_route(int32_t t, int32_t k, int32_t s, const void* x, mbq_dtype x_dtype,

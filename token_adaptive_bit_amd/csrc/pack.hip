@@ -20,17 +20,20 @@
 namespace mbq {
 namespace {
 
+// w holds the N rows being packed; they land in row blocks nb0 .. of a blob of NBT row
+// blocks (a part of a larger weight when nb0 > 0 or N < 16 NBT: groups are per row, so
+// packing rows on their own gives the same codes as packing them with their neighbours).
 template <int G, bool BF16>
 __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, int N, int K,
                                                   int S, int KB, int NG, uint64_t slice_stride,
-                                                  uint64_t params_offset,
+                                                  uint64_t params_offset, int nb0, int NBT,
                                                   uint8_t* __restrict__ packed,
                                                   int32_t* __restrict__ status) {
   constexpr int kWordsPerGroup = G / 64;
   constexpr int kGroupsPerTile = 256 / G;
-  const int kb = blockIdx.x, nb = blockIdx.y;
+  const int kb = blockIdx.x, nb = nb0 + blockIdx.y;
   const int lane = threadIdx.x, r = lane & 15, c = lane >> 4;
-  const int n = nb * 16 + r;
+  const int n = blockIdx.y * 16 + r;  // row of w
 
   float R[4][16];
   int bad = 0;
@@ -100,10 +103,10 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
     u32x4_t v = {word[0], word[1], word[2], word[3]};
     *reinterpret_cast<u32x4_t*>(slice + (size_t(nb) * KB + kb) * kTileBytes + 16 * lane) = v;
   }
-  // The first wave also clears each slice's alignment gap after its params, so that the
-  // whole blob is defined.
-  if (kb == 0 && nb == 0) {
-    const uint64_t used = params_offset + uint64_t(gridDim.y) * NG * 64;
+  // The wave of the blob's last row block and first k tile also clears each slice's
+  // alignment gap after its params, so that the whole blob is defined.
+  if (kb == 0 && nb == NBT - 1) {
+    const uint64_t used = params_offset + uint64_t(NBT) * NG * 64;
     for (int j = 0; j < S; ++j)
       for (uint64_t off = used + 4 * lane; off < slice_stride; off += 256)
         *reinterpret_cast<uint32_t*>(packed + uint64_t(j) * slice_stride + off) = 0u;
@@ -112,27 +115,30 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
 }
 
 template <int G>
-hipError_t launch_g(const mbq_desc& d, const void* w, bool w_bf16, void* packed,
-                    int32_t* st, hipStream_t stream) {
-  dim3 grid(d.k_tiles, d.row_blocks), block(64);
+hipError_t launch_g(const mbq_desc& d, int32_t row0, int32_t rows, const void* w, bool w_bf16,
+                    void* packed, int32_t* st, hipStream_t stream) {
+  dim3 grid(d.k_tiles, (rows + 15) / 16), block(64);
   auto* out = static_cast<uint8_t*>(packed);
+  const int nb0 = row0 / 16;
   if (w_bf16)
-    hipLaunchKernelGGL((pack_kernel<G, true>), grid, block, 0, stream, w, d.n, d.k, d.slices,
-                       d.k_tiles, d.groups_padded, d.slice_stride, d.params_offset, out, st);
+    hipLaunchKernelGGL((pack_kernel<G, true>), grid, block, 0, stream, w, rows, d.k, d.slices,
+                       d.k_tiles, d.groups_padded, d.slice_stride, d.params_offset, nb0,
+                       d.row_blocks, out, st);
   else
-    hipLaunchKernelGGL((pack_kernel<G, false>), grid, block, 0, stream, w, d.n, d.k, d.slices,
-                       d.k_tiles, d.groups_padded, d.slice_stride, d.params_offset, out, st);
+    hipLaunchKernelGGL((pack_kernel<G, false>), grid, block, 0, stream, w, rows, d.k, d.slices,
+                       d.k_tiles, d.groups_padded, d.slice_stride, d.params_offset, nb0,
+                       d.row_blocks, out, st);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_pack(const mbq_desc& d, const void* w, bool w_bf16, void* packed,
-                       int32_t* st, hipStream_t stream) {
+hipError_t launch_pack(const mbq_desc& d, int32_t row0, int32_t rows, const void* w, bool w_bf16,
+                       void* packed, int32_t* st, hipStream_t stream) {
   switch (d.group) {
-    case 64: return launch_g<64>(d, w, w_bf16, packed, st, stream);
-    case 128: return launch_g<128>(d, w, w_bf16, packed, st, stream);
-    default: return launch_g<256>(d, w, w_bf16, packed, st, stream);
+    case 64: return launch_g<64>(d, row0, rows, w, w_bf16, packed, st, stream);
+    case 128: return launch_g<128>(d, row0, rows, w, w_bf16, packed, st, stream);
+    default: return launch_g<256>(d, row0, rows, w, w_bf16, packed, st, stream);
   }
 }
 
