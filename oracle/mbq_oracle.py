@@ -35,6 +35,10 @@ Readings where the pages leave a step open (each one is listed in the design doc):
     Residual slices refine each other, so a token uses the leading run of passing
     slices: b = 1 + its length.  The pages name neither the activation nor the hidden
     width; ReLU is the plainest reading.
+  * The low-rank side path of the TTQ explainer (section 2: W ~ Wq + BA, with the
+    quantized part adjusted and the rank-r factors kept beside it; section 4: r = 16):
+    here Wq is the token's MoBiSlice reconstruction W^(b), and B [N, r], A [r, K] are one
+    pair shared by every token whatever its b, so y_t = x_t . W^(b(t))^T + (x_t . A^T) . B^T.
   * Regrouping is a stable sort of tokens by ascending slice count.
   * Dot products and reconstruction are exact in float64 on the stored codes and params.
 
@@ -241,6 +245,17 @@ def linear(X: np.ndarray, deq: np.ndarray, budget: np.ndarray) -> np.ndarray:
         if idx.size:
             Y[idx] = X[idx] @ reconstruct(deq, b).T
     return Y
+
+
+def lowrank_term(X, A, B) -> np.ndarray:
+    """The rank-r side path (TTQ explainer, section 2): (X . A^T) . B^T in float64, [T, N]."""
+    X, A, B = (np.asarray(a, np.float64) for a in (X, A, B))
+    return (X @ A.T) @ B.T
+
+
+def linear_lowrank(X, deq, budget, A, B) -> np.ndarray:
+    """Routed linear plus the side path: y_t = x_t . W^(b(t))^T + (x_t . A^T) . B^T."""
+    return linear(X, deq, budget) + lowrank_term(X, A, B)
 
 
 # ----------------------------------------------------------------------------------------

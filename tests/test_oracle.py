@@ -355,6 +355,45 @@ def test_average_bits():
     assert O.average_bits(np.array([3, 3]), bits_per_slice=2) == 6.0
 
 
+# ---------------------------------------------------------------- the low-rank side path
+def test_lowrank_zero_factors_leave_the_linear():
+    d = inputs.make_linear(41, 24, 256, 5, group=64, dtype="f32")
+    p = O.pack(d["W"], 64, 3)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 64)
+    b = np.array([1, 2, 3, 2, 1], np.int32)
+    r = inputs.make_lowrank(42, 24, 256, rank=4)
+    base = O.linear(d["X"], deq, b)
+    assert np.array_equal(O.linear_lowrank(d["X"], deq, b, np.zeros_like(r["A"]), r["B"]), base)
+    assert np.array_equal(O.linear_lowrank(d["X"], deq, b, r["A"], np.zeros_like(r["B"])), base)
+
+
+def test_lowrank_equals_effective_weight():
+    # x . (W^(b) + B A)^T computed with the rank-r product formed first (another association)
+    d = inputs.make_linear(43, 20, 512, 6, group=128, dtype="bf16")
+    p = O.pack(d["W"], 128, 3)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 128)
+    b = np.array([3, 1, 2, 2, 3, 1], np.int32)
+    r = inputs.make_lowrank(44, 20, 512, rank=16, b_scale=0.1)
+    got = O.linear_lowrank(d["X"], deq, b, r["A"], r["B"])
+    BA = r["B"].astype(np.float64) @ r["A"].astype(np.float64)
+    for t in range(6):
+        Weff = O.reconstruct(deq, int(b[t])) + BA
+        ref = [sum(float(d["X"][t, k]) * Weff[n, k] for k in range(512)) for n in range(20)]
+        np.testing.assert_allclose(got[t], ref, rtol=0, atol=1e-9)
+
+
+def test_lowrank_rank_one_closed_form_and_additivity():
+    X = np.random.default_rng(45).standard_normal((4, 32))
+    A = np.zeros((1, 32)); A[0, 7] = 1.0
+    B = np.full((5, 1), 0.5)
+    np.testing.assert_array_equal(O.lowrank_term(X, A, B), np.repeat(0.5 * X[:, [7]], 5, axis=1))
+    rng = np.random.default_rng(46)
+    A1, A2 = rng.standard_normal((3, 32)), rng.standard_normal((2, 32))
+    B1, B2 = rng.standard_normal((5, 3)), rng.standard_normal((5, 2))
+    np.testing.assert_allclose(O.lowrank_term(X, np.vstack([A1, A2]), np.hstack([B1, B2])),
+                               O.lowrank_term(X, A1, B1) + O.lowrank_term(X, A2, B2), atol=1e-12)
+
+
 # ---------------------------------------------------------------- the packed blob format
 def test_blob_sizes_match_workloads():
     # 2.25 bits per weight per slice at G=128, 2.5 at G=64 (codes + half scale and zero)

@@ -15,6 +15,9 @@ Draw order for one linear (numpy ``default_rng(seed)``):
   5. Wr = standard_normal((K, S), float32) * 0.1
   6. forced budget mixes: rng.permutation(T) over a block-sorted budget vector
 
+The low-rank side path's factors come from ``make_lowrank``: A ~ N(0, 1/K), B ~ N(0, s^2)
+(s = 0.005 unless stated), both rounded to bfloat16.
+
 The MLP router's weights have a generator of their own (``make_mlp_router``): hidden width
 256 unless stated, W1 ~ N(0, 1/K) rounded to bfloat16 (pre-activations ~ N(0, 1) on the
 activations above), b1 ~ N(0, 0.1^2), W2 ~ N(0, 2/H), b2 ~ N(0, 0.1^2), all float32.
@@ -84,6 +87,19 @@ def make_mlp_router(seed: int, K: int, slices: int = 3, hidden: int = 256) -> di
     b2 = rng.standard_normal(slices - 1, dtype=np.float32) * np.float32(0.1)
     return {"W1": W1, "b1": b1, "W2": W2, "b2": b2, "hidden": hidden, "K": K,
             "slices": slices}
+
+
+def make_lowrank(seed: int, N: int, K: int, rank: int = 16, b_scale: float = 0.005) -> dict:
+    """Synthetic low-rank side-path factors, bfloat16-representable float32.
+
+    Draw order (``default_rng(seed)``): A [rank, K] ~ N(0, 1/K), then B [N, rank] ~
+    N(0, b_scale^2).  With activations ~ N(0, 1), x . A^T is ~ N(0, 1) per rank, so the
+    side path is ~ sqrt(rank) * b_scale per output.
+    """
+    rng = np.random.default_rng(seed)
+    A = round_bf16(rng.standard_normal((rank, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K)))
+    B = round_bf16(rng.standard_normal((N, rank), dtype=np.float32) * np.float32(b_scale))
+    return {"A": A, "B": B, "rank": rank}
 
 
 def forced_mix(T: int, fractions) -> list:
