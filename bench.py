@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=16, help="decode batch (1, 4 or 16)")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer", "traffic", "route_mlp"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer", "traffic", "route_mlp", "lowrank"], default=None,
                     help="run one workload only (for profiling); prints its own JSON line.  "
                          "'traffic' runs a copy kernel of known size and then the decode linear, "
                          "for the FETCH_SIZE / WRITE_SIZE counter passes")
@@ -294,6 +294,46 @@ def bench_route_mlp(api, torch, inputs, dev, iters=50):
     return out
 
 
+def bench_lowrank(api, torch, inputs, dev, iters=30):
+    """The low-rank side path (rank 16) on the decode workload (T = 16) and the prefill
+    workload (T = 2048): routed linear with and without it, and u = x A^T alone."""
+    out = {}
+    for cfg, T in ((2, 16), (3, 2048)):
+        d = inputs.make_config(cfg)
+        N, K = d["N"], d["K"]
+        W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
+        p = api.pack(W, 128, 3)
+        del W
+        X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
+        if d["budget"] is not None:
+            perm, off = api.regroup(torch.from_numpy(d["budget"]).to(dev), 3)
+        else:
+            _, _, perm, off = api.route(X, torch.from_numpy(d["Wr"]).to(dev, torch.float32))
+        lr = inputs.make_lowrank(cfg + 100, N, K, rank=16)
+        A = torch.from_numpy(lr["A"]).to(dev, torch.bfloat16)
+        B = torch.from_numpy(lr["B"]).to(dev, torch.bfloat16)
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        ws0 = torch.empty(max(1, api.linear_workspace(p, T)), dtype=torch.uint8, device=dev)
+        ws1 = torch.empty(max(1, api.linear_lowrank_workspace(p, T, 16)), dtype=torch.uint8, device=dev)
+        plain = lambda i: api.linear(p, X, perm, off, y=y, workspace=ws0)
+        side = lambda i: api.linear_lowrank(p, X, perm, off, A, B, y=y, workspace=ws1)
+        for f in (plain, side):
+            for i in range(3):
+                f(i)
+        torch.cuda.synchronize()
+        t0 = time_events(torch, plain, iters)
+        t1 = time_events(torch, side, iters)
+        res = {"N": N, "K": K, "T": T, "rank": 16, "linear_us": t0 * 1e6, "linear_lowrank_us": t1 * 1e6,
+               "overhead_frac": t1 / t0 - 1.0}
+        if T <= 64:
+            g0 = graph_time(torch, lambda: plain(0))
+            g1 = graph_time(torch, lambda: side(0))
+            res.update({"linear_us_graph": g0 * 1e6, "linear_lowrank_us_graph": g1 * 1e6})
+        out[f"t{T}_{N}x{K}"] = res
+        del p
+    return out
+
+
 def bench_layer(api, torch, inputs, dev, iters=20):
     """Seven linears of a 14B-like decoder layer at T = 64 with one router on the layer
     input: total time of route + 7 routed linears, and HBM fraction of the linears; then
@@ -420,6 +460,9 @@ def main():
     if args.only == "layer":
         print(json.dumps({"workload": "layer", **bench_layer(api, torch, inputs, dev)}))
         return
+    if args.only == "lowrank":
+        print(json.dumps({"workload": "lowrank", **bench_lowrank(api, torch, inputs, dev)}))
+        return
     if args.only == "route_mlp":
         print(json.dumps({"workload": "route_mlp", **bench_route_mlp(api, torch, inputs, dev)}))
         return
@@ -476,6 +519,8 @@ def main():
         extra["sweep_14336x4096"] = bench_sweep(api, torch, inputs, dev)
         log("MLP router with threshold delta")
         extra["route_mlp_h256_s3"] = bench_route_mlp(api, torch, inputs, dev)
+        log("low-rank side path")
+        extra["lowrank_r16"] = bench_lowrank(api, torch, inputs, dev)
         log("14B-like layer, T=64")
         extra["layer14b_t64"] = bench_layer(api, torch, inputs, dev)
         log("pack")

@@ -223,6 +223,34 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
                       void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
                       hipStream_t stream);
 
+/* Host only: bytes of device workspace mbq_linear_lowrank needs: u (t x rank float32,
+ * rounded up to 256 bytes) followed by the routed linear's split-K partials under the
+ * side path's plan (one k tile and one 16-token block per wave).  0 when t == 0. */
+mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
+                                        int32_t rank, size_t* bytes);
+
+/*
+ * Routed linear with a low-rank side path: W ~ W^(b) + B A (TTQ Japanese page, section 2:
+ * a quantized weight plus rank-r factors kept beside it; section 4: rank 16), so
+ *   y_t = x_t . W^(b(t))^T + (x_t . A^T) . B^T
+ * with one (A, B) pair for every token whatever its budget.
+ *   a:     [rank x k] bfloat16 bit patterns, row-major, 16-byte aligned.
+ *   b:     [n x rank] bfloat16 bit patterns, row-major, 16-byte aligned.
+ *   rank:  a multiple of 8 in [8, 32] (MBQ_ERR_UNSUPPORTED otherwise).
+ *   workspace: at least mbq_linear_lowrank_workspace() bytes, 16-byte aligned.
+ *   Other arguments as in mbq_linear.
+ * u = x . A^T is computed first (float32 accumulation over k; float32 x as a bf16 hi + lo
+ * pair), then the linear kernels add u . B^T to their float32 accumulators before the one
+ * rounding to y (u enters their MFMAs as a bf16 hi + lo pair).  Kernels without that
+ * fusion (the generic decode and prefill) add it to y afterwards; bfloat16 y is then
+ * rounded twice.
+ */
+mbq_status mbq_linear_lowrank(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                              mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
+                              const uint16_t* a, const uint16_t* b, int32_t rank, void* y,
+                              mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* Static string for a status code. */
 const char* mbq_status_str(mbq_status status);
 

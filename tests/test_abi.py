@@ -104,6 +104,47 @@ def test_pack_rows_validation():
     assert L.mbq_pack_rows(None, 0, 16, f, F32, f, None, None) == ARG
 
 
+@pytest.mark.parametrize("N,K,G,S,t,rank,chunks", [
+    (18944, 3584, 128, 3, 16, 16, 2),   # 14 k tiles: one tile per wave with the side path
+    (5120, 5120, 128, 3, 64, 16, 3),    # one 16-token block per workgroup
+    (150, 2304, 64, 2, 48, 32, 2),
+    (512, 256, 64, 3, 16, 8, 1),        # K fits one workgroup: u only
+    (11008, 4096, 128, 3, 2048, 16, 1), # prefill: u only
+])
+def test_linear_lowrank_workspace(N, K, G, S, t, rank, chunks):
+    """u (t x rank float32, rounded up to 256 bytes), then the decode's split-K partials
+    under the side path's plan (one k tile per wave)."""
+    st, d = desc(N, K, G, S)
+    n = ctypes.c_size_t(123)
+    assert L.mbq_linear_lowrank_workspace(ctypes.byref(d), t, BF16, rank, ctypes.byref(n)) == OK
+    ub = (t * rank * 4 + 255) // 256 * 256
+    assert n.value == ub + (chunks * t * N * 4 if chunks > 1 else 0)
+    assert L.mbq_linear_lowrank_workspace(ctypes.byref(d), 0, BF16, rank, ctypes.byref(n)) == OK
+    assert n.value == 0
+    f = P(FAKE)
+    need = ub + (chunks * t * N * 4 if chunks > 1 else 0)
+    for ws, wsb in ((None, 0), (f, need - 1), (P(FAKE + 8), need)):
+        assert L.mbq_linear_lowrank(ctypes.byref(d), f, t, f, BF16, f, f, f, f, rank, f, BF16, ws, wsb,
+                                    None) == WS
+
+
+def test_linear_lowrank_validation():
+    st, d = desc(200, 640, 128, 3)
+    dp, f = ctypes.byref(d), P(FAKE)
+    n = ctypes.c_size_t(0)
+    for r in (0, 4, 12, 40, -8):
+        assert L.mbq_linear_lowrank_workspace(dp, 16, BF16, r, ctypes.byref(n)) == UNSUP
+        assert L.mbq_linear_lowrank(dp, f, 16, f, BF16, f, f, f, f, r, f, BF16, f, 1 << 30, None) == UNSUP
+
+    def call(a=f, b=f, t=16):
+        return L.mbq_linear_lowrank(dp, f, t, f, BF16, f, f, a, b, 16, f, BF16, f, 1 << 30, None)
+
+    assert call(a=None) == ARG and call(b=None) == ARG
+    assert call(a=P(FAKE + 8)) == ARG and call(b=P(FAKE + 2)) == ARG
+    assert call(t=-1) == SHAPE
+    assert call(t=0) == OK          # nothing to compute, nothing launched
+
+
 def test_route_and_regroup_validation():
     f = P(FAKE)
     assert L.mbq_route(4, 16, 0, f, F32, f, f, f, f, f, None) == UNSUP

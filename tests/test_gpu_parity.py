@@ -407,3 +407,43 @@ def test_full_layer14b_workload(mbq):
         err = token_errors(y.float().cpu().numpy()[:, rows], yref)
         assert err.max() <= TOL
         del p
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K,T", [(512, 24), (2304, 40)])
+def test_decode_every_variant(mbq, G, S, dtype, K, T):
+    """Every group / slice count / activation type of the decode, with one or two k tiles
+    per wave (K = 2304 is 9 tiles) and one or two 16-token blocks per workgroup."""
+    say(f"decode variant G={G} S={S} {dtype} K={K} T={T}")
+    d = inputs.make_linear(G + S + K, 96, K, T, group=G, slices=S, dtype=dtype)
+    yg, yref, _ = run_linear(mbq, d)
+    assert token_errors(yg, yref).max() <= TOL
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_generic_decode_every_variant(mbq, monkeypatch, G, S, dtype):
+    """The generic decode kernel over every group / slice count / activation type."""
+    monkeypatch.setenv("MBQ_GENERIC_DECODE", "1")
+    say(f"generic decode variant G={G} S={S} {dtype}")
+    d = inputs.make_linear(G + S + 7, 96, 512, 24, group=G, slices=S, dtype=dtype)
+    yg, yref, _ = run_linear(mbq, d)
+    assert token_errors(yg, yref).max() <= TOL
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("generic", [False, True])
+def test_prefill_every_variant(mbq, monkeypatch, G, S, dtype, generic):
+    """The MFMA prefill (and the generic one) over every group / slice count / activation
+    type, router-mixed budgets over 300 tokens (full and half tiles, ragged rows)."""
+    if generic:
+        monkeypatch.setenv("MBQ_GENERIC_PREFILL", "1")
+    say(f"prefill variant G={G} S={S} {dtype} generic={generic}")
+    d = inputs.make_linear(G + S + 11, 200, 768, 300, group=G, slices=S, dtype=dtype)
+    yg, yref, _ = run_linear(mbq, d)
+    assert token_errors(yg, yref).max() <= TOL

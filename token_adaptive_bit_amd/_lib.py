@@ -19,8 +19,8 @@ STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANG
           -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}
 
 EXPORTS = ("mbq_describe", "mbq_pack", "mbq_pack_rows", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
-           "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_status_str",
-           "mbq_abi_version")
+           "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_linear_lowrank_workspace",
+           "mbq_linear_lowrank", "mbq_status_str", "mbq_abi_version")
 
 
 class MbqDesc(ctypes.Structure):
@@ -66,6 +66,9 @@ def _load() -> ctypes.CDLL:
                                   VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
     lib.mbq_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
     lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, VP]
+    lib.mbq_linear_lowrank_workspace.argtypes = [D, I32, I32, I32, P(ctypes.c_size_t)]
+    lib.mbq_linear_lowrank.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, I32, VP, I32, VP,
+                                       ctypes.c_size_t, VP]
     lib.mbq_status_str.argtypes = [I32]
     lib.mbq_status_str.restype = ctypes.c_char_p
     lib.mbq_abi_version.argtypes = []
@@ -105,4 +108,11 @@ def workspace_bytes(desc: MbqDesc, t: int, x_dtype: int) -> int:
 def route_mlp_workspace_bytes(t: int, k: int, hidden: int) -> int:
     n = ctypes.c_size_t(0)
     check(LIB.mbq_route_mlp_workspace(t, k, hidden, ctypes.byref(n)), "mbq_route_mlp_workspace")
+    return int(n.value)
+
+
+def lowrank_workspace_bytes(desc: MbqDesc, t: int, x_dtype: int, rank: int) -> int:
+    n = ctypes.c_size_t(0)
+    check(LIB.mbq_linear_lowrank_workspace(ctypes.byref(desc), t, x_dtype, rank, ctypes.byref(n)),
+          "mbq_linear_lowrank_workspace")
     return int(n.value)

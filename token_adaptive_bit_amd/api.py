@@ -15,7 +15,8 @@ from ._lib import MBQ_BF16, MBQ_F32, MbqDesc, MbqError, check, describe
 
 __all__ = ["PackedLinear", "pack", "pack_concat", "route", "route_from_logits", "regroup", "linear",
            "linear_workspace", "describe", "MbqError", "MlpRouter", "route_mlp",
-           "route_mlp_from_scores", "route_mlp_workspace"]
+           "route_mlp_from_scores", "route_mlp_workspace", "linear_lowrank",
+           "linear_lowrank_workspace"]
 
 
 def _stream() -> ctypes.c_void_p:
@@ -228,4 +229,34 @@ def linear(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets: torch.
     check(_lib.LIB.mbq_linear(ctypes.byref(p.desc), _p(p.blob), t, _p(x), _dtype(x), _p(perm),
                               _p(offsets), _p(y), _dtype(y), _p(workspace), ws_bytes, _stream()),
           "mbq_linear")
+    return y
+
+
+def linear_lowrank_workspace(p: PackedLinear, t: int, rank: int, x_dtype=torch.bfloat16) -> int:
+    return _lib.lowrank_workspace_bytes(p.desc, t, MBQ_BF16 if x_dtype == torch.bfloat16 else MBQ_F32,
+                                        rank)
+
+
+def linear_lowrank(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor,
+                   a: torch.Tensor, b: torch.Tensor, out_dtype: torch.dtype | None = None,
+                   y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed linear plus the low-rank side path: y = x . W^(b(t))^T + (x . a^T) . b^T,
+    a [rank, k] and b [n, rank] bfloat16."""
+    _dev(x, "x")
+    _dev(a, "a")
+    _dev(b, "b")
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("a and b must be bfloat16")
+    t = x.shape[0]
+    rank = a.shape[0]
+    out_dtype = out_dtype or x.dtype
+    if y is None:
+        y = torch.empty((t, p.n), dtype=out_dtype, device=x.device)
+    need = linear_lowrank_workspace(p, t, rank, x.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    check(_lib.LIB.mbq_linear_lowrank(ctypes.byref(p.desc), _p(p.blob), t, _p(x), _dtype(x), _p(perm),
+                                      _p(offsets), _p(a), _p(b), rank, _p(y), _dtype(y), _p(workspace),
+                                      ws_bytes, _stream()), "mbq_linear_lowrank")
     return y

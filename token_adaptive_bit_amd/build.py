@@ -22,13 +22,19 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmbq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
+# gfx950: the compiler leaves too few wait states around 16x16x32 bf16 MFMAs for the
+# decode kernels' dependent chains (wrong products in some variants, exact once the
+# distances grew); these files are built with MFMA-to-MFMA padding.
+MFMA_PAD = ["-mllvm", "-amdgpu-mfma-padding-ratio=100"]
+
 SOURCES = {
     "api.hip": [],
     "pack.hip": ["-ffp-contract=off"],
     "route.hip": [],
     "route_mlp.hip": [],
-    "decode.hip": [],
-    "decode_stream.hip": [],
+    "lowrank.hip": [],
+    "decode.hip": MFMA_PAD,
+    "decode_stream.hip": MFMA_PAD,
     "prefill.hip": [],
     "prefill_mfma.hip": [],
 }
@@ -37,7 +43,7 @@ SOURCES = {
 # exact waits on the in-order memory counter, which spill traffic (scratch loads and
 # stores) would stall, and the variants a launcher can pick are chosen to fit.  The build
 # reads the compiler's resource-usage remarks and fails on any spill to scratch memory.
-SPILL_FREE = ("decode_stream.hip", "prefill_mfma.hip", "route_mlp.hip")
+SPILL_FREE = ("decode_stream.hip", "prefill_mfma.hip", "route_mlp.hip", "lowrank.hip")
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

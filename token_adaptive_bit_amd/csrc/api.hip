@@ -184,19 +184,75 @@ mbq_status mbq_route_mlp(int32_t t, int32_t k, int32_t s, int32_t hidden, const 
                                         budget, perm, offsets, workspace, stream));
 }
 
+namespace {
+
+// Workspace of the routed linear alone (split-K partials); lr: the side-path plan.
+size_t linear_ws(const mbq_desc& d, int32_t t, bool xb, bool lr) {
+  size_t n = 0;
+  if (t >= 1 && t <= 64) {  // enough for either decode kernel
+    n = mbq::decode_workspace(d, t, xb);
+    if (mbq::decode_stream_supported(d, t, xb, lr)) n = std::max(n, mbq::decode_stream_workspace(d, t, xb, lr));
+  }
+  return n;
+}
+
+size_t u_bytes(int32_t t, int32_t rank) { return align256(uint64_t(t) * uint64_t(rank) * 4); }
+
+bool rank_ok(int32_t rank) { return rank >= 8 && rank <= 32 && rank % 8 == 0; }
+
+mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                       mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
+                       const uint16_t* a, const uint16_t* b, int32_t rank, void* y,
+                       mbq_dtype y_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
+  if (rank && !rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
+  if (t == 0) return MBQ_OK;  // nothing to compute; t-sized pointers may be NULL
+  if (!packed || !x || !perm || !offsets || !y) return MBQ_ERR_ARG;
+  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(perm, 4) ||
+      !aligned(offsets, 4))
+    return MBQ_ERR_ARG;
+  if (rank && (!a || !b || !aligned(a, 16) || !aligned(b, 16))) return MBQ_ERR_ARG;
+  const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16, lr = rank > 0;
+  const size_t ub = lr ? u_bytes(t, rank) : 0, need = ub + linear_ws(*desc, t, xb, lr);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
+    return MBQ_ERR_WORKSPACE;
+  float* u = lr ? static_cast<float*>(workspace) : nullptr;
+  void* lws = need > ub ? static_cast<uint8_t*>(workspace) + ub : nullptr;
+  if (lr) {
+    st = launched(mbq::launch_lowrank_u(t, desc->k, x, xb, a, rank, u, stream));
+    if (st != MBQ_OK) return st;
+  }
+  // MBQ_GENERIC_DECODE forces the generic decode kernel (kept for slices of 4 GiB and more,
+  // which the streaming kernel's 32-bit buffer offsets cannot reach)
+  if (mbq::decode_stream_supported(*desc, t, xb, lr) && !std::getenv("MBQ_GENERIC_DECODE"))
+    return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb, lws, u,
+                                              b, rank, stream));
+  // MBQ_GENERIC_PREFILL forces the plain LDS kernel (kept for activations of 4 GiB and more
+  // or slices of 4 GiB and more, which the MFMA kernel's 32-bit buffer offsets cannot reach)
+  if (t > 64 && mbq::prefill_mfma_supported(*desc, t, x, xb) && !std::getenv("MBQ_GENERIC_PREFILL"))
+    return launched(mbq::launch_prefill_mfma(*desc, packed, t, x, xb, perm, offsets, y, yb, u, b, rank,
+                                             stream));
+  // the generic kernels: the side path is added to y afterwards
+  if (t <= 64)
+    st = launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb, lws, stream));
+  else
+    st = launched(mbq::launch_prefill(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
+  if (st != MBQ_OK || !lr) return st;
+  return launched(mbq::launch_lowrank_update(t, desc->n, u, b, rank, y, yb, stream));
+}
+
+}  // namespace
+
 mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                 size_t* bytes) {
   mbq_status st = check_desc(desc);
   if (st != MBQ_OK) return st;
   if (!bytes || !valid_dtype(x_dtype)) return MBQ_ERR_ARG;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
-  const bool xb = x_dtype == MBQ_BF16;
-  *bytes = 0;
-  if (t >= 1 && t <= 64) {  // enough for either decode kernel
-    *bytes = mbq::decode_workspace(*desc, t, xb);
-    if (mbq::decode_stream_supported(*desc, t, xb))
-      *bytes = std::max(*bytes, mbq::decode_stream_workspace(*desc, t, xb));
-  }
+  *bytes = linear_ws(*desc, t, x_dtype == MBQ_BF16, false);
   return MBQ_OK;
 }
 
@@ -204,34 +260,29 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
                       mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                       void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
                       hipStream_t stream) {
+  return linear_impl(desc, packed, t, x, x_dtype, perm, offsets, nullptr, nullptr, 0, y, y_dtype,
+                     workspace, ws_bytes, stream);
+}
+
+mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
+                                        int32_t rank, size_t* bytes) {
   mbq_status st = check_desc(desc);
   if (st != MBQ_OK) return st;
+  if (!bytes || !valid_dtype(x_dtype)) return MBQ_ERR_ARG;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
-  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
-  if (t == 0) return MBQ_OK;  // nothing to compute; t-sized pointers may be NULL
-  if (!packed || !x || !perm || !offsets || !y) return MBQ_ERR_ARG;
-  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(perm, 4) ||
-      !aligned(offsets, 4))
-    return MBQ_ERR_ARG;
-  size_t need = 0;
-  st = mbq_linear_workspace(desc, t, x_dtype, &need);
-  if (st != MBQ_OK) return st;
-  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
-    return MBQ_ERR_WORKSPACE;
-  const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16;
-  // MBQ_GENERIC_DECODE forces the generic decode kernel (kept for slices of 4 GiB and more,
-  // which the streaming kernel's 32-bit buffer offsets cannot reach)
-  if (mbq::decode_stream_supported(*desc, t, xb) && !std::getenv("MBQ_GENERIC_DECODE"))
-    return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb,
-                                              workspace, stream));
-  if (t <= 64)
-    return launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb,
-                                       workspace, stream));
-  // MBQ_GENERIC_PREFILL forces the plain LDS kernel (kept for activations of 4 GiB and more
-  // or slices of 4 GiB and more, which the MFMA kernel's 32-bit buffer offsets cannot reach)
-  if (mbq::prefill_mfma_supported(*desc, t, x, xb) && !std::getenv("MBQ_GENERIC_PREFILL"))
-    return launched(mbq::launch_prefill_mfma(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
-  return launched(mbq::launch_prefill(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
+  if (!rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
+  *bytes = t == 0 ? 0 : u_bytes(t, rank) + linear_ws(*desc, t, x_dtype == MBQ_BF16, true);
+  return MBQ_OK;
+}
+
+mbq_status mbq_linear_lowrank(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                              mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
+                              const uint16_t* a, const uint16_t* b, int32_t rank, void* y,
+                              mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
+  return linear_impl(desc, packed, t, x, x_dtype, perm, offsets, a, b, rank, y, y_dtype, workspace,
+                     ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -63,15 +63,37 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// On gfx950 the compiler's wait states between a 16x16x32 bf16 MFMA and the VALU or LDS
+// instructions that read its result fall short: with the results read 9 wait states
+// after the last MFMA, decode variants (group 128 with 1 or 4 slices, group 64 with 4)
+// produced garbage or stale products, and doubling every distance made all of them exact.
+// Each MFMA chain is therefore followed by this fence before its result is read, and the
+// file is built with MFMA-to-MFMA padding (-amdgpu-mfma-padding-ratio=100).
+__device__ __forceinline__ void mfma_result_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7");
+  asm volatile("s_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ u32x4_t ldg16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-template <int G, int S, int TPW>
+// The low-rank side path's B rows of one row block travel with its codes (LR only).
+template <bool LR>
+struct LrRows {
+  u32x4_t v;
+};
+template <>
+struct LrRows<false> {};
+
+template <int G, int S, int TPW, bool LR = false>
 struct Codes {
   static constexpr int GPT = 256 / G;
   u32x4_t cw[TPW][S];
   uint32_t pv[TPW][S][GPT];
+  LrRows<LR> lr;
 };
 
 // Raw buffer loads: one scalar resource per slice, a scalar tile offset and one per-lane
@@ -81,8 +103,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint8_t* base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, int(bytes), 0x00020000);
 }
 
-template <int G, int S, int TPW>
-__device__ __forceinline__ void load_codes(Codes<G, S, TPW>& C, const __amdgpu_buffer_rsrc_t (&rs)[S],
+template <int G, int S, int TPW, bool LR>
+__device__ __forceinline__ void load_codes(Codes<G, S, TPW, LR>& C, const __amdgpu_buffer_rsrc_t (&rs)[S],
                                            int nb, const int (&kt)[TPW], int KB, int NG,
                                            uint32_t po, uint32_t lane_code, uint32_t lane_par) {
   constexpr int GPT = 256 / G;
@@ -103,12 +125,20 @@ __device__ __forceinline__ void load_codes(Codes<G, S, TPW>& C, const __amdgpu_b
 // At most 8 waves (two per SIMD), so a wave has 256 registers: room for its stationary
 // A operand and seeds plus three buffers of codes and params without any spill (a spill
 // would wait on the in-order load counter behind the prefetched loads).
-template <int G, int S, int NA, int TPW, int TB>
+//
+// LR adds the low-rank side path u_t . B^T (u = x A^T from lowrank.hip, [T x R] float32;
+// B [N x R] bf16, R a multiple of 8 up to 32): wave 0 of the first k chunk multiplies the
+// token block's u (a bf16 hi + lo pair, held for the whole launch) by the row block's B
+// rows (loaded with its codes) in two more MFMAs and adds the product to its part of the
+// output before the waves' parts are summed.
+template <int G, int S, int NA, int TPW, int TB, bool LR>
 __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, uint64_t ss,
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, void* __restrict__ y, int y_bf16, int kchunk,
-    float* __restrict__ part) {
+    float* __restrict__ part, const float* __restrict__ lr_u, const uint16_t* __restrict__ lr_b,
+    int lr_r) {
+  static_assert(!LR || (TB == 1 && TPW == 1), "the side path is built for one tile and one token block");
   constexpr int GPT = 256 / G, WPG = G / 64;
   __shared__ f32x4_t red[2][kMaxWaves][TB][64];
   const int NW = blockDim.x >> 6;
@@ -167,6 +197,27 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           }
       }
   }
+
+  // The side path's u rows of this token block: lane (r, c) holds ranks 8c .. 8c + 7 of
+  // token row r (clamped like the activations; ranks past R read zeros).
+  __amdgpu_buffer_rsrc_t rlr_b = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_b), 0u);
+  uint32_t lr_lane = 0;
+  u32x4_t Uraw[2], Uop[2];
+  if constexpr (LR) {
+    const int xr = tb0 + min(r, Tw - 1);
+    const __amdgpu_buffer_rsrc_t ru = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_u), uint32_t(T) * lr_r * 4);
+    const uint32_t uo = 8 * c < lr_r ? (uint32_t(xr) * lr_r + 8 * c) * 4 : 0x80000000u;
+    Uraw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, uo, 0, 0));
+    Uraw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, uo == 0x80000000u ? uo : uo + 16, 0, 0));
+    // B rows: only wave 0 of k chunk 0 reads them (the others load zeros, no traffic)
+    rlr_b = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_b), (wave == 0 && blockIdx.z == 0) ? uint32_t(N) * lr_r * 2 : 0u);
+    lr_lane = 8 * c < lr_r ? (uint32_t(r) * lr_r + 8 * c) * 2 : 0x80000000u;
+  }
+  auto load_lr = [&](Codes<G, S, TPW, LR>& C, int nb) __attribute__((always_inline)) {
+    if constexpr (LR)
+      C.lr.v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                   rlr_b, lr_lane == 0x80000000u ? lr_lane : lr_lane + uint32_t(nb) * 16u * lr_r * 2, 0, 0));
+  };
 
   // Budgets of this block's tokens, published in LDS right before the first row block is
   // multiplied (by then every wave has its first three row blocks in flight): wave 0 clears
@@ -261,6 +312,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
               xs4 = mfma(aop(b, tp, i, 0, pa), ones, xs4);
               xs4 = mfma(aop(b, tp, i, 1, pa), ones, xs4);
             }
+          mfma_result_fence();
           gnb[b][tp][gi] = nb4;
           // lanes (0, c) hold X of tokens 4c + v (every row n sees the same sums)
           if (r == 0) {
@@ -268,6 +320,19 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
             for (int v = 0; v < 4; ++v) xsT[wave][b][tp * GPT + gi][4 * c + v] = xs4[v];
           }
         }
+    }
+    if constexpr (LR) {
+      // u as a bf16 hi + lo pair (8 ranks per lane)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float v0 = __uint_as_float(d < 2 ? Uraw[0][2 * d] : Uraw[1][2 * d - 4]);
+        const float v1 = __uint_as_float(d < 2 ? Uraw[0][2 * d + 1] : Uraw[1][2 * d - 3]);
+        const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
+        const uint32_t l0 = bf16_bits_rne(v0 - bf16_bits_to_float(h0));
+        const uint32_t l1 = bf16_bits_rne(v1 - bf16_bits_to_float(h1));
+        Uop[0][d] = h0 | (h1 << 16);
+        Uop[1][d] = l0 | (l1 << 16);
+      }
     }
   };
 
@@ -282,18 +347,19 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // them (group 64 with 4 slices: 32 registers of codes and params per buffer and tile):
   // then two (one row block in flight).
   constexpr bool kThreeBuffers = !(G == 64 && S == 4);
-  Codes<G, S, TPW> c0, c1, c2;
+  Codes<G, S, TPW, LR> c0, c1, c2;
   // Multiplies one row block.  JM, the slices processed, is a compile-time count, so the
   // MFMA chains and epilogues of a group form one straight-line block that the compiler
   // interleaves (a runtime test per slice or tile would split it into small blocks and
   // expose every MFMA's latency).  JM is S, or 1 when no token of the batch uses more;
   // slices in [jmax, JM) read zeros (empty buffer range) and so add exactly zero, and a
   // wave without one of its tiles zeroes that tile's scales and zeros.
-  auto process = [&](auto jm, const Codes<G, S, TPW>& C, int nb, int buf, Codes<G, S, TPW>& Cn,
+  auto process = [&](auto jm, const Codes<G, S, TPW, LR>& C, int nb, int buf, Codes<G, S, TPW, LR>& Cn,
                      int nbn) __attribute__((always_inline)) {
     constexpr int JM = decltype(jm)::value;
     // the next buffer's loads (row block nbn) go out first: two row blocks stay in flight
     load_codes(Cn, rs, nbn, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    load_lr(Cn, nbn);
     f32x4_t acc[TB][JM];
 #pragma unroll
     for (int b = 0; b < TB; ++b)
@@ -326,6 +392,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           }
         }
       }
+      mfma_result_fence();
       // the wave wrote this table itself, so its own in-order LDS accesses suffice
       f32x4_t X4[TB];
 #pragma unroll
@@ -352,6 +419,15 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
         out[1] += j < bud.y ? acc[b][j][1] : 0.f;
         out[2] += j < bud.z ? acc[b][j][2] : 0.f;
         out[3] += j < bud.w ? acc[b][j][3] : 0.f;
+      }
+      if constexpr (LR) {
+        f32x4_t L = mfma(Uop[0], C.lr.v, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        L = mfma(Uop[1], C.lr.v, L);
+        mfma_result_fence();
+        out[0] += bud.x > 0 ? L[0] : 0.f;
+        out[1] += bud.y > 0 ? L[1] : 0.f;
+        out[2] += bud.z > 0 ? L[2] : 0.f;
+        out[3] += bud.w > 0 ? L[3] : 0.f;
       }
       red[buf][wave][b][lane] = out;
     }
@@ -393,11 +469,13 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // wait below covers exactly the loads it needs)
   __builtin_amdgcn_sched_barrier(0);
   load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+  load_lr(c0, rb0);
   __builtin_amdgcn_sched_barrier(0);
   setup_a();
   if constexpr (kThreeBuffers) {
     __builtin_amdgcn_sched_barrier(0);
     load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    load_lr(c1, nbl(1));
   }
   __builtin_amdgcn_sched_barrier(0);
   route_budgets();
@@ -475,10 +553,11 @@ struct Plan {
   int tb, tpw, kchunk, ks, nw;
 };
 
-Plan make_plan(const mbq_desc& d, int32_t t, bool x_bf16) {
+// With the side path (lr) every variant takes one tile and one token block per wave.
+Plan make_plan(const mbq_desc& d, int32_t t, bool x_bf16, bool lr) {
   const int na = x_bf16 ? 1 : 2;
-  const int tb = (t > 32 && two_blocks_fit(d.group, d.slices, na)) ? 2 : 1;
-  const int tmax = (tb == 1 && two_tiles_fit(d.group, d.slices, na)) ? 2 : 1;
+  const int tb = (!lr && t > 32 && two_blocks_fit(d.group, d.slices, na)) ? 2 : 1;
+  const int tmax = (!lr && tb == 1 && two_tiles_fit(d.group, d.slices, na)) ? 2 : 1;
   const int kb = d.k_tiles;
   int ks = (kb + kMaxWaves * tmax - 1) / (kMaxWaves * tmax);
   const int kchunk = (kb + ks - 1) / ks;
@@ -488,10 +567,24 @@ Plan make_plan(const mbq_desc& d, int32_t t, bool x_bf16) {
   return Plan{tb, tpw, kchunk, ks, nw};
 }
 
-template <int G, int S, int NA, int TPW, int TB>
+// Group 64 with 4 slices and float32 activations does not fit a wave's registers even
+// with two buffers; the generic decode kernel serves it.
+constexpr bool stream_fits(int G, int S, int NA) { return !(G == 64 && S == 4 && NA == 2); }
+
+// Variants that carry the side path: every streaming variant (one tile and one token
+// block per wave leave room for its registers).
+constexpr bool lr_fits(int G, int S, int NA) { return stream_fits(G, S, NA); }
+
+struct LrArgs {
+  const float* u;
+  const uint16_t* b;
+  int r;
+};
+
+template <int G, int S, int NA, int TPW, int TB, bool LR>
 hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                       const void* x, const int32_t* perm, const int32_t* offsets, void* y,
-                      bool y_bf16, float* part, hipStream_t stream) {
+                      bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream) {
   // One workgroup per CU.  The token-block groups and k chunks of a launch share the CUs,
   // so they all run at once: with gridDim.x a multiple of 8, workgroups (x, y, z) of every
   // y and z sit on XCD x % 8, and the token groups of one k chunk walk the same row blocks
@@ -499,43 +592,44 @@ hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int
   // token groups by that XCD's L2.
   const int ty = (t + 16 * TB - 1) / (16 * TB);
   const int grid = std::min(d.row_blocks, std::max(8, (cu_count() / (ty * pl.ks)) & ~7));
-  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
+  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
                      0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
                      d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
-                     offsets, y, int(y_bf16), pl.kchunk, part);
+                     offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.b, lr.r);
   return hipGetLastError();
 }
 
 template <int G, int S, int NA>
 hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                      const void* x, const int32_t* perm, const int32_t* offsets, void* y,
-                     bool y_bf16, float* part, hipStream_t stream) {
+                     bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream) {
+  if constexpr (lr_fits(G, S, NA)) {
+    if (lr.r > 0)
+      return launch_gsn<G, S, NA, 1, 1, true>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
+  }
   if constexpr (two_blocks_fit(G, S, NA)) {
     if (pl.tb == 2)
-      return launch_gsn<G, S, NA, 1, 2>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+      return launch_gsn<G, S, NA, 1, 2, false>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
   }
   if constexpr (two_tiles_fit(G, S, NA)) {
     if (pl.tpw == 2)
-      return launch_gsn<G, S, NA, 2, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+      return launch_gsn<G, S, NA, 2, 1, false>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
   }
-  return launch_gsn<G, S, NA, 1, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+  return launch_gsn<G, S, NA, 1, 1, false>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
 }
 
-// Group 64 with 4 slices and float32 activations does not fit a wave's registers even
-// with two buffers; the generic decode kernel serves it.
-constexpr bool stream_fits(int G, int S, int NA) { return !(G == 64 && S == 4 && NA == 2); }
 
 template <int G, int NA>
 hipError_t launch_gn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                      const void* x, const int32_t* perm, const int32_t* offsets, void* y,
-                     bool y_bf16, float* part, hipStream_t stream) {
+                     bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream) {
   switch (d.slices) {
-    case 1: return launch_gs<G, 1, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
-    case 2: return launch_gs<G, 2, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
-    case 3: return launch_gs<G, 3, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+    case 1: return launch_gs<G, 1, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
+    case 2: return launch_gs<G, 2, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
+    case 3: return launch_gs<G, 3, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
     default:
       if constexpr (stream_fits(G, 4, NA))
-        return launch_gs<G, 4, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+        return launch_gs<G, 4, NA>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
       return hipErrorInvalidValue;  // excluded by decode_stream_supported
   }
 }
@@ -543,34 +637,37 @@ hipError_t launch_gn(const mbq_desc& d, const Plan& pl, const void* packed, int3
 template <int G>
 hipError_t launch_g(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                     const void* x, bool x_bf16, const int32_t* perm, const int32_t* offsets,
-                    void* y, bool y_bf16, float* part, hipStream_t stream) {
-  if (x_bf16) return launch_gn<G, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
-  return launch_gn<G, 2>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, stream);
+                    void* y, bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream) {
+  if (x_bf16) return launch_gn<G, 1>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
+  return launch_gn<G, 2>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
 }
 
 }  // namespace
 
-bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16) {
+bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16, bool lr) {
   // buffer offsets are 32-bit: a slice must stay below 4 GiB
+  const int na = x_bf16 ? 1 : 2;
   return t >= 1 && t <= kMaxTokens && d.slice_stride < (uint64_t(1) << 32) &&
-         stream_fits(d.group, d.slices, x_bf16 ? 1 : 2);
+         (lr ? lr_fits(d.group, d.slices, na) : stream_fits(d.group, d.slices, na));
 }
 
-size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16) {
-  const Plan pl = make_plan(d, t, x_bf16);
+size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool lr) {
+  const Plan pl = make_plan(d, t, x_bf16, lr);
   return pl.ks > 1 ? size_t(pl.ks) * size_t(t) * size_t(d.n) * sizeof(float) : 0;
 }
 
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
-                                void* y, bool y_bf16, void* workspace, hipStream_t stream) {
-  const Plan pl = make_plan(d, t, x_bf16);
+                                void* y, bool y_bf16, void* workspace, const float* lr_u,
+                                const uint16_t* lr_b, int32_t lr_r, hipStream_t stream) {
+  const LrArgs lr{lr_u, lr_b, lr_r};
+  const Plan pl = make_plan(d, t, x_bf16, lr_r > 0);
   float* part = pl.ks > 1 ? static_cast<float*>(workspace) : nullptr;
   hipError_t e;
   switch (d.group) {
-    case 64: e = launch_g<64>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, stream); break;
-    case 128: e = launch_g<128>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, stream); break;
-    default: e = launch_g<256>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, stream); break;
+    case 64: e = launch_g<64>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, lr, stream); break;
+    case 128: e = launch_g<128>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, lr, stream); break;
+    default: e = launch_g<256>(d, pl, packed, t, x, x_bf16, perm, offsets, y, y_bf16, part, lr, stream); break;
   }
   if (e != hipSuccess || !part) return e;
   const size_t tn = size_t(t) * size_t(d.n);

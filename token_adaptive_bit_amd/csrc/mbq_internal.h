@@ -50,17 +50,23 @@ size_t decode_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
 hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                          bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                          bool y_bf16, void* ws, hipStream_t stream);
-bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16);
-size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16);
+bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16, bool lr = false);
+size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool lr);
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
-                                void* y, bool y_bf16, void* ws, hipStream_t stream);
+                                void* y, bool y_bf16, void* ws, const float* lr_u,
+                                const uint16_t* lr_b, int32_t lr_r, hipStream_t stream);
 hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                           bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                           bool y_bf16, hipStream_t stream);
 bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_bf16);
 hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
-                               bool y_bf16, hipStream_t stream);
+                               bool y_bf16, const float* lr_u, const uint16_t* lr_b, int32_t lr_r,
+                               hipStream_t stream);
+hipError_t launch_lowrank_u(int32_t t, int32_t k, const void* x, bool x_bf16, const uint16_t* a,
+                            int32_t rank, float* u, hipStream_t stream);
+hipError_t launch_lowrank_update(int32_t t, int32_t n, const float* u, const uint16_t* b, int32_t rank,
+                                 void* y, bool y_bf16, hipStream_t stream);
 
 }  // namespace mbq

@@ -160,6 +160,10 @@ struct TileArgs {
   const int32_t* perm;
   void* y;
   int y_bf16;
+  // low-rank side path (lr_r == 0: none): u [T x lr_r] float32, B [N x lr_r] bf16
+  const float* lr_u;
+  const uint16_t* lr_b;
+  int lr_r;
 };
 
 // Epilogue: a wave's outputs are staged in LDS as rows of 64 values (+16 bytes of
@@ -423,6 +427,47 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& a, int start, int r
   }
   if (q < NQ) body(q, cw1, pw1, cw0, pw0);
 
+  // ---- low-rank side path: acc += u . B^T, 16 ranks per MFMA step, u as a bf16 hi + lo
+  // pair.  MFMA k group c2 is ranks k0 + 8 c2 .. + 7 on both operands: the A rows are the
+  // tile's tokens (row -> token table; padding rows read zeros), the B columns its outputs.
+  if (a.lr_r > 0) {
+    const int R = a.lr_r;
+    const __amdgpu_buffer_rsrc_t ru = rsrc(a.lr_u, uint32_t(a.T) * uint32_t(R) * 4u);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(a.lr_b, uint32_t(a.N) * uint32_t(R) * 2u);
+    for (int k0 = 0; k0 < R; k0 += 16) {
+      const int kk = k0 + 8 * c2;
+      u32x4_t bl[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int n = n0 + 64 * wn + 32 * k + col;
+        const uint32_t off = (kk < R && n < a.N) ? (uint32_t(n) * R + kk) * 2u : 0x80000000u;
+        bl[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int tok = tokT[WM * wm + 32 * i + col];
+        const uint32_t off = (tok >= 0 && kk < R) ? (uint32_t(tok) * R + kk) * 4u : 0x80000000u;
+        const u32x4_t u0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, 0));
+        const u32x4_t u1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                               ru, off == 0x80000000u ? off : off + 16u, 0, 0));
+        u32x4_t uh, ul;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float v0 = __uint_as_float(d < 2 ? u0[2 * d] : u1[2 * d - 4]);
+          const float v1 = __uint_as_float(d < 2 ? u0[2 * d + 1] : u1[2 * d - 3]);
+          const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
+          uh[d] = h0 | (h1 << 16);
+          ul[d] = bf16_bits_rne(v0 - bf16_bits_to_float(h0)) | (bf16_bits_rne(v1 - bf16_bits_to_float(h1)) << 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          acc[i][k] = mfma32(uh, bl[k], acc[i][k]);
+          acc[i][k] = mfma32(ul, bl[k], acc[i][k]);
+        }
+      }
+    }
+  }
+
   if (a.y_bf16)
     store_tile<MB, WM, true>(acc, a, tokT, lds, wave, wn, wm, lane, n0);
   else
@@ -510,7 +555,8 @@ bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_
 
 hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
-                               bool y_bf16, hipStream_t stream) {
+                               bool y_bf16, const float* lr_u, const uint16_t* lr_b, int32_t lr_r,
+                               hipStream_t stream) {
   const int BM = x_bf16 ? 256 : 128;
   TileArgs a{};
   a.packed = static_cast<const uint8_t*>(packed);
@@ -529,6 +575,9 @@ hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t,
   a.perm = perm;
   a.y = y;
   a.y_bf16 = int(y_bf16);
+  a.lr_u = lr_u;
+  a.lr_b = lr_b;
+  a.lr_r = lr_r;
   const int NT = (d.n + kBN - 1) / kBN;
   // at most ceil(R / BM) tiles per budget group (a half tile replaces a full one)
   const int max_tiles = NT * ((t + BM - 1) / BM + d.slices - 1);
