@@ -223,9 +223,10 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
                       void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
                       hipStream_t stream);
 
-/* Host only: bytes of device workspace mbq_linear_lowrank needs: u (t x rank float32,
- * rounded up to 256 bytes) followed by the routed linear's split-K partials under the
- * side path's plan (one k tile and one 16-token block per wave).  0 when t == 0. */
+/* Host only: bytes of device workspace mbq_linear_lowrank needs: u as c float32 partials
+ * over chunks of K ([c x t x rank], c <= 8 chosen from t and k; rounded up to 256 bytes)
+ * followed by the routed linear's split-K partials under the side path's plan (one
+ * 16-token block per workgroup).  0 when t == 0. */
 mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                         int32_t rank, size_t* bytes);
 

@@ -104,20 +104,21 @@ def test_pack_rows_validation():
     assert L.mbq_pack_rows(None, 0, 16, f, F32, f, None, None) == ARG
 
 
-@pytest.mark.parametrize("N,K,G,S,t,rank,chunks", [
-    (18944, 3584, 128, 3, 16, 16, 2),   # 14 k tiles: one tile per wave with the side path
-    (5120, 5120, 128, 3, 64, 16, 3),    # one 16-token block per workgroup
-    (150, 2304, 64, 2, 48, 32, 2),
-    (512, 256, 64, 3, 16, 8, 1),        # K fits one workgroup: u only
-    (11008, 4096, 128, 3, 2048, 16, 1), # prefill: u only
+@pytest.mark.parametrize("N,K,G,S,t,rank,uchunks,chunks", [
+    (18944, 3584, 128, 3, 16, 16, 7, 1),    # 14 k tiles: two per wave, no split
+    (5120, 5120, 128, 3, 64, 16, 8, 2),     # one 16-token block per workgroup, K in 2 chunks
+    (150, 2304, 64, 2, 48, 32, 4, 2),       # one tile per wave (group 64): K in 2 chunks
+    (512, 256, 64, 3, 16, 8, 1, 1),         # K fits one workgroup: u only
+    (11008, 4096, 128, 3, 2048, 16, 1, 1),  # prefill: u only
 ])
-def test_linear_lowrank_workspace(N, K, G, S, t, rank, chunks):
-    """u (t x rank float32, rounded up to 256 bytes), then the decode's split-K partials
-    under the side path's plan (one k tile per wave)."""
+def test_linear_lowrank_workspace(N, K, G, S, t, rank, uchunks, chunks):
+    """u as uchunks float32 partials [uchunks x t x rank] (rounded up to 256 bytes), then
+    the decode's split-K partials under the side path's plan (one 16-token block per
+    workgroup)."""
     st, d = desc(N, K, G, S)
     n = ctypes.c_size_t(123)
     assert L.mbq_linear_lowrank_workspace(ctypes.byref(d), t, BF16, rank, ctypes.byref(n)) == OK
-    ub = (t * rank * 4 + 255) // 256 * 256
+    ub = (uchunks * t * rank * 4 + 255) // 256 * 256
     assert n.value == ub + (chunks * t * N * 4 if chunks > 1 else 0)
     assert L.mbq_linear_lowrank_workspace(ctypes.byref(d), 0, BF16, rank, ctypes.byref(n)) == OK
     assert n.value == 0

@@ -196,7 +196,9 @@ size_t linear_ws(const mbq_desc& d, int32_t t, bool xb, bool lr) {
   return n;
 }
 
-size_t u_bytes(int32_t t, int32_t rank) { return align256(uint64_t(t) * uint64_t(rank) * 4); }
+size_t u_bytes(int32_t t, int32_t k, int32_t rank) {
+  return align256(uint64_t(mbq::lowrank_u_chunks(t, k)) * uint64_t(t) * uint64_t(rank) * 4);
+}
 
 bool rank_ok(int32_t rank) { return rank >= 8 && rank <= 32 && rank % 8 == 0; }
 
@@ -216,7 +218,8 @@ mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, cons
     return MBQ_ERR_ARG;
   if (rank && (!a || !b || !aligned(a, 16) || !aligned(b, 16))) return MBQ_ERR_ARG;
   const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16, lr = rank > 0;
-  const size_t ub = lr ? u_bytes(t, rank) : 0, need = ub + linear_ws(*desc, t, xb, lr);
+  const size_t ub = lr ? u_bytes(t, desc->k, rank) : 0, need = ub + linear_ws(*desc, t, xb, lr);
+  const int ksu = lr ? mbq::lowrank_u_chunks(t, desc->k) : 0;
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
     return MBQ_ERR_WORKSPACE;
   float* u = lr ? static_cast<float*>(workspace) : nullptr;
@@ -229,19 +232,19 @@ mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, cons
   // which the streaming kernel's 32-bit buffer offsets cannot reach)
   if (mbq::decode_stream_supported(*desc, t, xb, lr) && !std::getenv("MBQ_GENERIC_DECODE"))
     return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb, lws, u,
-                                              b, rank, stream));
+                                              ksu, b, rank, stream));
   // MBQ_GENERIC_PREFILL forces the plain LDS kernel (kept for activations of 4 GiB and more
   // or slices of 4 GiB and more, which the MFMA kernel's 32-bit buffer offsets cannot reach)
   if (t > 64 && mbq::prefill_mfma_supported(*desc, t, x, xb) && !std::getenv("MBQ_GENERIC_PREFILL"))
-    return launched(mbq::launch_prefill_mfma(*desc, packed, t, x, xb, perm, offsets, y, yb, u, b, rank,
-                                             stream));
+    return launched(mbq::launch_prefill_mfma(*desc, packed, t, x, xb, perm, offsets, y, yb, u, ksu, b,
+                                             rank, stream));
   // the generic kernels: the side path is added to y afterwards
   if (t <= 64)
     st = launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb, lws, stream));
   else
     st = launched(mbq::launch_prefill(*desc, packed, t, x, xb, perm, offsets, y, yb, stream));
   if (st != MBQ_OK || !lr) return st;
-  return launched(mbq::launch_lowrank_update(t, desc->n, u, b, rank, y, yb, stream));
+  return launched(mbq::launch_lowrank_update(t, desc->n, u, ksu, b, rank, y, yb, stream));
 }
 
 }  // namespace
@@ -271,7 +274,7 @@ mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dty
   if (!bytes || !valid_dtype(x_dtype)) return MBQ_ERR_ARG;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
   if (!rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
-  *bytes = t == 0 ? 0 : u_bytes(t, rank) + linear_ws(*desc, t, x_dtype == MBQ_BF16, true);
+  *bytes = t == 0 ? 0 : u_bytes(t, desc->k, rank) + linear_ws(*desc, t, x_dtype == MBQ_BF16, true);
   return MBQ_OK;
 }
 

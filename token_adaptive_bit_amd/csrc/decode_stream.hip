@@ -67,11 +67,12 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
 // instructions that read its result fall short: with the results read 9 wait states
 // after the last MFMA, decode variants (group 128 with 1 or 4 slices, group 64 with 4)
 // produced garbage or stale products, and doubling every distance made all of them exact.
-// Each MFMA chain is therefore followed by this fence before its result is read, and the
-// file is built with MFMA-to-MFMA padding (-amdgpu-mfma-padding-ratio=100).
+// Each MFMA chain is therefore followed by this fence (8 more wait states; 4, 8 and 32
+// all made every variant exact) before its result is read, and the file is built with
+// MFMA-to-MFMA padding (-amdgpu-mfma-padding-ratio=100), without which group 128 with 4
+// slices stayed wrong.
 __device__ __forceinline__ void mfma_result_fence() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7");
   asm volatile("s_nop 7");
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -136,9 +137,9 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, uint64_t ss,
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, void* __restrict__ y, int y_bf16, int kchunk,
-    float* __restrict__ part, const float* __restrict__ lr_u, const uint16_t* __restrict__ lr_b,
-    int lr_r) {
-  static_assert(!LR || (TB == 1 && TPW == 1), "the side path is built for one tile and one token block");
+    float* __restrict__ part, const float* __restrict__ lr_u, int lr_ks,
+    const uint16_t* __restrict__ lr_b, int lr_r) {
+  static_assert(!LR || TB == 1, "the side path is built for one token block per workgroup");
   constexpr int GPT = 256 / G, WPG = G / 64;
   __shared__ f32x4_t red[2][kMaxWaves][TB][64];
   const int NW = blockDim.x >> 6;
@@ -172,6 +173,36 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     if (off[j] <= T - 1) jmax = j + 1;
   const int pi = (wave == 0 && lane < T) ? perm[lane] : -1;
 
+  // The side path's u rows of this token block: lane (r, c) holds ranks 8c .. 8c + 7 of
+  // token row r (clamped like the activations; ranks past R read zeros), summed over the
+  // lr_ks chunks of K in order.  Issued before the activations so that the sum waits
+  // for these loads only.
+  __amdgpu_buffer_rsrc_t rlr_b = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_b), 0u);
+  uint32_t lr_lane = 0;
+  u32x4_t Uraw[2], Uop[2];
+  if constexpr (LR) {
+    const int xr = 16 * TB * blockIdx.y + min(r, min(16 * TB, T - 16 * TB * int(blockIdx.y)) - 1);
+    const __amdgpu_buffer_rsrc_t ru =
+        slice_rsrc(reinterpret_cast<const uint8_t*>(lr_u), uint32_t(lr_ks) * uint32_t(T) * lr_r * 4);
+    u32x4_t ul[kMaxLrChunks][2];
+#pragma unroll
+    for (int z = 0; z < kMaxLrChunks; ++z) {
+      const uint32_t uo = (8 * c < lr_r && z < lr_ks) ? ((uint32_t(z) * T + xr) * lr_r + 8 * c) * 4 : 0x80000000u;
+      ul[z][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, uo, 0, 0));
+      ul[z][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, uo == 0x80000000u ? uo : uo + 16, 0, 0));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4_t acc = __builtin_bit_cast(f32x4_t, ul[0][h]);
+#pragma unroll
+      for (int z = 1; z < kMaxLrChunks; ++z) acc += __builtin_bit_cast(f32x4_t, ul[z][h]);  // + 0 past lr_ks
+      Uraw[h] = __builtin_bit_cast(u32x4_t, acc);
+    }
+    // B rows: only wave 0 of k chunk 0 reads them (the others load zeros, no traffic)
+    rlr_b = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_b), (wave == 0 && blockIdx.z == 0) ? uint32_t(N) * lr_r * 2 : 0u);
+    lr_lane = 8 * c < lr_r ? (uint32_t(r) * lr_r + 8 * c) * 2 : 0x80000000u;
+  }
+
   // ---- 2. this wave's activations.  Workgroup row blockIdx.y takes the TB 16-token
   // blocks starting at token tb0 = 16 TB blockIdx.y; in block b, MFMA row r is token
   // tb0 + 16 b + r (rows past T repeat a real token and are never stored).
@@ -198,21 +229,6 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       }
   }
 
-  // The side path's u rows of this token block: lane (r, c) holds ranks 8c .. 8c + 7 of
-  // token row r (clamped like the activations; ranks past R read zeros).
-  __amdgpu_buffer_rsrc_t rlr_b = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_b), 0u);
-  uint32_t lr_lane = 0;
-  u32x4_t Uraw[2], Uop[2];
-  if constexpr (LR) {
-    const int xr = tb0 + min(r, Tw - 1);
-    const __amdgpu_buffer_rsrc_t ru = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_u), uint32_t(T) * lr_r * 4);
-    const uint32_t uo = 8 * c < lr_r ? (uint32_t(xr) * lr_r + 8 * c) * 4 : 0x80000000u;
-    Uraw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, uo, 0, 0));
-    Uraw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, uo == 0x80000000u ? uo : uo + 16, 0, 0));
-    // B rows: only wave 0 of k chunk 0 reads them (the others load zeros, no traffic)
-    rlr_b = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_b), (wave == 0 && blockIdx.z == 0) ? uint32_t(N) * lr_r * 2 : 0u);
-    lr_lane = 8 * c < lr_r ? (uint32_t(r) * lr_r + 8 * c) * 2 : 0x80000000u;
-  }
   auto load_lr = [&](Codes<G, S, TPW, LR>& C, int nb) __attribute__((always_inline)) {
     if constexpr (LR)
       C.lr.v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
@@ -542,6 +558,18 @@ constexpr bool two_blocks_fit(int G, int S, int NA) {
   return NA == 1 && (G == 64 ? S == 1 : (G == 128 ? S <= 3 : S <= 4));
 }
 
+// Group 64 with 4 slices and float32 activations does not fit a wave's registers even
+// with two buffers; the generic decode kernel serves it.
+constexpr bool stream_fits(int G, int S, int NA) { return !(G == 64 && S == 4 && NA == 2); }
+
+// Variants that carry the side path: every streaming variant with one token block per
+// workgroup, and two k tiles per wave where its 20 more registers still fit (group 256
+// with 2 slices and float32 activations would spill).
+constexpr bool lr_fits(int G, int S, int NA) { return stream_fits(G, S, NA); }
+constexpr bool lr_two_tiles_fit(int G, int S, int NA) {
+  return two_tiles_fit(G, S, NA) && !(G == 256 && S == 2 && NA == 2);
+}
+
 // How a launch covers the tokens and k tiles.  Batches of more than 32 tokens put two
 // 16-token blocks in each workgroup (TB = 2) where the registers allow, so the codes are
 // unpacked (and read from L2) once for both; a wave then holds one k tile, so K may need
@@ -553,11 +581,12 @@ struct Plan {
   int tb, tpw, kchunk, ks, nw;
 };
 
-// With the side path (lr) every variant takes one tile and one token block per wave.
+// With the side path (lr) every variant takes one token block per workgroup.
 Plan make_plan(const mbq_desc& d, int32_t t, bool x_bf16, bool lr) {
   const int na = x_bf16 ? 1 : 2;
   const int tb = (!lr && t > 32 && two_blocks_fit(d.group, d.slices, na)) ? 2 : 1;
-  const int tmax = (!lr && tb == 1 && two_tiles_fit(d.group, d.slices, na)) ? 2 : 1;
+  const bool two = lr ? lr_two_tiles_fit(d.group, d.slices, na) : two_tiles_fit(d.group, d.slices, na);
+  const int tmax = (tb == 1 && two) ? 2 : 1;
   const int kb = d.k_tiles;
   int ks = (kb + kMaxWaves * tmax - 1) / (kMaxWaves * tmax);
   const int kchunk = (kb + ks - 1) / ks;
@@ -567,16 +596,10 @@ Plan make_plan(const mbq_desc& d, int32_t t, bool x_bf16, bool lr) {
   return Plan{tb, tpw, kchunk, ks, nw};
 }
 
-// Group 64 with 4 slices and float32 activations does not fit a wave's registers even
-// with two buffers; the generic decode kernel serves it.
-constexpr bool stream_fits(int G, int S, int NA) { return !(G == 64 && S == 4 && NA == 2); }
-
-// Variants that carry the side path: every streaming variant (one tile and one token
-// block per wave leave room for its registers).
-constexpr bool lr_fits(int G, int S, int NA) { return stream_fits(G, S, NA); }
 
 struct LrArgs {
   const float* u;
+  int ks;
   const uint16_t* b;
   int r;
 };
@@ -595,7 +618,7 @@ hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int
   hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
                      0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
                      d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
-                     offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.b, lr.r);
+                     offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.ks, lr.b, lr.r);
   return hipGetLastError();
 }
 
@@ -604,8 +627,13 @@ hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int3
                      const void* x, const int32_t* perm, const int32_t* offsets, void* y,
                      bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream) {
   if constexpr (lr_fits(G, S, NA)) {
-    if (lr.r > 0)
+    if (lr.r > 0) {
+      if constexpr (lr_two_tiles_fit(G, S, NA)) {
+        if (pl.tpw == 2)
+          return launch_gsn<G, S, NA, 2, 1, true>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
+      }
       return launch_gsn<G, S, NA, 1, 1, true>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
+    }
   }
   if constexpr (two_blocks_fit(G, S, NA)) {
     if (pl.tb == 2)
@@ -659,8 +687,8 @@ size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool l
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
                                 void* y, bool y_bf16, void* workspace, const float* lr_u,
-                                const uint16_t* lr_b, int32_t lr_r, hipStream_t stream) {
-  const LrArgs lr{lr_u, lr_b, lr_r};
+                                int32_t lr_ks, const uint16_t* lr_b, int32_t lr_r, hipStream_t stream) {
+  const LrArgs lr{lr_u, lr_ks, lr_b, lr_r};
   const Plan pl = make_plan(d, t, x_bf16, lr_r > 0);
   float* part = pl.ks > 1 ? static_cast<float*>(workspace) : nullptr;
   hipError_t e;

@@ -8,10 +8,12 @@
 // two MFMAs per row block; MFMA prefill: two per output block after the last chunk).  The
 // generic fallback kernels add it afterwards with lowrank_update_kernel.
 //
-// lowrank_u_kernel: one workgroup of 16 waves per 16 tokens.  The waves split K into
-// contiguous ranges of 32-input steps; each multiplies 16 tokens x 16 ranks per step on
-// bf16 MFMA (float32 x as a bf16 hi + lo pair) with two load groups in flight, and LDS
-// sums the 16 partial tiles in a fixed order, so u repeats exactly from run to run.
+// lowrank_u_kernel: workgroups of 16 waves over 16 tokens x one of KSU chunks of K (few
+// tokens get several chunks, so the launch spreads over the chip).  The waves split the
+// chunk into contiguous ranges of 32-input steps; each multiplies 16 tokens x 16 ranks per
+// step on bf16 MFMA (float32 x as a bf16 hi + lo pair) with two load groups in flight,
+// and LDS sums the 16 partial tiles in a fixed order.  Chunk z writes u_part[z] [T x R];
+// the consumers add the chunks in order 0, 1, ..., so u repeats exactly from run to run.
 #include <type_traits>
 
 #include "mbq_internal.h"
@@ -85,17 +87,20 @@ struct LrFrag {
   u32x4_t b[kU][NF];
 };
 
-// u [T x R] = x [T x K] . A^T, A [R x K] bf16.  NF = ceil(R / 16) rank fragments.
+// u_part [KSU x T x R]: chunk blockIdx.y of x [T x K] . A^T, A [R x K] bf16.
+// NF = ceil(R / 16) rank fragments; kpc 32-input steps per chunk.
 template <bool XBF16, bool VEC, int NF>
 __global__ __launch_bounds__(1024) void lowrank_u_kernel(const void* __restrict__ x, int T, int K,
                                                          const uint16_t* __restrict__ A, int R,
-                                                         float* __restrict__ u) {
+                                                         int kpc, float* __restrict__ u) {
   constexpr int NW = 16, ESZ = XBF16 ? 2 : 4;
   __shared__ float red[NW][16][16 * NF];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * 16;
-  const int nsteps = (K + 31) >> 5, q = (nsteps + NW - 1) / NW;
-  const int sb = min(wave * q, nsteps), se = min(sb + q, nsteps);
+  const int nsteps = (K + 31) >> 5;
+  const int cb = min(int(blockIdx.y) * kpc, nsteps), ce = min(cb + kpc, nsteps);
+  const int q = (ce - cb + NW - 1) / NW;
+  const int sb = min(cb + wave * q, ce), se = min(sb + q, ce);
   const __amdgpu_buffer_rsrc_t rx = rsrc(x, uint32_t(T) * uint32_t(K) * ESZ);
   const __amdgpu_buffer_rsrc_t ra = rsrc(A, uint32_t(R) * uint32_t(K) * 2);
   const int row = t0 + (lane & 15), kq = 8 * (lane >> 4);
@@ -166,21 +171,26 @@ __global__ __launch_bounds__(1024) void lowrank_u_kernel(const void* __restrict_
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += red[w][tr][rr];
-      u[size_t(t0 + tr) * R + rr] = s;
+      u[(size_t(blockIdx.y) * T + t0 + tr) * R + rr] = s;
     }
   }
 }
 
 // y[t][n] += sum_r u[t][r] B[n][r] (float32 accumulate, fixed order), for the generic
-// kernels.  One thread per (t, n); y is float32 or bfloat16 (rounded once).
-__global__ __launch_bounds__(256) void lowrank_update_kernel(const float* __restrict__ u,
+// kernels; u[t][r] is the sum of the KSU chunks in order.  One thread per (t, n); y is
+// float32 or bfloat16 (rounded again).
+__global__ __launch_bounds__(256) void lowrank_update_kernel(const float* __restrict__ u, int ksu,
                                                              const uint16_t* __restrict__ B, int T, int N,
                                                              int R, void* __restrict__ y, int y_bf16) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
     float s = 0.f;
-    for (int r = 0; r < R; ++r) s = fmaf(u[size_t(t) * R + r], bf16_bits_to_float(B[size_t(n) * R + r]), s);
+    for (int r = 0; r < R; ++r) {
+      float ur = u[size_t(t) * R + r];
+      for (int z = 1; z < ksu; ++z) ur += u[(size_t(z) * T + t) * R + r];
+      s = fmaf(ur, bf16_bits_to_float(B[size_t(n) * R + r]), s);
+    }
     const size_t i = size_t(t) * N + n;
     if (y_bf16) {
       uint16_t* p = static_cast<uint16_t*>(y) + i;
@@ -194,15 +204,26 @@ __global__ __launch_bounds__(256) void lowrank_update_kernel(const float* __rest
 
 }  // namespace
 
+int lowrank_u_chunks(int32_t t, int32_t k) {
+  if (t <= 0) return 1;
+  const int tiles = (t + 15) / 16, nsteps = (k + 31) / 32;
+  // about 128 workgroups, every wave with at least one 32-input step, at most 8 chunks
+  const int ksu = std::min(std::min((128 + tiles - 1) / tiles, kMaxLrChunks), std::max(1, nsteps / 16));
+  const int kpc = (nsteps + ksu - 1) / ksu;
+  return (nsteps + kpc - 1) / kpc;
+}
+
 hipError_t launch_lowrank_u(int32_t t, int32_t k, const void* x, bool x_bf16, const uint16_t* a,
                             int32_t rank, float* u, hipStream_t stream) {
   if (t <= 0) return hipSuccess;
   const bool vec = k % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a) & 15) == 0;
-  const dim3 grid((t + 15) / 16);
+  const int nsteps = (k + 31) / 32, ksu = lowrank_u_chunks(t, k);
+  const int kpc = (nsteps + ksu - 1) / ksu;
+  const dim3 grid((t + 15) / 16, ksu);
   auto go = [&](auto xb, auto vv, auto nf) {
     hipLaunchKernelGGL((lowrank_u_kernel<decltype(xb)::value, decltype(vv)::value, decltype(nf)::value>),
-                       grid, dim3(1024), 0, stream, x, t, k, a, rank, u);
+                       grid, dim3(1024), 0, stream, x, t, k, a, rank, kpc, u);
   };
   auto go_nf = [&](auto xb, auto vv) {
     if (rank > 16) go(xb, vv, std::integral_constant<int, 2>{});
@@ -217,11 +238,11 @@ hipError_t launch_lowrank_u(int32_t t, int32_t k, const void* x, bool x_bf16, co
   return hipGetLastError();
 }
 
-hipError_t launch_lowrank_update(int32_t t, int32_t n, const float* u, const uint16_t* b, int32_t rank,
-                                 void* y, bool y_bf16, hipStream_t stream) {
+hipError_t launch_lowrank_update(int32_t t, int32_t n, const float* u, int32_t ksu, const uint16_t* b,
+                                 int32_t rank, void* y, bool y_bf16, hipStream_t stream) {
   if (t <= 0) return hipSuccess;
   hipLaunchKernelGGL(lowrank_update_kernel, dim3((n + 255) / 256, std::min(t, 4096)), dim3(256), 0,
-                     stream, u, b, t, n, rank, y, int(y_bf16));
+                     stream, u, ksu, b, t, n, rank, y, int(y_bf16));
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ constexpr int kWave = 64;
 constexpr int kRowBlock = 16;    // rows per packed tile
 constexpr int kKTile = 256;      // inputs per packed tile
 constexpr int kTileBytes = 1024; // 16 rows x 256 inputs x 2 bits
+constexpr int kMaxLrChunks = 8;  // K chunks of the low-rank side path's u = x A^T
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -54,7 +55,7 @@ bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16, bool lr 
 size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool lr);
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
-                                void* y, bool y_bf16, void* ws, const float* lr_u,
+                                void* y, bool y_bf16, void* ws, const float* lr_u, int32_t lr_ks,
                                 const uint16_t* lr_b, int32_t lr_r, hipStream_t stream);
 hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                           bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
@@ -62,11 +63,12 @@ hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, cons
 bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_bf16);
 hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
-                               bool y_bf16, const float* lr_u, const uint16_t* lr_b, int32_t lr_r,
-                               hipStream_t stream);
+                               bool y_bf16, const float* lr_u, int32_t lr_ks, const uint16_t* lr_b,
+                               int32_t lr_r, hipStream_t stream);
 hipError_t launch_lowrank_u(int32_t t, int32_t k, const void* x, bool x_bf16, const uint16_t* a,
                             int32_t rank, float* u, hipStream_t stream);
-hipError_t launch_lowrank_update(int32_t t, int32_t n, const float* u, const uint16_t* b, int32_t rank,
-                                 void* y, bool y_bf16, hipStream_t stream);
+int lowrank_u_chunks(int32_t t, int32_t k);
+hipError_t launch_lowrank_update(int32_t t, int32_t n, const float* u, int32_t ksu, const uint16_t* b,
+                                 int32_t rank, void* y, bool y_bf16, hipStream_t stream);
 
 }  // namespace mbq

@@ -160,10 +160,11 @@ struct TileArgs {
   const int32_t* perm;
   void* y;
   int y_bf16;
-  // low-rank side path (lr_r == 0: none): u [T x lr_r] float32, B [N x lr_r] bf16
+  // low-rank side path (lr_r == 0: none): u [lr_ks x T x lr_r] float32 (chunks of K,
+  // summed in order), B [N x lr_r] bf16
   const float* lr_u;
   const uint16_t* lr_b;
-  int lr_r;
+  int lr_r, lr_ks;
 };
 
 // Epilogue: a wave's outputs are staged in LDS as rows of 64 values (+16 bytes of
@@ -432,7 +433,7 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& a, int start, int r
   // tile's tokens (row -> token table; padding rows read zeros), the B columns its outputs.
   if (a.lr_r > 0) {
     const int R = a.lr_r;
-    const __amdgpu_buffer_rsrc_t ru = rsrc(a.lr_u, uint32_t(a.T) * uint32_t(R) * 4u);
+    const __amdgpu_buffer_rsrc_t ru = rsrc(a.lr_u, uint32_t(a.lr_ks) * uint32_t(a.T) * uint32_t(R) * 4u);
     const __amdgpu_buffer_rsrc_t rb = rsrc(a.lr_b, uint32_t(a.N) * uint32_t(R) * 2u);
     for (int k0 = 0; k0 < R; k0 += 16) {
       const int kk = k0 + 8 * c2;
@@ -446,10 +447,14 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& a, int start, int r
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int tok = tokT[WM * wm + 32 * i + col];
-        const uint32_t off = (tok >= 0 && kk < R) ? (uint32_t(tok) * R + kk) * 4u : 0x80000000u;
-        const u32x4_t u0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, 0));
-        const u32x4_t u1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                               ru, off == 0x80000000u ? off : off + 16u, 0, 0));
+        f32x4_t f0{0.f, 0.f, 0.f, 0.f}, f1{0.f, 0.f, 0.f, 0.f};
+        for (int z = 0; z < a.lr_ks; ++z) {
+          const uint32_t off = (tok >= 0 && kk < R) ? ((uint32_t(z) * a.T + tok) * R + kk) * 4u : 0x80000000u;
+          f0 += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, off, 0, 0));
+          f1 += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    ru, off == 0x80000000u ? off : off + 16u, 0, 0));
+        }
+        const u32x4_t u0 = __builtin_bit_cast(u32x4_t, f0), u1 = __builtin_bit_cast(u32x4_t, f1);
         u32x4_t uh, ul;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -555,8 +560,8 @@ bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_
 
 hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
-                               bool y_bf16, const float* lr_u, const uint16_t* lr_b, int32_t lr_r,
-                               hipStream_t stream) {
+                               bool y_bf16, const float* lr_u, int32_t lr_ks, const uint16_t* lr_b,
+                               int32_t lr_r, hipStream_t stream) {
   const int BM = x_bf16 ? 256 : 128;
   TileArgs a{};
   a.packed = static_cast<const uint8_t*>(packed);
@@ -578,6 +583,7 @@ hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t,
   a.lr_u = lr_u;
   a.lr_b = lr_b;
   a.lr_r = lr_r;
+  a.lr_ks = lr_ks;
   const int NT = (d.n + kBN - 1) / kBN;
   // at most ceil(R / BM) tiles per budget group (a half tile replaces a full one)
   const int max_tiles = NT * ((t + BM - 1) / BM + d.slices - 1);
