@@ -39,6 +39,13 @@ Readings where the pages leave a step open (each one is listed in the design doc):
     quantized part adjusted and the rank-r factors kept beside it; section 4: r = 16):
     here Wq is the token's MoBiSlice reconstruction W^(b), and B [N, r], A [r, K] are one
     pair shared by every token whatever its b, so y_t = x_t . W^(b(t))^T + (x_t . A^T) . B^T.
+  * The bit-plane reading of the "MSB slice plus residual slices" wording (English
+    explainer section 2.A, Japanese section 2.1): one uniform 2S-bit min/max code per
+    weight (4^S levels, step = span / (4^S - 1), rounded to half, zero = half(min)), slice
+    j holding its j-th 2-bit plane from the top.  The slice params are chosen so that the
+    same prefix sum the kernels compute gives the b-plane value centred over the dropped
+    planes: scale_j = step * 4^(S-j), zero_1 = min + c_1, zero_j = c_j - c_(j-1) with
+    c_b = step * (4^(S-b) - 1) / 2 (each rounded to half).
   * Regrouping is a stable sort of tokens by ascending slice count.
   * Dot products and reconstruction are exact in float64 on the stored codes and params.
 
@@ -121,6 +128,44 @@ def pack(W: np.ndarray, group: int, slices: int):
         flags |= f
     return {"codes": codes, "scale": scale, "zero": zero, "residuals": residuals,
             "flags": flags, "group": group}
+
+
+def pack_bitplane(W: np.ndarray, group: int, slices: int):
+    """Bit-plane slices: planes of one uniform 2S-bit code per weight (see the reading
+    above).  Same output layout as pack(): codes uint8 [S, N, K] (plane values 0..3),
+    scale/zero float16 [S, N, K/G], flags; plus the full codes q [N, K] (uint16)."""
+    W = np.asarray(W, dtype=F32)
+    flags = 0 if np.all(np.isfinite(W)) else 1
+    N, K = W.shape
+    S = slices
+    levels = 4 ** S - 1
+    Wg = W.reshape(N, K // group, group)
+    lo = (Wg.min(axis=2) + F32(0.0)).astype(F32)   # a signed-zero minimum is stored as +0
+    hi = Wg.max(axis=2)
+    with np.errstate(over="ignore", invalid="ignore"):
+        span = (hi - lo).astype(F32)
+        step = (span / F32(levels)).astype(F32).astype(F16)
+        zero_h = lo.astype(F16)
+    sf = step.astype(F32)
+    zf = zero_h.astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        u = ((Wg - zf[:, :, None]).astype(F32) / sf[:, :, None]).astype(F32)
+        q = np.clip(np.rint(u), 0.0, float(levels))
+    q = np.where(sf[:, :, None] == 0.0, 0.0, q).astype(np.uint16)
+    codes = np.zeros((S, N, K), np.uint8)
+    scale = np.zeros((S, N, K // group), F16)
+    zero = np.zeros((S, N, K // group), F16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        c = [(sf * F32((4 ** (S - b) - 1) / 2)).astype(F32) for b in range(1, S + 1)]
+        for j in range(1, S + 1):
+            codes[j - 1] = ((q >> (2 * (S - j))) & 3).reshape(N, K).astype(np.uint8)
+            scale[j - 1] = (sf * F32(4 ** (S - j))).astype(F32).astype(F16)
+            z = (zf + c[0]) if j == 1 else (c[j - 1] - c[j - 2])
+            zero[j - 1] = z.astype(F32).astype(F16)
+    if not (np.all(np.isfinite(scale)) and np.all(np.isfinite(zero))):
+        flags |= 2
+    return {"codes": codes, "scale": scale, "zero": zero, "flags": flags, "group": group,
+            "q": q.reshape(N, K), "step": step, "lo": zero_h}
 
 
 # ----------------------------------------------------------------------------------------

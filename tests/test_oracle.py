@@ -394,6 +394,89 @@ def test_lowrank_rank_one_closed_form_and_additivity():
                                O.lowrank_term(X, A1, B1) + O.lowrank_term(X, A2, B2), atol=1e-12)
 
 
+# ---------------------------------------------------------------- bit-plane slices
+def _bp(seed=51, N=24, K=512, G=128, S=3):
+    d = inputs.make_linear(seed, N, K, 1, group=G, dtype="f32", n_outliers=3, outlier_scale=8.0)
+    return d["W"], O.pack_bitplane(d["W"], G, S)
+
+
+def test_bitplane_planes_reassemble_the_code():
+    W, p = _bp()
+    q = np.zeros_like(p["q"], dtype=np.int64)
+    for j in range(3):
+        q = q * 4 + p["codes"][j]
+    assert np.array_equal(q, p["q"])
+    assert p["q"].max() <= 63 and p["codes"].max() <= 3
+
+
+def test_bitplane_code_is_nearest_level():
+    # brute force over the 64 levels zero + m * step (float64), away from exact ties
+    W, p = _bp(seed=52, N=8, K=256, G=64)
+    step = p["step"].astype(np.float64)
+    lo = p["lo"].astype(np.float64)
+    for n in range(8):
+        for k in range(256):
+            g = k // 64
+            if step[n, g] == 0:
+                assert p["q"][n, k] == 0
+                continue
+            levels = lo[n, g] + step[n, g] * np.arange(64)
+            dist = np.abs(levels - float(W[n, k]))
+            best = np.argsort(dist)[:2]
+            if dist[best[1]] - dist[best[0]] > 1e-6 * step[n, g]:
+                assert p["q"][n, k] == best[0]
+
+
+def test_bitplane_full_precision_is_the_uniform_grid():
+    # all S planes: zero + q * step, up to the half rounding of the stored zeros (the
+    # scales are the half step times powers of four, exact)
+    W, p = _bp(seed=53)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 128)
+    full = O.reconstruct(deq, 3)
+    step = np.repeat(p["step"].astype(np.float64), 128, axis=1)
+    grid = np.repeat(p["lo"].astype(np.float64), 128, axis=1) + p["q"] * step
+    for j in range(3):
+        assert np.array_equal(p["scale"][j].astype(np.float64), p["step"].astype(np.float64) * 4 ** (2 - j))
+    half_ulp = sum(np.spacing(np.abs(p["zero"][j])).astype(np.float64) / 2 for j in range(3))
+    assert np.all(np.abs(full - grid) <= np.repeat(half_ulp, 128, axis=1) + 1e-12)
+
+
+def test_bitplane_exact_grid_closed_form():
+    # a group on a half-exact grid with zero = 0 and step = 1/64 is reproduced exactly at
+    # S = 3, and b planes give the centred truncation
+    q = np.arange(128) % 64
+    W = (q / 64.0).astype(np.float32)[None, :]
+    W[0, -1] = 63 / 64   # max so that step = (63/64) / 63 = 1/64
+    W[0, 0] = 0.0
+    p = O.pack_bitplane(W, 128, 3)
+    assert p["step"][0, 0] == np.float16(1 / 64) and p["lo"][0, 0] == 0
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 128)
+    np.testing.assert_array_equal(O.reconstruct(deq, 3)[0], W[0].astype(np.float64))
+    for b, keep in ((1, 16), (2, 4)):
+        want = (np.floor(p["q"][0] / keep) * keep + (keep - 1) / 2) / 64
+        np.testing.assert_array_equal(O.reconstruct(deq, b)[0], want)
+
+
+def test_bitplane_error_bounds_and_comparison():
+    W, p = _bp(seed=54, N=32, K=1024)
+    deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 128)
+    step = np.repeat(p["step"].astype(np.float64), 128, axis=1)
+    prev = np.inf
+    for b in range(1, 4):
+        err = np.abs(W.astype(np.float64) - O.reconstruct(deq, b))
+        # b planes: half the b-plane step (centred truncation) plus half a fine step
+        bound = step * (4 ** (3 - b) / 2 + 0.5) * (1 + 1e-3) + 1e-12
+        assert np.all(err <= bound)
+        assert err.max() <= prev
+        prev = err.max()
+    # against the residual slices at full precision: the uniform 6-bit grid is finer
+    pr = O.pack(W, 128, 3)
+    dr = O.dequant_slices(pr["codes"], pr["scale"], pr["zero"], 128)
+    e_bp = np.abs(W - O.reconstruct(deq, 3)).mean()
+    e_rr = np.abs(W - O.reconstruct(dr, 3)).mean()
+    assert e_bp < e_rr
+
+
 # ---------------------------------------------------------------- the packed blob format
 def test_blob_sizes_match_workloads():
     # 2.25 bits per weight per slice at G=128, 2.5 at G=64 (codes + half scale and zero)
