@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=16, help="decode batch (1, 4 or 16)")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer", "traffic", "route_mlp", "lowrank"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "sweep", "layer", "traffic", "route_mlp", "lowrank", "bitplane"], default=None,
                     help="run one workload only (for profiling); prints its own JSON line.  "
                          "'traffic' runs a copy kernel of known size and then the decode linear, "
                          "for the FETCH_SIZE / WRITE_SIZE counter passes")
@@ -294,6 +294,34 @@ def bench_route_mlp(api, torch, inputs, dev, iters=50):
     return out
 
 
+def bench_bitplane(api, torch, inputs, dev):
+    """Residual slices against bit-plane slices on the decode weight (18944 x 3584, G128,
+    S3): relative error of x . W^(b)^T against the float32 product x . W^T for each b
+    (every token forced to b), the routed linear's time on each blob, and pack times."""
+    d = inputs.make_config(2)
+    T = 16
+    W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
+    X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
+    ref = X.float() @ W.float().t()
+    out = {}
+    for name, fn in (("residual", api.pack), ("bitplane", api.pack_bitplane)):
+        p = fn(W, 128, 3)
+        torch.cuda.synchronize()
+        tp = time_events(torch, lambda i: fn(W, 128, 3, out=p.blob), 5)
+        res = {"pack_us": tp * 1e6}
+        y = torch.empty((T, d["N"]), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, api.linear_workspace(p, T)), dtype=torch.uint8, device=dev)
+        for b in (1, 2, 3):
+            perm, off = api.regroup(torch.full((T,), b, dtype=torch.int32, device=dev), 3)
+            api.linear(p, X, perm, off, y=y, workspace=ws)
+            torch.cuda.synchronize()
+            res[f"rel_err_b{b}"] = float(((y - ref).norm() / ref.norm()).item())
+            res[f"linear_us_b{b}"] = time_events(torch, lambda i: api.linear(p, X, perm, off, y=y, workspace=ws), 20) * 1e6
+        out[name] = res
+        del p
+    return out
+
+
 def bench_lowrank(api, torch, inputs, dev, iters=30):
     """The low-rank side path (rank 16) on the decode workload (T = 16) and the prefill
     workload (T = 2048): routed linear with and without it, and u = x A^T alone."""
@@ -460,6 +488,9 @@ def main():
     if args.only == "layer":
         print(json.dumps({"workload": "layer", **bench_layer(api, torch, inputs, dev)}))
         return
+    if args.only == "bitplane":
+        print(json.dumps({"workload": "bitplane", **bench_bitplane(api, torch, inputs, dev)}))
+        return
     if args.only == "lowrank":
         print(json.dumps({"workload": "lowrank", **bench_lowrank(api, torch, inputs, dev)}))
         return
@@ -519,6 +550,8 @@ def main():
         extra["sweep_14336x4096"] = bench_sweep(api, torch, inputs, dev)
         log("MLP router with threshold delta")
         extra["route_mlp_h256_s3"] = bench_route_mlp(api, torch, inputs, dev)
+        log("bit-plane slices")
+        extra["bitplane_vs_residual_18944x3584"] = bench_bitplane(api, torch, inputs, dev)
         log("low-rank side path")
         extra["lowrank_r16"] = bench_lowrank(api, torch, inputs, dev)
         log("14B-like layer, T=64")

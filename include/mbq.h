@@ -115,6 +115,20 @@ mbq_status mbq_pack(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void
                     int32_t* dev_status, hipStream_t stream);
 
 /*
+ * Bit-plane pack: the other reading of the English page's "MSB slice plus residual bit
+ * slices" (section 2.A; Japanese page section 2.1).  Each weight gets one uniform 2S-bit
+ * min/max code per group (4^S levels, step = half((max - min) / (4^S - 1)), zero =
+ * half(min), code = clamp(rint((w - zero) / step), 0, 4^S - 1), float32 as in mbq_pack);
+ * slice j (1-based) stores the code's j-th 2-bit plane from the top, with scale
+ * half(step * 4^(S-j)) and zero half(zero + c_1) for j = 1, half(c_j - c_(j-1)) after,
+ * c_b = step * (4^(S-b) - 1) / 2, so that the linear kernels' prefix sum over b slices is
+ * the b-plane value centred over the dropped planes.  Same blob layout, arguments and
+ * status bits as mbq_pack; the routed linear is unchanged.
+ */
+mbq_status mbq_pack_bitplane(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void* packed,
+                             int32_t* dev_status, hipStream_t stream);
+
+/*
  * MoBiSlice pack of a row range: W_part [rows x k] becomes rows row0 .. row0 + rows - 1 of
  * the blob described by desc (desc->n rows in all).  Quantization groups lie within one
  * row, so the codes and params of those rows are exactly what mbq_pack of the whole

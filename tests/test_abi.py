@@ -90,6 +90,16 @@ def test_pack_validation():
     assert L.mbq_pack(ctypes.byref(bad), P(FAKE), F32, P(FAKE), None, None) == SHAPE
 
 
+def test_pack_bitplane_validation():
+    st, d = desc(100, 512, 128, 3)
+    dp, f = ctypes.byref(d), P(FAKE)
+    assert L.mbq_pack_bitplane(dp, None, F32, f, None, None) == ARG
+    assert L.mbq_pack_bitplane(dp, f, 7, f, None, None) == ARG
+    assert L.mbq_pack_bitplane(dp, f, F32, P(FAKE + 16), None, None) == ARG
+    assert L.mbq_pack_bitplane(dp, f, F32, f, P(FAKE + 2), None) == ARG
+    assert L.mbq_pack_bitplane(None, f, F32, f, None, None) == ARG
+
+
 def test_pack_rows_validation():
     st, d = desc(100, 512, 128, 3)
     dp, f = ctypes.byref(d), P(FAKE)

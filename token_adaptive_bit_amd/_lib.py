@@ -18,7 +18,7 @@ ABI_VERSION = 1
 STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANGE",
           -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}
 
-EXPORTS = ("mbq_describe", "mbq_pack", "mbq_pack_rows", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
+EXPORTS = ("mbq_describe", "mbq_pack", "mbq_pack_rows", "mbq_pack_bitplane", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
            "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_linear_lowrank_workspace",
            "mbq_linear_lowrank", "mbq_status_str", "mbq_abi_version")
 
@@ -59,6 +59,7 @@ def _load() -> ctypes.CDLL:
     lib.mbq_describe.argtypes = [I32, I32, I32, I32, D]
     lib.mbq_pack.argtypes = [D, VP, I32, VP, VP, VP]
     lib.mbq_pack_rows.argtypes = [D, I32, I32, VP, I32, VP, VP, VP]
+    lib.mbq_pack_bitplane.argtypes = [D, VP, I32, VP, VP, VP]
     lib.mbq_route.argtypes = [I32, I32, I32, VP, I32, VP, VP, VP, VP, VP, VP]
     lib.mbq_regroup.argtypes = [I32, I32, VP, VP, VP, VP]
     lib.mbq_route_mlp_workspace.argtypes = [I32, I32, I32, P(ctypes.c_size_t)]

@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import MBQ_BF16, MBQ_F32, MbqDesc, MbqError, check, describe
 
-__all__ = ["PackedLinear", "pack", "pack_concat", "route", "route_from_logits", "regroup", "linear",
+__all__ = ["PackedLinear", "pack", "pack_bitplane", "pack_concat", "route", "route_from_logits", "regroup", "linear",
            "linear_workspace", "describe", "MbqError", "MlpRouter", "route_mlp",
            "route_mlp_from_scores", "route_mlp_workspace", "linear_lowrank",
            "linear_lowrank_workspace"]
@@ -76,6 +76,22 @@ def pack(w: torch.Tensor, group: int = 128, slices: int = 3, status: torch.Tenso
         raise ValueError("out is smaller than the packed size")
     check(_lib.LIB.mbq_pack(ctypes.byref(d), _p(w), _dtype(w), _p(out), _p(status), _stream()),
           "mbq_pack")
+    return PackedLinear(d, out)
+
+
+def pack_bitplane(w: torch.Tensor, group: int = 128, slices: int = 3,
+                  status: torch.Tensor | None = None, out: torch.Tensor | None = None) -> PackedLinear:
+    """Bit-plane pack of W [n, k]: slice j is the j-th 2-bit plane of one uniform 2S-bit
+    code; the routed linear reads it like any other blob."""
+    _dev(w, "w")
+    n, k = w.shape
+    d = describe(n, k, group, slices)
+    if out is None:
+        out = torch.empty(int(d.total_bytes), dtype=torch.uint8, device=w.device)
+    if out.numel() < d.total_bytes:
+        raise ValueError("out is smaller than the packed size")
+    check(_lib.LIB.mbq_pack_bitplane(ctypes.byref(d), _p(w), _dtype(w), _p(out), _p(status), _stream()),
+          "mbq_pack_bitplane")
     return PackedLinear(d, out)
 
 

@@ -90,6 +90,16 @@ mbq_status mbq_pack(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void
                                    stream));
 }
 
+mbq_status mbq_pack_bitplane(const mbq_desc* desc, const void* w, mbq_dtype w_dtype, void* packed,
+                             int32_t* dev_status, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (!valid_dtype(w_dtype) || !w || !packed) return MBQ_ERR_ARG;
+  if (!aligned(packed, 256) || !aligned(w, w_dtype == MBQ_F32 ? 4 : 2)) return MBQ_ERR_ARG;
+  if (dev_status && !aligned(dev_status, 4)) return MBQ_ERR_ARG;
+  return launched(mbq::launch_pack_bitplane(*desc, w, w_dtype == MBQ_BF16, packed, dev_status, stream));
+}
+
 mbq_status mbq_pack_rows(const mbq_desc* desc, int32_t row0, int32_t rows, const void* w,
                          mbq_dtype w_dtype, void* packed, int32_t* dev_status, hipStream_t stream) {
   mbq_status st = check_desc(desc);

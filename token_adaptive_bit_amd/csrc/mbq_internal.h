@@ -39,6 +39,8 @@ __device__ __forceinline__ float load_x(const void* p, size_t idx, bool is_bf16)
 // Host-side launchers (one per translation unit).
 hipError_t launch_pack(const mbq_desc& d, int32_t row0, int32_t rows, const void* w, bool w_bf16,
                        void* packed, int32_t* dev_status, hipStream_t stream);
+hipError_t launch_pack_bitplane(const mbq_desc& d, const void* w, bool w_bf16, void* packed,
+                                int32_t* dev_status, hipStream_t stream);
 hipError_t launch_route(int32_t t, int32_t k, int32_t s, const void* x, bool x_bf16,
                         const float* wr, float* logits, const int32_t* budget_in,
                         int32_t* budget, int32_t* perm, int32_t* offsets, hipStream_t stream);
