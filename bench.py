@@ -6,12 +6,15 @@ G = 128, 3 slices, a batch of 16 bf16 tokens): router logits + argmax + stable r
 (mbq_route) and the routed decode linear (mbq_linear).  Packing is an offline, once-per-
 weight step and is timed separately (reported under "extra").
 
-value = tokens / s over the timed steps (inputs resident in HBM).  The roofline object
-is for the dominant kernel (the routed decode GEMV): algorithmic bytes per launch (the
-slices the batch needs, plus activations and outputs) over its average duration measured
-with HIP events on the launch stream inside the timed region.  The packed weight is
-rotated over enough copies (> 512 MiB) that neither L2 nor the 256 MiB Infinity Cache
-can serve a repeat.
+value = tokens / s over the timed steps (inputs resident in HBM), each step replayed from
+a HIP graph captured once per weight copy (the three kernels of a step launch without the
+host's per-call overhead between them; the same steps launched one by one are reported as
+eager_ms_per_step).  The roofline object is for the dominant kernel (the routed decode
+GEMV): algorithmic bytes per launch (the slices the batch needs, plus activations and
+outputs) over its average duration measured with HIP events on the launch stream around
+each routed linear of a timed pass of the same steps launched one by one.  The packed
+weight is rotated over enough copies (> 512 MiB) that neither L2 nor the 256 MiB Infinity
+Cache can serve a repeat.
 """
 from __future__ import annotations
 
@@ -151,7 +154,7 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: exactly `steps` steps; events bracket the routed linear of each step
+    # the dominant kernel's duration: events bracket the routed linear of each step
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -163,9 +166,33 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lin_s = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    eager_step_s = (t1 - t0) / steps
+    # timed region for the step rate: each step (route + routed linear on weight copy
+    # i % nb) replayed from a HIP graph captured once per copy, so the host's launch
+    # overhead does not gap the three kernels
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step(0)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for c in range(nb):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(c)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % nb].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % nb].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     jmax = int((off[:3] < T).sum().item())      # slices with at least one token
     counts = torch.diff(off).cpu().tolist()
-    return {"T": T, "step_s": (t1 - t0) / steps, "linear_s": lin_s, "jmax": jmax,
+    return {"T": T, "step_s": (t1 - t0) / steps, "eager_step_s": eager_step_s, "linear_s": lin_s, "jmax": jmax,
             "budget_counts": counts, "bytes": decode_bytes(blobs[0], T, jmax),
             "weight_bytes": weight_bytes(blobs[0], jmax), "copies": nb,
             "blob_bytes": int(blobs[0].blob.numel()), "N": d["N"], "K": d["K"]}
@@ -528,6 +555,8 @@ def main():
                      "traffic": traffic},
         "effective_weight_gbs": r["weight_bytes"] / r["linear_s"] / 1e9,
         "linear_us": r["linear_s"] * 1e6,
+        "step_launch": "hip_graph",
+        "eager_ms_per_step": r["eager_step_s"] * 1e3,
     }
     if not args.no_extra and args.only is None:  # (--only decode prints the headline line alone)
         extra = {}

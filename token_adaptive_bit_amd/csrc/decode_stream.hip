@@ -140,6 +140,12 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     float* __restrict__ part, const float* __restrict__ lr_u, int lr_ks,
     const uint16_t* __restrict__ lr_b, int lr_r) {
   static_assert(!LR || TB == 1, "the side path is built for one token block per workgroup");
+  // Every kernel argument is read in one batch behind one wait: loaded lazily, they come
+  // from up to three scalar cache lines in turn, each a round trip before the first
+  // activation load can be issued.
+  asm volatile("" ::"s"(packed), "s"(x), "s"(perm), "s"(offsets), "s"(y), "s"(part), "s"(lr_u), "s"(lr_b));
+  asm volatile("" ::"s"(N), "s"(K), "s"(KB), "s"(NG), "s"(NB), "s"(ss), "s"(po), "s"(T), "s"(y_bf16),
+               "s"(kchunk), "s"(lr_ks), "s"(lr_r));
   constexpr int GPT = 256 / G, WPG = G / 64;
   __shared__ f32x4_t red[2][kMaxWaves][TB][64];
   const int NW = blockDim.x >> 6;
@@ -159,18 +165,15 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     kt[tp] = live[tp] ? t : kb0;
   }
 
-  // ---- 1. routing.  The number of slices read (jmax) comes from offsets alone, through
-  // the scalar cache: 1 + #{j >= 1 : offsets[j] < T} (every slice some token of the batch
-  // uses).  Per-token budgets come from perm: lane i of wave 0 takes sorted position i
-  // (T <= 64) and later publishes that token's budget in an LDS table.  The perm load is
-  // issued first, so waiting for it never waits for the activation loads behind it.
-  int off[S + 1];
-#pragma unroll
-  for (int j = 0; j <= S; ++j) off[j] = offsets[j];
-  int jmax = 1;
-#pragma unroll
-  for (int j = 1; j < S; ++j)
-    if (off[j] <= T - 1) jmax = j + 1;
+  // ---- 1. routing.  The number of slices read (jmax) comes from offsets alone: 1 +
+  // #{j >= 1 : offsets[j] < T} (every slice some token of the batch uses).  offsets[0..S]
+  // arrive through one vector load (lane j takes offsets[j]) and are read back with
+  // readlane after the activation loads have been issued: a scalar load would sit in front
+  // of them, since a wait for any later kernel argument waits for every scalar load.
+  // Per-token budgets come from perm: lane i of wave 0 takes sorted position i (T <= 64)
+  // and later publishes that token's budget in an LDS table.  Both loads are issued
+  // first, so waiting for them never waits for the activation loads behind them.
+  const int offv = offsets[min(lane, S)];
   const int pi = (wave == 0 && lane < T) ? perm[lane] : -1;
 
   // The side path's u rows of this token block: lane (r, c) holds ranks 8c .. 8c + 7 of
@@ -228,6 +231,16 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           }
       }
   }
+
+  // (the fence keeps every activation load ahead of the wait for offsets)
+  __builtin_amdgcn_sched_barrier(0);
+  int off[S + 1];
+#pragma unroll
+  for (int j = 0; j <= S; ++j) off[j] = __builtin_amdgcn_readlane(offv, j);
+  int jmax = 1;
+#pragma unroll
+  for (int j = 1; j < S; ++j)
+    if (off[j] <= T - 1) jmax = j + 1;
 
   auto load_lr = [&](Codes<G, S, TPW, LR>& C, int nb) __attribute__((always_inline)) {
     if constexpr (LR)
