@@ -3,16 +3,19 @@
 Prints one JSON line.  A step is one pass of the per-batch hot path on the decode
 workload (Qwen2.5-7B-like up-projection, W 18944 x 3584 bf16 with 0.5% outlier columns,
 G = 128, 3 slices, a batch of 16 bf16 tokens): router logits + argmax + stable regroup
-(mbq_route) and the routed decode linear (mbq_linear).  Packing is an offline, once-per-
-weight step and is timed separately (reported under "extra").
+and the routed decode linear, in one call (mbq_route_linear: the streaming decode kernel
+routes the batch itself, one launch per step).  Packing is an offline, once-per-weight
+step and is timed separately (reported under "extra").
 
-value = tokens / s over the timed steps (inputs resident in HBM), each step replayed from
-a HIP graph captured once per weight copy (the three kernels of a step launch without the
-host's per-call overhead between them; the same steps launched one by one are reported as
-eager_ms_per_step).  The roofline object is for the dominant kernel (the routed decode
-GEMV): algorithmic bytes per launch (the slices the batch needs, plus activations and
-outputs) over its average duration measured with HIP events on the launch stream around
-each routed linear of a timed pass of the same steps launched one by one.  The packed
+value = tokens / s over the timed steps (inputs resident in HBM), replayed from HIP graphs
+(one graph holding a step per weight copy, so neither the host's per-call overhead nor a
+per-replay submission gaps the kernels; the same steps launched one by one are reported as
+eager_ms_per_step, and the two-call form -- mbq_route's two kernels, then mbq_linear -- as
+two_call_ms_per_step).  The roofline object is for the dominant kernel (the step's one
+kernel): algorithmic bytes per launch (the slices the batch needs, activations, outputs,
+Wr and the routing outputs) over its average duration from HIP events on the launch
+stream around the timed replays (one launch per step, so this holds the kernel and the
+gap to the next launch; the committed rocprofv3 trace gives the kernel alone).  The packed
 weight is rotated over enough copies (> 512 MiB) that neither L2 nor the 256 MiB Infinity
 Cache can serve a repeat.
 """
@@ -66,10 +69,15 @@ def make_blobs(api, torch, W, group, slices, dev):
     return blobs
 
 
-def decode_bytes(p, T, jmax):
-    """Algorithmic bytes of one routed decode launch: needed slices + x + y + routing."""
+def decode_bytes(p, T, jmax, router=False):
+    """Algorithmic bytes of one routed decode launch: needed slices + x + y + routing
+    (perm and offsets read; with the router in the launch, Wr read and logits, budget,
+    perm and offsets written instead)."""
     d = p.desc
-    return jmax * int(d.slice_stride) + T * d.k * 2 + T * d.n * 2 + T * 4 + (d.slices + 1) * 4
+    base = jmax * int(d.slice_stride) + T * d.k * 2 + T * d.n * 2
+    if router:
+        return base + d.k * d.slices * 4 + T * d.slices * 4 + 2 * T * 4 + (d.slices + 1) * 4
+    return base + T * 4 + (d.slices + 1) * 4
 
 
 def weight_bytes(p, jmax):
@@ -148,52 +156,65 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev):
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
     def step(i):
+        # one launch: routing inside the streaming decode kernel (mbq_route_linear)
+        api.route_linear(blobs[i % nb], X, Wr, y=y, logits=logits, budget=budget, perm=perm, offsets=off,
+                         workspace=ws if ws_n else None)
+
+    def step_two_calls(i):
         api.route(X, Wr, logits, budget, perm, off)
         api.linear(blobs[i % nb], X, perm, off, y=y, workspace=ws if ws_n else None)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # the dominant kernel's duration: events bracket the routed linear of each step
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        api.route(X, Wr, logits, budget, perm, off)
-        ev[i][0].record()
-        api.linear(blobs[i % nb], X, perm, off, y=y, workspace=ws if ws_n else None)
-        ev[i][1].record()
+        step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    lin_s = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
-    eager_step_s = (t1 - t0) / steps
-    # timed region for the step rate: each step (route + routed linear on weight copy
-    # i % nb) replayed from a HIP graph captured once per copy, so the host's launch
-    # overhead does not gap the three kernels
-    graphs = []
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        step(0)
-    torch.cuda.current_stream().wait_stream(cap)
-    torch.cuda.synchronize()
-    for c in range(nb):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(c)
-        graphs.append(g)
-    for i in range(warmup):
-        graphs[i % nb].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % nb].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    eager_step_s = (time.perf_counter() - t0) / steps
+
+    def graph_steps(fn):
+        """Exactly `steps` steps (step i on weight copy i % nb) from HIP graphs: one graph
+        holding a step per copy, replayed steps // nb times, then one-step graphs for the
+        rest, so neither the host's launch overhead nor a per-replay submission gaps the
+        kernels.  Returns (s per step, s per step from HIP events around the replays)."""
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        big = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(big):
+            for c in range(nb):
+                fn(c)
+        single = []
+        for c in range(steps % nb):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(c)
+            single.append(g)
+        for _ in range(max(1, warmup // nb)):
+            big.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        for _ in range(steps // nb):
+            big.replay()
+        for g in single:
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps, a.elapsed_time(b) / 1e3 / steps
+
+    two_call_step_s, _ = graph_steps(step_two_calls)
+    step_s, lin_s = graph_steps(step)   # last, so logits .. offsets hold this path's routes
     jmax = int((off[:3] < T).sum().item())      # slices with at least one token
     counts = torch.diff(off).cpu().tolist()
-    return {"T": T, "step_s": (t1 - t0) / steps, "eager_step_s": eager_step_s, "linear_s": lin_s, "jmax": jmax,
-            "budget_counts": counts, "bytes": decode_bytes(blobs[0], T, jmax),
+    return {"T": T, "step_s": step_s, "two_call_step_s": two_call_step_s, "eager_step_s": eager_step_s,
+            "linear_s": lin_s, "jmax": jmax,
+            "budget_counts": counts, "bytes": decode_bytes(blobs[0], T, jmax, router=True),
             "weight_bytes": weight_bytes(blobs[0], jmax), "copies": nb,
             "blob_bytes": int(blobs[0].blob.numel()), "N": d["N"], "K": d["K"]}
 
@@ -440,7 +461,7 @@ def bench_layer(api, torch, inputs, dev, iters=20):
 
 def run_traffic(api, torch, inputs, dev, T, launches=20):
     """For the counter passes: 3 copies of 1 GiB (known bytes), then `launches` decode
-    linears over rotated weight copies."""
+    steps (mbq_route_linear) over rotated weight copies."""
     bench_copy(torch, dev)
     d = inputs.make_config(2)
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
@@ -448,15 +469,14 @@ def run_traffic(api, torch, inputs, dev, T, launches=20):
     Wr = torch.from_numpy(d["Wr"]).to(dev, torch.float32)
     blobs = make_blobs(api, torch, W, 128, 3, dev)
     del W
-    _, _, perm, off = api.route(X, Wr)
     y = torch.empty((T, d["N"]), dtype=torch.bfloat16, device=dev)
-    for i in range(launches):
-        api.linear(blobs[i % len(blobs)], X, perm, off, y=y)
+    for i in range(launches):          # the decode step as timed: one launch, routing inside
+        _, _, _, _, off = api.route_linear(blobs[i % len(blobs)], X, Wr, y=y)
     torch.cuda.synchronize()
     counts = torch.diff(off).cpu().tolist()
     jmax = max(j + 1 for j in range(3) if counts[j] > 0)
-    return {"workload": "traffic", "copy_bytes": 2 * (1 << 30), "decode_bytes": decode_bytes(blobs[0], T, jmax),
-            "launches": launches}
+    return {"workload": "traffic", "copy_bytes": 2 * (1 << 30),
+            "decode_bytes": decode_bytes(blobs[0], T, jmax, router=True), "launches": launches}
 
 
 def cpu_baseline(inputs, T):
@@ -555,8 +575,9 @@ def main():
                      "traffic": traffic},
         "effective_weight_gbs": r["weight_bytes"] / r["linear_s"] / 1e9,
         "linear_us": r["linear_s"] * 1e6,
-        "step_launch": "hip_graph",
+        "step_launch": "hip_graph, one kernel per step (mbq_route_linear)",
         "eager_ms_per_step": r["eager_step_s"] * 1e3,
+        "two_call_ms_per_step": r["two_call_step_s"] * 1e3,
     }
     if not args.no_extra and args.only is None:  # (--only decode prints the headline line alone)
         extra = {}

@@ -237,6 +237,27 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
                       void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
                       hipStream_t stream);
 
+/*
+ * One decode step in one call: MoBiRoute (linear-argmax form) and the routed linear
+ * (English page sections 2.A, 2.B and 3).  Results are those of mbq_route(t, desc->k,
+ * desc->slices, x, x_dtype, wr, logits, budget, perm, offsets) followed by
+ * mbq_linear(desc, packed, t, x, x_dtype, perm, offsets, y, ...), except that the logits
+ * are summed in another order (they may differ from mbq_route's in the last bits; budget,
+ * perm and offsets are exactly the argmax and stable regroup of the logits written here).
+ *   wr, logits, budget, perm, offsets: as in mbq_route; all written.
+ *   y, y_dtype, workspace, ws_bytes: as in mbq_linear (size from mbq_linear_workspace).
+ * With bfloat16 x, 1 <= t <= 16, K within one workgroup of the streaming decode kernel
+ * (at most 16 k tiles of 256 where a wave holds two, 8 where it holds one) and wr 16-byte
+ * aligned, that kernel routes the batch itself: every workgroup multiplies the
+ * activations it already holds by Wr (fixed summation order, so all of them reach the
+ * same budgets) and workgroup 0 writes the routing outputs -- one launch instead of
+ * three.  Otherwise the two calls run in sequence.  Errors as in the two calls.
+ */
+mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                            mbq_dtype x_dtype, const float* wr, float* logits, int32_t* budget,
+                            int32_t* perm, int32_t* offsets, void* y, mbq_dtype y_dtype,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Host only: bytes of device workspace mbq_linear_lowrank needs: u as c float32 partials
  * over chunks of K ([c x t x rank], c <= 8 chosen from t and k; rounded up to 256 bytes)
  * followed by the routed linear's split-K partials under the side path's plan (one

@@ -19,7 +19,7 @@ STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANG
           -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}
 
 EXPORTS = ("mbq_describe", "mbq_pack", "mbq_pack_rows", "mbq_pack_bitplane", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
-           "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_linear_lowrank_workspace",
+           "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_route_linear", "mbq_linear_lowrank_workspace",
            "mbq_linear_lowrank", "mbq_status_str", "mbq_abi_version")
 
 
@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
                                   VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
     lib.mbq_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
     lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, VP]
+    lib.mbq_route_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP,
+                                     ctypes.c_size_t, VP]
     lib.mbq_linear_lowrank_workspace.argtypes = [D, I32, I32, I32, P(ctypes.c_size_t)]
     lib.mbq_linear_lowrank.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, I32, VP, I32, VP,
                                        ctypes.c_size_t, VP]

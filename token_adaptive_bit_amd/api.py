@@ -248,6 +248,34 @@ def linear(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets: torch.
     return y
 
 
+def route_linear(p: PackedLinear, x: torch.Tensor, wr: torch.Tensor, out_dtype: torch.dtype | None = None,
+                 y: torch.Tensor | None = None, logits=None, budget=None, perm=None, offsets=None,
+                 workspace: torch.Tensor | None = None):
+    """One decode step: route (logits x . wr, budgets, stable regroup) and the routed linear.
+    Returns (y, logits, budget, perm, offsets); one launch for bfloat16 x and t <= 16 when
+    K fits one workgroup, else route then linear."""
+    _dev(x, "x")
+    _dev(wr, "wr")
+    t = x.shape[0]
+    s = p.slices
+    dev = x.device
+    out_dtype = out_dtype or x.dtype
+    if y is None:
+        y = torch.empty((t, p.n), dtype=out_dtype, device=dev)
+    logits = torch.empty((t, s), dtype=torch.float32, device=dev) if logits is None else logits
+    budget = torch.empty(t, dtype=torch.int32, device=dev) if budget is None else budget
+    perm = torch.empty(t, dtype=torch.int32, device=dev) if perm is None else perm
+    offsets = torch.empty(s + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    need = linear_workspace(p, t, x.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    check(_lib.LIB.mbq_route_linear(ctypes.byref(p.desc), _p(p.blob), t, _p(x), _dtype(x), _p(wr),
+                                    _p(logits), _p(budget), _p(perm), _p(offsets), _p(y), _dtype(y),
+                                    _p(workspace), ws_bytes, _stream()), "mbq_route_linear")
+    return y, logits, budget, perm, offsets
+
+
 def linear_lowrank_workspace(p: PackedLinear, t: int, rank: int, x_dtype=torch.bfloat16) -> int:
     return _lib.lowrank_workspace_bytes(p.desc, t, MBQ_BF16 if x_dtype == torch.bfloat16 else MBQ_F32,
                                         rank)

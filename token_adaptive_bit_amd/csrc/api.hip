@@ -277,6 +277,30 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
                      workspace, ws_bytes, stream);
 }
 
+mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                            mbq_dtype x_dtype, const float* wr, float* logits, int32_t* budget,
+                            int32_t* perm, int32_t* offsets, void* y, mbq_dtype y_dtype,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
+  if (!offsets) return MBQ_ERR_ARG;
+  if (t > 0 && (!packed || !x || !wr || !logits || !budget || !perm || !y)) return MBQ_ERR_ARG;
+  if (t > 0 && x_dtype == MBQ_BF16 && mbq::decode_route_supported(*desc, t) &&
+      !std::getenv("MBQ_GENERIC_DECODE")) {
+    if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) ||
+        !aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4))
+      return MBQ_ERR_ARG;
+    if (aligned(wr, 16))
+      return launched(mbq::launch_decode_route(*desc, packed, t, x, wr, logits, budget, perm, offsets,
+                                               y, y_dtype == MBQ_BF16, stream));
+  }
+  st = mbq_route(t, desc->k, desc->slices, x, x_dtype, wr, logits, budget, perm, offsets, stream);
+  if (st != MBQ_OK) return st;
+  return mbq_linear(desc, packed, t, x, x_dtype, perm, offsets, y, y_dtype, workspace, ws_bytes, stream);
+}
+
 mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                         int32_t rank, size_t* bytes) {
   mbq_status st = check_desc(desc);

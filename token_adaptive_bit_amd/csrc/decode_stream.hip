@@ -132,20 +132,37 @@ __device__ __forceinline__ void load_codes(Codes<G, S, TPW, LR>& C, const __amdg
 // token block's u (a bf16 hi + lo pair, held for the whole launch) by the row block's B
 // rows (loaded with its codes) in two more MFMAs and adds the product to its part of the
 // output before the waves' parts are summed.
-template <int G, int S, int NA, int TPW, int TB, bool LR>
+// RT routes the batch inside the kernel (MoBiRoute, linear-argmax form, and the regroup:
+// MoBiQuant explainer, gist.science English page, section 2.B) instead of reading perm
+// and offsets: T <= 16 tokens (one token block), K within one workgroup.  Every wave
+// takes the dot products of its own activations (already in registers) with Wr rows
+// staged in LDS; the lanes' and waves' partial sums are added in a fixed order, so every
+// workgroup derives bit-identical logits and budgets, and workgroup 0 writes logits,
+// budget, perm and offsets for the caller.
+struct RouteIO {
+  const float* wr;  // [K x S] row-major
+  float* logits;    // [T x S]
+  int32_t* budget;  // [T]
+  int32_t* perm;    // [T]
+  int32_t* offsets; // [S + 1]
+};
+
+template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT>
 __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, uint64_t ss,
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, void* __restrict__ y, int y_bf16, int kchunk,
     float* __restrict__ part, const float* __restrict__ lr_u, int lr_ks,
-    const uint16_t* __restrict__ lr_b, int lr_r) {
+    const uint16_t* __restrict__ lr_b, int lr_r, RouteIO rio) {
   static_assert(!LR || TB == 1, "the side path is built for one token block per workgroup");
+  static_assert(!RT || (TB == 1 && !LR), "in-kernel routing takes one token block, no side path");
   // Every kernel argument is read in one batch behind one wait: loaded lazily, they come
   // from up to three scalar cache lines in turn, each a round trip before the first
   // activation load can be issued.
   asm volatile("" ::"s"(packed), "s"(x), "s"(perm), "s"(offsets), "s"(y), "s"(part), "s"(lr_u), "s"(lr_b));
   asm volatile("" ::"s"(N), "s"(K), "s"(KB), "s"(NG), "s"(NB), "s"(ss), "s"(po), "s"(T), "s"(y_bf16),
                "s"(kchunk), "s"(lr_ks), "s"(lr_r));
+  if constexpr (RT) asm volatile("" ::"s"(rio.wr), "s"(rio.logits), "s"(rio.budget), "s"(rio.perm), "s"(rio.offsets));
   constexpr int GPT = 256 / G, WPG = G / 64;
   __shared__ f32x4_t red[2][kMaxWaves][TB][64];
   const int NW = blockDim.x >> 6;
@@ -173,8 +190,8 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // Per-token budgets come from perm: lane i of wave 0 takes sorted position i (T <= 64)
   // and later publishes that token's budget in an LDS table.  Both loads are issued
   // first, so waiting for them never waits for the activation loads behind them.
-  const int offv = offsets[min(lane, S)];
-  const int pi = (wave == 0 && lane < T) ? perm[lane] : -1;
+  const int offv = RT ? 0 : offsets[min(lane, S)];
+  const int pi = (!RT && wave == 0 && lane < T) ? perm[lane] : -1;
 
   // The side path's u rows of this token block: lane (r, c) holds ranks 8c .. 8c + 7 of
   // token row r (clamped like the activations; ranks past R read zeros), summed over the
@@ -232,6 +249,18 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       }
   }
 
+  // RT: this wave's tiles of Wr (rows kt * 256 .. + 255: 256 S contiguous floats) as
+  // 16-byte loads, issued right behind the activations; rows past K read zeros
+  u32x4_t wld[RT ? TPW : 1][RT ? S : 1];
+  if constexpr (RT) {
+    const __amdgpu_buffer_rsrc_t rw = slice_rsrc(reinterpret_cast<const uint8_t*>(rio.wr), uint32_t(K) * S * 4);
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+      for (int q = 0; q < S; ++q)
+        wld[tp][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         rw, (uint32_t(kt[tp]) * 256 * S + (64 * q + lane) * 4) * 4, 0, 0));
+  }
   // (the fence keeps every activation load ahead of the wait for offsets)
   __builtin_amdgcn_sched_barrier(0);
   int off[S + 1];
@@ -254,8 +283,17 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // within the wave, so one barrier suffices).  A token that perm does not name keeps
   // budget 0, so its row is written as zero.  The epilogue reads the table back.
   __shared__ __align__(16) int budT[16 * TB];
+  // RT: Wr planes of each wave's tiles and the waves' partial logits
+  __shared__ __align__(16) uint16_t wrp[RT ? kMaxWaves : 1][2][3][4][256];
+  __shared__ float lgp[RT ? kMaxWaves : 1][16][4];
+  int rbud = 0;  // RT: budget of token (lane & 15), 0 past T
   auto route_budgets = [&]() {
-    if (wave == 0) {
+    if constexpr (RT) {
+      // every wave holds the same budgets (derived from the same logits) and writes the
+      // table it reads itself; no other wave's copy can differ, so no barrier is needed
+      if (lane < 16) budT[lane] = rbud;
+      return;
+    } else if (wave == 0) {
       int pv = pi;
       asm volatile("" : "+v"(pv));  // keep the use of perm (and its wait) here
       int b = 1;
@@ -501,12 +539,106 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   load_lr(c0, rb0);
   __builtin_amdgcn_sched_barrier(0);
   setup_a();
+  if constexpr (RT) {
+    // Row blocks 0 and 1 go out with every slice's range (jmax is not known yet); slices
+    // past jmax add nothing there, since no token's budget reaches them.
+    // Wr as three bfloat16 planes (hi + mid + lo = the float32 value: each plane takes the
+    // previous one's exact remainder), column-major per tile: wrp[wave][tile][plane][j][k]
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+      for (int q = 0; q < S; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int f = 4 * (64 * q + lane) + u;  // float f of the tile's 256 S: row f / S, column f % S
+          const float w0 = __uint_as_float(wld[tp][q][u]);
+          const uint32_t p0 = bf16_bits_rne(w0);
+          const float w1 = w0 - bf16_bits_to_float(p0);
+          const uint32_t p1 = bf16_bits_rne(w1);
+          const uint32_t p2 = bf16_bits_rne(w1 - bf16_bits_to_float(p1));
+          wrp[wave][tp][0][f % S][f / S] = uint16_t(p0);
+          wrp[wave][tp][1][f % S][f / S] = uint16_t(p1);
+          wrp[wave][tp][2][f % S][f / S] = uint16_t(p2);
+        }
+    // logits^T = Wr^T x^T on the matrix cores: the activation registers (lane (r, c): token r,
+    // 8 inputs per 32-input step) are the B operand as they stand; lane (j, c) of the A
+    // operand holds column j of Wr over the same inputs (rows j >= S zero), so lane (n, 0)
+    // ends with token n's S logits.  Inputs past K or in a tile this wave does not have
+    // get zero Wr.
+    f32x4_t L{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kl = 64 * i + 16 * c + 8 * h;  // first input of the lane's 8 within the tile
+          const bool use = r < S && live[tp] && kt[tp] * 256 + kl < K;
+#pragma unroll
+          for (int pl = 0; pl < 3; ++pl) {
+            u32x4_t a{0u, 0u, 0u, 0u};
+            if (use) a = *reinterpret_cast<const u32x4_t*>(&wrp[wave][tp][pl][r & 3][kl]);
+            L = mfma(a, Araw[0][tp][i][h][0], L);
+          }
+        }
+    mfma_result_fence();
+    if (c == 0) {
+#pragma unroll
+      for (int j = 0; j < S; ++j) lgp[wave][r][j] = L[j];
+    }
+  }
   if constexpr (kThreeBuffers) {
     __builtin_amdgcn_sched_barrier(0);
     load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_par);
     load_lr(c1, nbl(1));
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (RT) {
+    __syncthreads();
+    // every lane: token (lane & 15), the waves' partials in wave order
+    float lg[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) lg[j] = 0.f;
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int j = 0; j < S; ++j) lg[j] += lgp[w][r][j];
+    // b = 1 + the first index of the largest logit
+    int bb = 1;
+    float best = lg[0];
+#pragma unroll
+    for (int j = 1; j < S; ++j)
+      if (lg[j] > best) {
+        best = lg[j];
+        bb = j + 1;
+      }
+    rbud = r < T ? bb : 0;
+    jmax = 1;
+#pragma unroll
+    for (int v = 2; v <= S; ++v)
+      if (__ballot(lane < T && rbud >= v) != 0ull) jmax = v;
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      if (j >= jmax) rs[j] = slice_rsrc(packed + uint64_t(j) * ss, 0u);
+    if (blockIdx.x == 0 && blockIdx.z == 0 && wave == 0) {
+      // the regroup: stable ascending order by budget, ranks from ballots
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      int base = 0, pos = 0;
+      if (lane == 0) rio.offsets[0] = 0;
+#pragma unroll
+      for (int v = 1; v <= S; ++v) {
+        const uint64_t m = __ballot(lane < T && rbud == v);
+        if (lane < T && rbud == v) pos = base + __popcll(m & below);
+        base += __popcll(m);
+        if (lane == 0) rio.offsets[v] = base;
+      }
+      if (lane < T) {
+        rio.perm[pos] = lane;
+        rio.budget[lane] = rbud;
+#pragma unroll
+        for (int j = 0; j < S; ++j) rio.logits[lane * S + j] = lg[j];
+      }
+    }
+  }
   route_budgets();
   auto stream = [&](auto jm) __attribute__((always_inline)) {
     int buf = 0;
@@ -617,10 +749,11 @@ struct LrArgs {
   int r;
 };
 
-template <int G, int S, int NA, int TPW, int TB, bool LR>
+template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT = false>
 hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                       const void* x, const int32_t* perm, const int32_t* offsets, void* y,
-                      bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream) {
+                      bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream,
+                      const RouteIO& rio = RouteIO{}) {
   // One workgroup per CU.  The token-block groups and k chunks of a launch share the CUs,
   // so they all run at once: with gridDim.x a multiple of 8, workgroups (x, y, z) of every
   // y and z sit on XCD x % 8, and the token groups of one k chunk walk the same row blocks
@@ -628,10 +761,10 @@ hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int
   // token groups by that XCD's L2.
   const int ty = (t + 16 * TB - 1) / (16 * TB);
   const int grid = std::min(d.row_blocks, std::max(8, (cu_count() / (ty * pl.ks)) & ~7));
-  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
+  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR, RT>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
                      0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
                      d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
-                     offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.ks, lr.b, lr.r);
+                     offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.ks, lr.b, lr.r, rio);
   return hipGetLastError();
 }
 
@@ -659,6 +792,33 @@ hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int3
   return launch_gsn<G, S, NA, 1, 1, false>(d, pl, packed, t, x, perm, offsets, y, y_bf16, part, lr, stream);
 }
 
+
+// In-kernel routing: bfloat16 activations, one token block, no side path, one k chunk.
+template <int G, int S>
+hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
+                           const void* x, void* y, bool y_bf16, const RouteIO& rio, hipStream_t stream) {
+  if constexpr (stream_fits(G, S, 1)) {
+    if constexpr (two_tiles_fit(G, S, 1)) {
+      if (pl.tpw == 2)
+        return launch_gsn<G, S, 1, 2, 1, false, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
+                                                      nullptr, LrArgs{}, stream, rio);
+    }
+    return launch_gsn<G, S, 1, 1, 1, false, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
+                                                  nullptr, LrArgs{}, stream, rio);
+  }
+  return hipErrorInvalidValue;  // excluded by decode_route_supported
+}
+
+template <int G>
+hipError_t launch_route_g(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
+                          const void* x, void* y, bool y_bf16, const RouteIO& rio, hipStream_t stream) {
+  switch (d.slices) {
+    case 1: return launch_route_gs<G, 1>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+    case 2: return launch_route_gs<G, 2>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+    case 3: return launch_route_gs<G, 3>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+    default: return launch_route_gs<G, 4>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+  }
+}
 
 template <int G, int NA>
 hipError_t launch_gn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
@@ -690,6 +850,24 @@ bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16, bool lr)
   const int na = x_bf16 ? 1 : 2;
   return t >= 1 && t <= kMaxTokens && d.slice_stride < (uint64_t(1) << 32) &&
          (lr ? lr_fits(d.group, d.slices, na) : stream_fits(d.group, d.slices, na));
+}
+
+bool decode_route_supported(const mbq_desc& d, int32_t t) {
+  if (t < 1 || t > 16 || !decode_stream_supported(d, t, true, false)) return false;
+  const Plan pl = make_plan(d, t, true, false);
+  return pl.ks == 1 && pl.tb == 1;
+}
+
+hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
+                               const float* wr, float* logits, int32_t* budget, int32_t* perm,
+                               int32_t* offsets, void* y, bool y_bf16, hipStream_t stream) {
+  const RouteIO rio{wr, logits, budget, perm, offsets};
+  const Plan pl = make_plan(d, t, true, false);
+  switch (d.group) {
+    case 64: return launch_route_g<64>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+    case 128: return launch_route_g<128>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+    default: return launch_route_g<256>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+  }
 }
 
 size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool lr) {

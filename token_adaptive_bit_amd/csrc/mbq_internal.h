@@ -55,6 +55,12 @@ hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const
                          bool y_bf16, void* ws, hipStream_t stream);
 bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16, bool lr = false);
 size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool lr);
+// Decode with the routing in the kernel (bfloat16 x, 1 <= t <= 16, K within one
+// workgroup): writes logits, budget, perm and offsets as launch_route does, and y.
+bool decode_route_supported(const mbq_desc& d, int32_t t);
+hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
+                               const float* wr, float* logits, int32_t* budget, int32_t* perm,
+                               int32_t* offsets, void* y, bool y_bf16, hipStream_t stream);
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
                                 void* y, bool y_bf16, void* ws, const float* lr_u, int32_t lr_ks,
