@@ -77,6 +77,14 @@ __device__ __forceinline__ void mfma_result_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Two floats rounded to nearest even into one register of two bfloat16 (a low, b high):
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 __device__ __forceinline__ u32x4_t ldg16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
@@ -535,13 +543,15 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // (scheduling fences keep the issue order perm, x, row block 0, row block 1, so each
   // wait below covers exactly the loads it needs)
   __builtin_amdgcn_sched_barrier(0);
-  load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_par);
-  load_lr(c0, rb0);
+  if constexpr (!RT) {
+    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    load_lr(c0, rb0);
+  }
   __builtin_amdgcn_sched_barrier(0);
   setup_a();
   if constexpr (RT) {
-    // Row blocks 0 and 1 go out with every slice's range (jmax is not known yet); slices
-    // past jmax add nothing there, since no token's budget reaches them.
+    // Row blocks 0 and 1 go out after this, before the budgets are known, with every
+    // slice's range; slices past jmax add nothing there, since no budget reaches them.
     // Wr as three bfloat16 planes (hi + mid + lo = the float32 value: each plane takes the
     // previous one's exact remainder), column-major per tile: wrp[wave][tile][plane][j][k]
 #pragma unroll
@@ -549,23 +559,29 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
 #pragma unroll
       for (int q = 0; q < S; ++q)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int f = 4 * (64 * q + lane) + u;  // float f of the tile's 256 S: row f / S, column f % S
-          const float w0 = __uint_as_float(wld[tp][q][u]);
-          const uint32_t p0 = bf16_bits_rne(w0);
-          const float w1 = w0 - bf16_bits_to_float(p0);
-          const uint32_t p1 = bf16_bits_rne(w1);
-          const uint32_t p2 = bf16_bits_rne(w1 - bf16_bits_to_float(p1));
+        for (int u = 0; u < 4; u += 2) {
+          // floats f, f + 1 of the tile's 256 S (row f / S, column f % S), a pair at a time
+          const int f = 4 * (64 * q + lane) + u;
+          const float a0 = __uint_as_float(wld[tp][q][u]), b0 = __uint_as_float(wld[tp][q][u + 1]);
+          const uint32_t p0 = pk_bf16(a0, b0);
+          const float a1 = a0 - __uint_as_float(p0 << 16), b1 = b0 - __uint_as_float(p0 & 0xFFFF0000u);
+          const uint32_t p1 = pk_bf16(a1, b1);
+          const uint32_t p2 = pk_bf16(a1 - __uint_as_float(p1 << 16), b1 - __uint_as_float(p1 & 0xFFFF0000u));
           wrp[wave][tp][0][f % S][f / S] = uint16_t(p0);
           wrp[wave][tp][1][f % S][f / S] = uint16_t(p1);
           wrp[wave][tp][2][f % S][f / S] = uint16_t(p2);
+          wrp[wave][tp][0][(f + 1) % S][(f + 1) / S] = uint16_t(p0 >> 16);
+          wrp[wave][tp][1][(f + 1) % S][(f + 1) / S] = uint16_t(p1 >> 16);
+          wrp[wave][tp][2][(f + 1) % S][(f + 1) / S] = uint16_t(p2 >> 16);
         }
     // logits^T = Wr^T x^T on the matrix cores: the activation registers (lane (r, c): token r,
-    // 8 inputs per 32-input step) are the B operand as they stand; lane (j, c) of the A
-    // operand holds column j of Wr over the same inputs (rows j >= S zero), so lane (n, 0)
-    // ends with token n's S logits.  Inputs past K or in a tile this wave does not have
-    // get zero Wr.
-    f32x4_t L{0.f, 0.f, 0.f, 0.f};
+    // 8 inputs per 32-input step) are the B operand as they stand -- setup has already
+    // zeroed those of inputs past K and of tiles this wave does not have -- and lane (j, c)
+    // of the A operand holds column j of Wr over the same inputs (rows past S repeat a real
+    // column; their products land in rows of D nobody reads), so lane (n, 0) ends with
+    // token n's S logits.  One accumulator per plane, added lo + mid + hi at the end.
+    const int jr = min(r & 3, S - 1);
+    f32x4_t Lp[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
@@ -573,19 +589,22 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int kl = 64 * i + 16 * c + 8 * h;  // first input of the lane's 8 within the tile
-          const bool use = r < S && live[tp] && kt[tp] * 256 + kl < K;
 #pragma unroll
-          for (int pl = 0; pl < 3; ++pl) {
-            u32x4_t a{0u, 0u, 0u, 0u};
-            if (use) a = *reinterpret_cast<const u32x4_t*>(&wrp[wave][tp][pl][r & 3][kl]);
-            L = mfma(a, Araw[0][tp][i][h][0], L);
-          }
+          for (int pl = 0; pl < 3; ++pl)
+            Lp[pl] = mfma(*reinterpret_cast<const u32x4_t*>(&wrp[wave][tp][pl][jr][kl]), Araw[0][tp][i][h][0], Lp[pl]);
         }
     mfma_result_fence();
+    const f32x4_t L = (Lp[2] + Lp[1]) + Lp[0];
     if (c == 0) {
 #pragma unroll
       for (int j = 0; j < S; ++j) lgp[wave][r][j] = L[j];
     }
+  }
+  if constexpr (RT) {
+    // (row block 0 goes out here with routing: until now the activation and Wr loads of
+    // every wave had the CU's memory queue to themselves)
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_par);
   }
   if constexpr (kThreeBuffers) {
     __builtin_amdgcn_sched_barrier(0);
