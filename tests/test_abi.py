@@ -171,6 +171,34 @@ def test_route_and_regroup_validation():
     assert L.mbq_regroup(-2, 3, f, f, f, None) == SHAPE
 
 
+def test_route_linear_validation():
+    """Errors of the one-call decode step, all caught before any launch (the shape here,
+    16 bf16 tokens on a 200 x 640 weight, takes the one-launch path, which checks
+    alignment itself)."""
+    st, d = desc(200, 640, 128, 3)
+    dp, f = ctypes.byref(d), P(FAKE)
+
+    def call(**kw):
+        a = dict(desc=dp, packed=f, t=16, x=f, xd=BF16, wr=f, lg=f, b=f, perm=f, off=f, y=f, yd=BF16)
+        a.update(kw)
+        return L.mbq_route_linear(a["desc"], a["packed"], a["t"], a["x"], a["xd"], a["wr"], a["lg"], a["b"],
+                                  a["perm"], a["off"], a["y"], a["yd"], None, 0, None)
+
+    assert call(desc=None) == ARG
+    assert call(t=-1) == SHAPE and call(t=1 << 25) == SHAPE
+    assert call(xd=7) == ARG and call(yd=7) == ARG
+    assert call(off=None) == ARG
+    for k in ("packed", "x", "wr", "lg", "b", "perm", "y"):
+        assert call(**{k: None}) == ARG, k
+    assert call(packed=P(FAKE + 64)) == ARG
+    assert call(x=P(FAKE + 8)) == ARG
+    assert call(y=P(FAKE + 8)) == ARG
+    assert call(perm=P(FAKE + 2)) == ARG and call(lg=P(FAKE + 2)) == ARG
+    bad = lib_mod.MbqDesc.from_buffer_copy(d)
+    bad.groups_padded += 1
+    assert call(desc=ctypes.byref(bad)) == SHAPE
+
+
 def mlp_ws(t, k, h):
     n = ctypes.c_size_t(123)
     st = L.mbq_route_mlp_workspace(t, k, h, ctypes.byref(n))
