@@ -21,6 +21,7 @@
 //   * the waves' partial 16x16 tiles are summed in LDS (double-buffered, one barrier per
 //     row block) and written out with per-token slice masks already applied.
 // Token perm[i] (sorted position i) has budget b with offsets[b-1] <= i < offsets[b].
+#include <cstdlib>
 #include <type_traits>
 
 #include "mbq_internal.h"
@@ -77,10 +78,105 @@ __device__ __forceinline__ void mfma_result_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Two floats rounded to nearest even into one register of two bfloat16 (a low, b high):
-// one v_cvt_pk_bf16_f32 on gfx950.
+// ---- F4: bfloat16 activations on the scaled fp8 x fp4 matrix instruction
+// (v_mfma_scale_f32_16x16x128_f8f6f4), which takes the codes almost as stored.
+//
+// A 2-bit code q in the low two bits of a nibble whose upper bits are zero is the e2m1
+// (fp4) number q / 2 exactly (0 and 0.5 subnormal, 1 and 1.5 normal), so a code word
+// masked with 0x33333333 is eight fp4 values (its codes at bit positions 0, 4, ..., 28:
+// inputs 0, 4, 8, 12, 1, 5, 9, 13 of the word's 16) and the word shifted right by two is
+// the other eight (inputs 2, 6, 10, 14, 3, 7, 11, 15): three instructions per word where
+// bf16 operands take ten.
+//
+// Operand layouts of the instruction (16 x 16 x 128, measured on gfx950): byte q of lane
+// (r, c)'s A operand (8 registers of e4m3) is row r, logical input 16c + (q mod 16) +
+// 64 (q div 16); nibble p of lane (n, c)'s B operand (4 registers of e2m1) is column n,
+// logical input 32c + p; the e8m0 scale of row r (column n) and logical inputs 32b ..
+// 32b + 31 comes from lane r + 16b (n + 16b).  B of lane (n, c) is its code words 2m and
+// 2m + 1 of the tile (inputs 128m + 64 i' + 16c + e, i' = 0, 1), masked even and odd, which
+// makes logical input 32c + 8j + t the physical input 128m + 64 (j >> 1) + 16c +
+// E_(j & 1)(t), E_0 = (0 4 8 12 1 5 9 13), E_1 = (2 6 10 14 3 7 11 15).  The A operand is
+// loaded to match: lane (r, c) holds token r's inputs 128m + 64 (c & 1) + 16 (c >> 1) +
+// [0, 16) and the same + 32, bytes in the order E_0, E_1 within each run.
+//
+// The activations of a 128-input block are split exactly into two e4m3 numbers with one
+// power-of-two scale per token row: sc = 2^(e8 - 127) puts the row's largest |x| of the
+// 128 in [128, 256) sc, hi = e4m3(x / sc) and lo = e4m3((x - hi sc) / sc), both rounded to
+// nearest even (the scaled converters of gfx950); hi + lo = x / sc exactly for every
+// |x / sc| >= 1/4 (2^-10 of the block's largest), smaller inputs keep an absolute error
+// below 2^-10 sc.  The instruction's own sum of the 128 products is not exact: measured,
+// its error is about 1e-5 of the sum of |products|.
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+struct AF4 {
+  i32x8_t hi, lo;
+  uint32_t sc;  // e8m0 scale of the lane's row (every lane of a row holds the same)
+};
+
+__device__ __forceinline__ uint32_t f4_even(uint32_t w) { return w & 0x33333333u; }
+__device__ __forceinline__ uint32_t f4_odd(uint32_t w) { return (w >> 2) & 0x33333333u; }
+
+// B's scale is 2 (e8m0 128) for code products, so they come out as sum x q, and 1 (127)
+// for the group sums, whose B operand is every nibble 1.0
+template <int BSCALE>
+__device__ __forceinline__ f32x4_t mfma_f4(const i32x8_t& a, const uint32_t (&bw)[4], uint32_t scale, f32x4_t c) {
+  const i32x8_t b{int(bw[0]), int(bw[1]), int(bw[2]), int(bw[3]), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, int(scale), 0, BSCALE);
+}
+
+// One byte pair (q, q + 1) of the hi and lo registers: x0, x1 in float32 (word half sel).
+template <bool SEL>
+__device__ __forceinline__ void split_pair(float x0, float x1, float sc, int& hw, int& lw) {
+  i16x2_t h = __builtin_bit_cast(i16x2_t, hw), l = __builtin_bit_cast(i16x2_t, lw);
+  h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x0, x1, sc, SEL);
+  const f32x2_t hb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(__builtin_bit_cast(int, h), sc, SEL);
+  l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, x0 - hb[0], x1 - hb[1], sc, SEL);
+  hw = __builtin_bit_cast(int, h);
+  lw = __builtin_bit_cast(int, l);
+}
+
+// run[0], run[1]: inputs base + [0, 16) of the lane's token (8 bf16 each); run[2], run[3]:
+// base + 32 + [0, 16).  Every lane of the wave takes part (the row maximum crosses lanes).
+__device__ __forceinline__ AF4 prep_a_f4(const u32x4_t& r0, const u32x4_t& r1, const u32x4_t& r2,
+                                         const u32x4_t& r3) {
+  const u32x4_t run[4] = {r0, r1, r2, r3};
+  float v[32];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      v[8 * h + 2 * d] = __uint_as_float(run[h][d] << 16);
+      v[8 * h + 2 * d + 1] = __uint_as_float(run[h][d] & 0xFFFF0000u);
+    }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  // e8 >= 1 keeps the scale a normal float (rows below 2^-119 lose their small bits)
+  const int e8 = max(int(__float_as_uint(m) >> 23) - 7, 1);
+  const float sc = __uint_as_float(uint32_t(e8) << 23);
+  constexpr int kE[16] = {0, 4, 8, 12, 1, 5, 9, 13, 2, 6, 10, 14, 3, 7, 11, 15};
+  AF4 a;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = 4 * j;  // bytes q .. q + 3: run q >> 4, elements kE[(q & 15) ..]
+    const float* vr = &v[16 * (q >> 4)];
+    int hw = 0, lw = 0;
+    split_pair<false>(vr[kE[q & 15]], vr[kE[(q & 15) + 1]], sc, hw, lw);
+    split_pair<true>(vr[kE[(q & 15) + 2]], vr[kE[(q & 15) + 3]], sc, hw, lw);
+    a.hi[j] = hw;
+    a.lo[j] = lw;
+  }
+  a.sc = uint32_t(e8);
+  return a;
+}
+
+// Two floats rounded to nearest even into one register of two bfloat16 (a low, b high):
+// one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
@@ -155,7 +251,7 @@ struct RouteIO {
   int32_t* offsets; // [S + 1]
 };
 
-template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT>
+template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT, bool F4>
 __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, uint64_t ss,
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
@@ -164,6 +260,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint16_t* __restrict__ lr_b, int lr_r, RouteIO rio) {
   static_assert(!LR || TB == 1, "the side path is built for one token block per workgroup");
   static_assert(!RT || (TB == 1 && !LR), "in-kernel routing takes one token block, no side path");
+  static_assert(!F4 || (NA == 1 && TB == 1 && !LR), "fp4 operands: bfloat16 activations, one token block");
   // Every kernel argument is read in one batch behind one wait: loaded lazily, they come
   // from up to three scalar cache lines in turn, each a round trip before the first
   // activation load can be issued.
@@ -235,6 +332,11 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // blocks starting at token tb0 = 16 TB blockIdx.y; in block b, MFMA row r is token
   // tb0 + 16 b + r (rows past T repeat a real token and are never stored).
   const int tb0 = 16 * TB * blockIdx.y, Tw = min(16 * TB, T - tb0);
+  // first input of activation load (i, h) of tile tp within the tile: bf16 operands take
+  // inputs 64i + 16c + 8h; fp8 ones (F4) the runs of 128-input block i >> 1 (see above)
+  auto xk = [&](int i, int h) {
+    return F4 ? 128 * (i >> 1) + 64 * (c & 1) + 16 * (c >> 1) + 32 * (i & 1) + 8 * h : 64 * i + 16 * c + 8 * h;
+  };
   u32x4_t Araw[TB][TPW][4][2][NA];
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
@@ -243,14 +345,14 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int k = kt[tp] * 256 + 64 * i + 16 * c;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int q = 0; q < NA; ++q) {
             // K is a multiple of 64, so these 8 inputs are all real or all padding; padding
             // reads the row's first inputs instead (zeroed with the seeds)
-            const int kk = k + 8 * h < K ? k + 8 * h : 0;
+            const int k = kt[tp] * 256 + xk(i, h);
+            const int kk = k < K ? k : 0;
             const uint8_t* p = static_cast<const uint8_t*>(x) + (size_t(xr) * K + kk) * (2 * NA) + 16 * q;
             Araw[b][tp][i][h][q] = ldg16(p);
           }
@@ -331,22 +433,60 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // The A operands live in the load registers: bf16 activations as loaded, float32 ones
   // (8 values in two registers) split once, in place, into bf16 high and low parts.
   auto aop = [&](int b, int tp, int i, int h, int pa) -> const u32x4_t& { return Araw[b][tp][i][h][pa]; };
-  auto setup_a = [&]() {
+  // inputs past K and tiles this wave does not have get zero activations, so their
+  // products and sums are exactly zero whatever the redirected loads hold
+  auto setup_zero = [&]() {
 #pragma unroll
-    for (int b = 0; b < TB; ++b) {
-      // inputs past K and tiles this wave does not have get zero activations, so their
-      // products and sums are exactly zero whatever the redirected loads hold
+    for (int b = 0; b < TB; ++b)
 #pragma unroll
       for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const bool real = live[tp] && kt[tp] * 256 + 64 * i + 16 * c + 8 * h < K;
+            const bool real = live[tp] && kt[tp] * 256 + xk(i, h) < K;
 #pragma unroll
             for (int q = 0; q < NA; ++q)
               if (!real) Araw[b][tp][i][h][q] = u32x4_t{0u, 0u, 0u, 0u};
           }
+  };
+  AF4 af[F4 ? TPW : 1][2];
+  auto setup_a = [&]() {
+    if constexpr (F4) {
+      // fp8 pairs and scales of the wave's 128-input blocks, then the group sums X on the
+      // same instruction with every code 2 (fp4 1.0, B scale 1): X = sum x
+      constexpr uint32_t kOne4 = 0x22222222u;
+#pragma unroll
+      for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          af[tp][m] = prep_a_f4(Araw[0][tp][2 * m][0][0], Araw[0][tp][2 * m][1][0],
+                                Araw[0][tp][2 * m + 1][0][0], Araw[0][tp][2 * m + 1][1][0]);
+#pragma unroll
+      for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+        for (int gi = 0; gi < GPT; ++gi) {
+          f32x4_t xs4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            // group gi's inputs within block m: all of it (128, 256) or one half (64)
+            if (G == 64 && m != (gi >> 1)) continue;
+            if (G == 128 && m != gi) continue;
+            const uint32_t lo = (G == 64 && (gi & 1)) ? 0u : kOne4, hi = (G == 64 && !(gi & 1)) ? 0u : kOne4;
+            const uint32_t ones[4] = {lo, lo, hi, hi};
+            xs4 = mfma_f4<127>(af[tp][m].hi, ones, af[tp][m].sc, xs4);
+            xs4 = mfma_f4<127>(af[tp][m].lo, ones, af[tp][m].sc, xs4);
+          }
+          mfma_result_fence();
+          if (r == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) xsT[wave][0][tp * GPT + gi][4 * c + v] = xs4[v];
+          }
+        }
+      return;
+    }
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
 #pragma unroll
       for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
@@ -450,9 +590,41 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
-        for (int j = 0; j < JM; ++j) P[b][j] = gnb[b][tp][gi];
+        for (int j = 0; j < JM; ++j) P[b][j] = F4 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : gnb[b][tp][gi];
+      if constexpr (F4) {
+        // group gi: 128-input blocks gi (G 128), 0 and 1 (G 256), or one half of block
+        // gi >> 1 (G 64: the other half's nibbles zero); every slice's high parts, then
+        // every slice's low parts, so the chains interleave
 #pragma unroll
-      for (int ii = 0; ii < WPG; ++ii) {
+        for (int m = 0; m < 2; ++m) {
+          if (G == 64 && m != (gi >> 1)) continue;
+          if (G == 128 && m != gi) continue;
+          uint32_t bw[JM][4];
+#pragma unroll
+          for (int j = 0; j < JM; ++j) {
+            if constexpr (G == 64) {
+              const uint32_t w = C.cw[tp][j][gi];
+              const bool up = gi & 1;
+              bw[j][0] = up ? 0u : f4_even(w);
+              bw[j][1] = up ? 0u : f4_odd(w);
+              bw[j][2] = up ? f4_even(w) : 0u;
+              bw[j][3] = up ? f4_odd(w) : 0u;
+            } else {
+              const uint32_t w0 = C.cw[tp][j][2 * m], w1 = C.cw[tp][j][2 * m + 1];
+              bw[j][0] = f4_even(w0);
+              bw[j][1] = f4_odd(w0);
+              bw[j][2] = f4_even(w1);
+              bw[j][3] = f4_odd(w1);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < JM; ++j) P[0][j] = mfma_f4<128>(af[tp][m].hi, bw[j], af[tp][m].sc, P[0][j]);
+#pragma unroll
+          for (int j = 0; j < JM; ++j) P[0][j] = mfma_f4<128>(af[tp][m].lo, bw[j], af[tp][m].sc, P[0][j]);
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < (F4 ? 0 : WPG); ++ii) {
         const int i = gi * WPG + ii;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -548,7 +720,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     load_lr(c0, rb0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  setup_a();
+  setup_zero();
   if constexpr (RT) {
     // Row blocks 0 and 1 go out after this, before the budgets are known, with every
     // slice's range; slices past jmax add nothing there, since no budget reaches them.
@@ -588,7 +760,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int kl = 64 * i + 16 * c + 8 * h;  // first input of the lane's 8 within the tile
+          const int kl = xk(i, h);  // first input of the lane's 8 within the tile
 #pragma unroll
           for (int pl = 0; pl < 3; ++pl)
             Lp[pl] = mfma(*reinterpret_cast<const u32x4_t*>(&wrp[wave][tp][pl][jr][kl]), Araw[0][tp][i][h][0], Lp[pl]);
@@ -600,6 +772,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       for (int j = 0; j < S; ++j) lgp[wave][r][j] = L[j];
     }
   }
+  setup_a();
   if constexpr (RT) {
     // (row block 0 goes out here with routing: until now the activation and Wr loads of
     // every wave had the CU's memory queue to themselves)
@@ -768,7 +941,7 @@ struct LrArgs {
   int r;
 };
 
-template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT = false>
+template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT = false, bool F4 = false>
 hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                       const void* x, const int32_t* perm, const int32_t* offsets, void* y,
                       bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream,
@@ -780,7 +953,7 @@ hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int
   // token groups by that XCD's L2.
   const int ty = (t + 16 * TB - 1) / (16 * TB);
   const int grid = std::min(d.row_blocks, std::max(8, (cu_count() / (ty * pl.ks)) & ~7));
-  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR, RT>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
+  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR, RT, F4>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
                      0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
                      d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
                      offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.ks, lr.b, lr.r, rio);
@@ -813,15 +986,24 @@ hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int3
 
 
 // In-kernel routing: bfloat16 activations, one token block, no side path, one k chunk.
+// f4 selects the fp8 x fp4 multiply (see above).
 template <int G, int S>
 hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
-                           const void* x, void* y, bool y_bf16, const RouteIO& rio, hipStream_t stream) {
+                           const void* x, void* y, bool y_bf16, const RouteIO& rio, bool f4,
+                           hipStream_t stream) {
   if constexpr (stream_fits(G, S, 1)) {
     if constexpr (two_tiles_fit(G, S, 1)) {
-      if (pl.tpw == 2)
+      if (pl.tpw == 2) {
+        if (f4)
+          return launch_gsn<G, S, 1, 2, 1, false, true, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
+                                                              nullptr, LrArgs{}, stream, rio);
         return launch_gsn<G, S, 1, 2, 1, false, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
                                                       nullptr, LrArgs{}, stream, rio);
+      }
     }
+    if (f4)
+      return launch_gsn<G, S, 1, 1, 1, false, true, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
+                                                          nullptr, LrArgs{}, stream, rio);
     return launch_gsn<G, S, 1, 1, 1, false, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
                                                   nullptr, LrArgs{}, stream, rio);
   }
@@ -830,12 +1012,13 @@ hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed
 
 template <int G>
 hipError_t launch_route_g(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
-                          const void* x, void* y, bool y_bf16, const RouteIO& rio, hipStream_t stream) {
+                          const void* x, void* y, bool y_bf16, const RouteIO& rio, bool f4,
+                          hipStream_t stream) {
   switch (d.slices) {
-    case 1: return launch_route_gs<G, 1>(d, pl, packed, t, x, y, y_bf16, rio, stream);
-    case 2: return launch_route_gs<G, 2>(d, pl, packed, t, x, y, y_bf16, rio, stream);
-    case 3: return launch_route_gs<G, 3>(d, pl, packed, t, x, y, y_bf16, rio, stream);
-    default: return launch_route_gs<G, 4>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+    case 1: return launch_route_gs<G, 1>(d, pl, packed, t, x, y, y_bf16, rio, false, stream);
+    case 2: return launch_route_gs<G, 2>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
+    case 3: return launch_route_gs<G, 3>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
+    default: return launch_route_gs<G, 4>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
   }
 }
 
@@ -882,10 +1065,16 @@ hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t,
                                int32_t* offsets, void* y, bool y_bf16, hipStream_t stream) {
   const RouteIO rio{wr, logits, budget, perm, offsets};
   const Plan pl = make_plan(d, t, true, false);
+  // The fp8 x fp4 multiply saves ~1/4 of a row block's time but its activation split
+  // costs every workgroup about two row blocks' worth up front: taken from 4 row blocks
+  // per workgroup and 2 slices on (MBQ_DECODE_F4=1 / =0 forces it on / off).
+  const int grid = std::min(d.row_blocks, std::max(8, cu_count() & ~7));
+  bool f4 = d.slices >= 2 && (d.row_blocks + grid - 1) / grid >= 4;
+  if (const char* e = std::getenv("MBQ_DECODE_F4")) f4 = e[0] == '1';
   switch (d.group) {
-    case 64: return launch_route_g<64>(d, pl, packed, t, x, y, y_bf16, rio, stream);
-    case 128: return launch_route_g<128>(d, pl, packed, t, x, y, y_bf16, rio, stream);
-    default: return launch_route_g<256>(d, pl, packed, t, x, y, y_bf16, rio, stream);
+    case 64: return launch_route_g<64>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
+    case 128: return launch_route_g<128>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
+    default: return launch_route_g<256>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
   }
 }
 
