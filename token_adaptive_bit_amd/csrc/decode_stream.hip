@@ -360,7 +360,8 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   }
 
   // RT: this wave's tiles of Wr (rows kt * 256 .. + 255: 256 S contiguous floats) as
-  // 16-byte loads, issued right behind the activations; rows past K read zeros
+  // 16-byte loads, issued right behind the activations (ahead of them, they delay the
+  // activations everything else waits for); rows past K read zeros
   u32x4_t wld[RT ? TPW : 1][RT ? S : 1];
   if constexpr (RT) {
     const __amdgpu_buffer_rsrc_t rw = slice_rsrc(reinterpret_cast<const uint8_t*>(rio.wr), uint32_t(K) * S * 4);
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // budget 0, so its row is written as zero.  The epilogue reads the table back.
   __shared__ __align__(16) int budT[16 * TB];
   // RT: Wr planes of each wave's tiles and the waves' partial logits
-  __shared__ __align__(16) uint16_t wrp[RT ? kMaxWaves : 1][2][3][4][256];
+  __shared__ __align__(16) uint16_t wrp[RT ? kMaxWaves : 1][2][3][4][256 + 8];  // rows padded: banks
   __shared__ float lgp[RT ? kMaxWaves : 1][16][4];
   int rbud = 0;  // RT: budget of token (lane & 15), 0 past T
   auto route_budgets = [&]() {
