@@ -338,39 +338,42 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     return F4 ? 128 * (i >> 1) + 64 * (c & 1) + 16 * (c >> 1) + 32 * (i & 1) + 8 * h : 64 * i + 16 * c + 8 * h;
   };
   u32x4_t Araw[TB][TPW][4][2][NA];
-#pragma unroll
-  for (int b = 0; b < TB; ++b) {
+  auto load_x = [&](int b, int tp) __attribute__((always_inline)) {
     const int xr = tb0 + min(16 * b + r, Tw - 1);
 #pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int q = 0; q < NA; ++q) {
-            // K is a multiple of 64, so these 8 inputs are all real or all padding; padding
-            // reads the row's first inputs instead (zeroed with the seeds)
-            const int k = kt[tp] * 256 + xk(i, h);
-            const int kk = k < K ? k : 0;
-            const uint8_t* p = static_cast<const uint8_t*>(x) + (size_t(xr) * K + kk) * (2 * NA) + 16 * q;
-            Araw[b][tp][i][h][q] = ldg16(p);
-          }
-      }
-  }
-
-  // RT: this wave's tiles of Wr (rows kt * 256 .. + 255: 256 S contiguous floats) as
-  // 16-byte loads, issued right behind the activations (ahead of them, they delay the
-  // activations everything else waits for); rows past K read zeros
+        for (int q = 0; q < NA; ++q) {
+          // K is a multiple of 64, so these 8 inputs are all real or all padding; padding
+          // reads the row's first inputs instead (zeroed with the seeds)
+          const int k = kt[tp] * 256 + xk(i, h);
+          const int kk = k < K ? k : 0;
+          const uint8_t* p = static_cast<const uint8_t*>(x) + (size_t(xr) * K + kk) * (2 * NA) + 16 * q;
+          Araw[b][tp][i][h][q] = ldg16(p);
+        }
+  };
+  // RT: each tile's Wr rows (kt * 256 .. + 255: 256 S contiguous floats) as 16-byte loads
+  // right behind that tile's activations, so the first tile can be routed while the
+  // second one's loads are still arriving (Wr ahead of the activations delays what
+  // everything else waits for); rows past K read zeros
   u32x4_t wld[RT ? TPW : 1][RT ? S : 1];
   if constexpr (RT) {
     const __amdgpu_buffer_rsrc_t rw = slice_rsrc(reinterpret_cast<const uint8_t*>(rio.wr), uint32_t(K) * S * 4);
 #pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
+    for (int tp = 0; tp < TPW; ++tp) {
+      load_x(0, tp);
 #pragma unroll
       for (int q = 0; q < S; ++q)
         wld[tp][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                          rw, (uint32_t(kt[tp]) * 256 * S + (64 * q + lane) * 4) * 4, 0, 0));
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int tp = 0; tp < TPW; ++tp) load_x(b, tp);
   }
   // (the fence keeps every activation load ahead of the wait for offsets)
   __builtin_amdgcn_sched_barrier(0);
@@ -436,54 +439,58 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   auto aop = [&](int b, int tp, int i, int h, int pa) -> const u32x4_t& { return Araw[b][tp][i][h][pa]; };
   // inputs past K and tiles this wave does not have get zero activations, so their
   // products and sums are exactly zero whatever the redirected loads hold
+  auto zero_tile = [&](int b, int tp) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool real = live[tp] && kt[tp] * 256 + xk(i, h) < K;
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+          if (!real) Araw[b][tp][i][h][q] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+  };
   auto setup_zero = [&]() {
 #pragma unroll
     for (int b = 0; b < TB; ++b)
 #pragma unroll
-      for (int tp = 0; tp < TPW; ++tp)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const bool real = live[tp] && kt[tp] * 256 + xk(i, h) < K;
-#pragma unroll
-            for (int q = 0; q < NA; ++q)
-              if (!real) Araw[b][tp][i][h][q] = u32x4_t{0u, 0u, 0u, 0u};
-          }
+      for (int tp = 0; tp < TPW; ++tp) zero_tile(b, tp);
   };
   AF4 af[F4 ? TPW : 1][2];
-  auto setup_a = [&]() {
+  // F4: fp8 pairs and scales of one tile's 128-input blocks, then its group sums X on the
+  // same instruction with every code 2 (fp4 1.0, B scale 1): X = sum x
+  auto f4_tile = [&](int tp) __attribute__((always_inline)) {
     if constexpr (F4) {
-      // fp8 pairs and scales of the wave's 128-input blocks, then the group sums X on the
-      // same instruction with every code 2 (fp4 1.0, B scale 1): X = sum x
       constexpr uint32_t kOne4 = 0x22222222u;
 #pragma unroll
-      for (int tp = 0; tp < TPW; ++tp)
+      for (int m = 0; m < 2; ++m)
+        af[tp][m] = prep_a_f4(Araw[0][tp][2 * m][0][0], Araw[0][tp][2 * m][1][0],
+                              Araw[0][tp][2 * m + 1][0][0], Araw[0][tp][2 * m + 1][1][0]);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-          af[tp][m] = prep_a_f4(Araw[0][tp][2 * m][0][0], Araw[0][tp][2 * m][1][0],
-                                Araw[0][tp][2 * m + 1][0][0], Araw[0][tp][2 * m + 1][1][0]);
+      for (int gi = 0; gi < GPT; ++gi) {
+        f32x4_t xs4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int tp = 0; tp < TPW; ++tp)
-#pragma unroll
-        for (int gi = 0; gi < GPT; ++gi) {
-          f32x4_t xs4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            // group gi's inputs within block m: all of it (128, 256) or one half (64)
-            if (G == 64 && m != (gi >> 1)) continue;
-            if (G == 128 && m != gi) continue;
-            const uint32_t lo = (G == 64 && (gi & 1)) ? 0u : kOne4, hi = (G == 64 && !(gi & 1)) ? 0u : kOne4;
-            const uint32_t ones[4] = {lo, lo, hi, hi};
-            xs4 = mfma_f4<127>(af[tp][m].hi, ones, af[tp][m].sc, xs4);
-            xs4 = mfma_f4<127>(af[tp][m].lo, ones, af[tp][m].sc, xs4);
-          }
-          mfma_result_fence();
-          if (r == 0) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) xsT[wave][0][tp * GPT + gi][4 * c + v] = xs4[v];
-          }
+        for (int m = 0; m < 2; ++m) {
+          // group gi's inputs within block m: all of it (128, 256) or one half (64)
+          if (G == 64 && m != (gi >> 1)) continue;
+          if (G == 128 && m != gi) continue;
+          const uint32_t lo = (G == 64 && (gi & 1)) ? 0u : kOne4, hi = (G == 64 && !(gi & 1)) ? 0u : kOne4;
+          const uint32_t ones[4] = {lo, lo, hi, hi};
+          xs4 = mfma_f4<127>(af[tp][m].hi, ones, af[tp][m].sc, xs4);
+          xs4 = mfma_f4<127>(af[tp][m].lo, ones, af[tp][m].sc, xs4);
         }
+        mfma_result_fence();
+        if (r == 0) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xsT[wave][0][tp * GPT + gi][4 * c + v] = xs4[v];
+        }
+      }
+    }
+  };
+  auto setup_a = [&]() {
+    if constexpr (F4) {
+#pragma unroll
+      for (int tp = 0; tp < TPW; ++tp) f4_tile(tp);
       return;
     }
 #pragma unroll
@@ -721,14 +728,24 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     load_lr(c0, rb0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  setup_zero();
   if constexpr (RT) {
     // Row blocks 0 and 1 go out after this, before the budgets are known, with every
     // slice's range; slices past jmax add nothing there, since no budget reaches them.
     // Wr as three bfloat16 planes (hi + mid + lo = the float32 value: each plane takes the
     // previous one's exact remainder), column-major per tile: wrp[wave][tile][plane][j][k]
+    // logits^T = Wr^T x^T on the matrix cores: the activation registers (lane (r, c): token r,
+    // 8 inputs per 32-input step) are the B operand as they stand -- setup has already
+    // zeroed those of inputs past K and of tiles this wave does not have -- and lane (j, c)
+    // of the A operand holds column j of Wr over the same inputs (rows past S repeat a real
+    // column; their products land in rows of D nobody reads), so lane (n, 0) ends with
+    // token n's S logits.  One accumulator per plane, added lo + mid + hi at the end.
+    const int jr = min(r & 3, S - 1);
+    f32x4_t Lp[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // tile by tile, so the first tile's work overlaps the second tile's loads: zero its
+    // inputs past K, stage its Wr planes, route it, and (F4) split it into fp8 pairs
 #pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
+    for (int tp = 0; tp < TPW; ++tp) {
+      zero_tile(0, tp);
 #pragma unroll
       for (int q = 0; q < S; ++q)
 #pragma unroll
@@ -747,16 +764,6 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           wrp[wave][tp][1][(f + 1) % S][(f + 1) / S] = uint16_t(p1 >> 16);
           wrp[wave][tp][2][(f + 1) % S][(f + 1) / S] = uint16_t(p2 >> 16);
         }
-    // logits^T = Wr^T x^T on the matrix cores: the activation registers (lane (r, c): token r,
-    // 8 inputs per 32-input step) are the B operand as they stand -- setup has already
-    // zeroed those of inputs past K and of tiles this wave does not have -- and lane (j, c)
-    // of the A operand holds column j of Wr over the same inputs (rows past S repeat a real
-    // column; their products land in rows of D nobody reads), so lane (n, 0) ends with
-    // token n's S logits.  One accumulator per plane, added lo + mid + hi at the end.
-    const int jr = min(r & 3, S - 1);
-    f32x4_t Lp[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -766,14 +773,19 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           for (int pl = 0; pl < 3; ++pl)
             Lp[pl] = mfma(*reinterpret_cast<const u32x4_t*>(&wrp[wave][tp][pl][jr][kl]), Araw[0][tp][i][h][0], Lp[pl]);
         }
+      f4_tile(tp);
+    }
     mfma_result_fence();
     const f32x4_t L = (Lp[2] + Lp[1]) + Lp[0];
     if (c == 0) {
 #pragma unroll
       for (int j = 0; j < S; ++j) lgp[wave][r][j] = L[j];
     }
+    if constexpr (!F4) setup_a();
+  } else {
+    setup_zero();
+    setup_a();
   }
-  setup_a();
   if constexpr (RT) {
     // (row block 0 goes out here with routing: until now the activation and Wr loads of
     // every wave had the CU's memory queue to themselves)
