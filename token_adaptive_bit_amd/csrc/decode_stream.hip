@@ -3,16 +3,19 @@
 // Same arithmetic as decode.hip (MoBiQuant explainer, gist.science English page, sections
 // 2.A and 3: each token sums its own slices; only slices some token uses are fetched):
 //   y[t, n] = sum_j [b(t) >= j] sum_g ( s_jng * P_jng[t] + z_jng * X_g[t] ),
-//   P = sum_{k in g} x_k q_k on MFMA 16x16x32 bf16 with raw codes as bf16 (o + q) values
-//   and the accumulator seeded with -sum_k x_k o_k.
+//   P = sum_{k in g} x_k q_k, on one of two multiplies:
+//   * bf16 operands: MFMA 16x16x32 bf16 with raw codes as bf16 (o + q) values and the
+//     accumulator seeded with -sum_k x_k o_k;
+//   * F4: MFMA 16x16x128 fp8 x fp4 with the codes as e2m1 nibbles (q / 2, B scale 2) and the
+//     activations split exactly into e4m3 hi + lo pairs (see the F4 section below).
 //
 // Organisation (one persistent workgroup per CU):
 //   * tokens come in blocks of 16 (workgroup row blockIdx.y, at most 4 for T <= 64), one
 //     MFMA token block each; rows stay in the tokens' original order, so x is read with no
 //     dependence on perm, and perm / offsets only decide which slices count for which row;
 //   * wave w owns k tiles w, w + NW, ... (TPW of them): their slice of its token block's x
-//     (the A operand) and the per-group seeds -sum x*o and sum x are computed once and stay
-//     in registers for the whole kernel;
+//     (the A operand) and the per-group seeds -sum x*o and sums X are computed once and stay
+//     in registers (X in LDS) for the whole kernel;
 //   * the workgroup walks row blocks nb = blockIdx.x, + gridDim.x, ...; for each, every
 //     wave multiplies its k tiles of every needed slice while the next two row blocks'
 //     codes and params are already loading (three register buffers with fixed roles,
@@ -21,6 +24,8 @@
 //   * the waves' partial 16x16 tiles are summed in LDS (double-buffered, one barrier per
 //     row block) and written out with per-token slice masks already applied.
 // Token perm[i] (sorted position i) has budget b with offsets[b-1] <= i < offsets[b].
+// With RT (the one-launch decode step, mbq_route_linear) the kernel computes perm and
+// offsets itself: see RouteIO below.
 #include <cstdlib>
 #include <type_traits>
 
