@@ -251,7 +251,13 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
  * aligned, that kernel routes the batch itself: every workgroup multiplies the
  * activations it already holds by Wr (fixed summation order, so all of them reach the
  * same budgets) and workgroup 0 writes the routing outputs -- one launch instead of
- * three.  Otherwise the two calls run in sequence.  Errors as in the two calls.
+ * three.  Where each workgroup streams 4 or more row blocks of 16 outputs over 2 or more
+ * slices, that kernel multiplies on the fp8 x fp4 matrix instruction instead of bf16:
+ * codes enter exactly, the activations as an exact e4m3 pair per 128 inputs, and the
+ * instruction's own sum adds an error of about 1e-5 of the sum of |products| (y stays
+ * within 1e-3 per token of the bf16 multiply); the environment variable MBQ_DECODE_F4=1
+ * or =0 forces the choice.  Otherwise the two calls run in sequence.  Errors as in the
+ * two calls.
  */
 mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                             mbq_dtype x_dtype, const float* wr, float* logits, int32_t* budget,
