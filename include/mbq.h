@@ -229,8 +229,11 @@ mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dty
  * partials a second small kernel sums in a fixed order when K is long; prefill
  * (t > 64) runs an MFMA GEMM over tiles of one budget group each: the summed slices are
  * dequantized to bfloat16 MFMA operands once per 256-token tile and shared between the
- * two waves of a SIMD through LDS.  Rows whose perm entry is outside [0, t) are not
- * written; offsets outside [0, t] are clamped (no access outside x, y, perm).
+ * two waves of a SIMD through LDS.  Full tiles past the first round of workgroups (one
+ * per CU) are split into 128-token tiles when that lets the second round fit; the
+ * environment variable MBQ_PREFILL_SLOTS sets the workgroup count that rule assumes (it
+ * changes which tiles are split, not what is computed).  Rows whose perm entry is outside
+ * [0, t) are not written; offsets outside [0, t] are clamped (no access outside x, y, perm).
  */
 mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                       mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,

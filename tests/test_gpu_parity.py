@@ -301,6 +301,26 @@ def test_prefill_generic_kernel(mbq, monkeypatch):
     assert token_errors(yg, yref).max() <= TOL
 
 
+@pytest.mark.parametrize("slots", [9, 10, 11, 12])
+def test_prefill_halved_tail_tiles(mbq, monkeypatch, slots):
+    """Full tiles past the first round of workgroups halved into 128-token tiles.  With
+    budget groups of 300 / 600 / 200 tokens and 600 outputs (3 column tiles) there are 12
+    full tiles and 6 half tiles: 10 or 11 workgroup slots halve the last 2 or 1 (the last
+    one holding 200 tokens: parts of 128 and 72), 9 and 12 halve none.  Against the oracle,
+    and against the launch on the real CU count (no halving) within float32 rounding."""
+    d = inputs.make_linear(8, 600, 512, 1100, group=128, slices=3, dtype="bf16", n_outliers=2,
+                           outlier_scale=10.0)
+    b = np.repeat(np.arange(1, 4, dtype=np.int32), [300, 600, 200])
+    b = b[np.random.default_rng(8).permutation(1100)]
+    monkeypatch.delenv("MBQ_PREFILL_SLOTS", raising=False)
+    base, _, _ = run_linear(mbq, d, b, out_dtype=torch.float32)
+    monkeypatch.setenv("MBQ_PREFILL_SLOTS", str(slots))
+    say(f"prefill halved tail tiles, {slots} slots")
+    yg, yref, _ = run_linear(mbq, d, b, out_dtype=torch.float32)
+    assert token_errors(yg, yref).max() <= TOL
+    assert token_errors(yg, base.astype(np.float64)).max() <= 1e-6
+
+
 @pytest.mark.parametrize("T,K,dtype", [(16, 640, "bf16"), (40, 5120, "bf16"), (9, 2304, "f32")])
 def test_decode_generic_kernel(mbq, monkeypatch, T, K, dtype):
     """The generic decode kernel (kept for slices of 4 GiB and more) against the oracle."""

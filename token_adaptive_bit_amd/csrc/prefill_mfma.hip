@@ -28,6 +28,8 @@
 // fenced around half of the dequantization of chunk q + 1, so one wave's VALU work runs
 // in the shadow of the other wave's MFMAs; codes, params and activations of chunk q + 2
 // load during chunk q, so the loop has no load it waits on at once.
+#include <cstdlib>
+
 #include "mbq_internal.h"
 
 namespace mbq {
@@ -489,8 +491,15 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& a, int start, int r
 // schedule); the grid is sized for the most tiles any budget split can need and the real
 // count comes from offsets.  The 256 MiB last-level cache serves the activation and
 // weight tiles that several XCDs read.
+//
+// One workgroup fills a CU (its LDS), so P workgroups run at once (P = the CU count).
+// When the full tiles outnumber P, the F - P of them past the first round would make a
+// second round as long as the first while most CUs idle.  If halving them (two tiles of
+// 128 tokens each, numbered right after the first P) lets the second round's tiles, the
+// budget groups' own half tiles included, fit in P, they are halved: the second round
+// then takes a half tile's time (the dequantization of 256 outputs plus half the MFMAs).
 template <bool XBF16>
-__global__ __launch_bounds__(512) void prefill_mfma_kernel(TileArgs a, int S,
+__global__ __launch_bounds__(512) void prefill_mfma_kernel(TileArgs a, int S, int P,
                                                            const int32_t* __restrict__ offsets) {
   constexpr int BMb = XBF16 ? 256 : 128, BMs = XBF16 ? 128 : 0;
   __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<XBF16>()];
@@ -511,11 +520,24 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(TileArgs a, int S,
     nhalf += half_[bb];
   }
   const int NT = (a.N + kBN - 1) / kBN;
+  // tile ti in the unsplit numbering (full tiles, then half tiles) and, for a halved full
+  // tile, which 128 of its tokens (part 0 or 1)
+  const int F = NT * nfull, H = NT * nhalf;
+  const int X = (BMs > 0 && F > P && 2 * (F - P) + H <= P) ? F - P : 0;
   const int lin = blockIdx.x;
-  if (lin >= NT * (nfull + nhalf)) return;
-  int m = lin / NT;
-  const int n0 = (lin % NT) * kBN;
-  const bool is_half = m >= nfull;
+  int ti = lin, part = -1;
+  if (X > 0 && lin >= P) {
+    if (lin < P + 2 * X) {
+      ti = P + ((lin - P) >> 1);
+      part = (lin - P) & 1;
+    } else {
+      ti = lin - X;
+    }
+  }
+  if (ti >= F + H) return;
+  int m = ti / NT;
+  const int n0 = (ti % NT) * kBN;
+  bool is_half = m >= nfull;
   if (is_half) m -= nfull;
   int b = 0, start = 0, rows = 0;
 #pragma unroll
@@ -531,6 +553,12 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(TileArgs a, int S,
     m -= cnt;
   }
   if (b == 0) return;  // uniform; unreachable for lin below the tile count
+  if (part >= 0) {
+    // a full tile holds more than BMs rows, so either part has at least one
+    start += BMs * part;
+    rows = min(BMs, rows - BMs * part);
+    is_half = true;
+  }
   if constexpr (BMs > 0) {
     if (is_half) {
       switch (b) {
@@ -548,6 +576,20 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(TileArgs a, int S,
     case 3: prefill_tile<3, XBF16, BMb>(a, start, rows, n0, lds); break;
     default: prefill_tile<4, XBF16, BMb>(a, start, rows, n0, lds); break;
   }
+}
+
+// Workgroups of the kernel that run at once: one per CU.  MBQ_PREFILL_SLOTS overrides the
+// count (it only changes which full tiles are halved, never the results' definition).
+int resident_slots() {
+  if (const char* e = std::getenv("MBQ_PREFILL_SLOTS")) {
+    const int v = std::atoi(e);
+    if (v > 0) return v;
+  }
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 }  // namespace
@@ -585,13 +627,15 @@ hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t,
   a.lr_r = lr_r;
   a.lr_ks = lr_ks;
   const int NT = (d.n + kBN - 1) / kBN;
-  // at most ceil(R / BM) tiles per budget group (a half tile replaces a full one)
-  const int max_tiles = NT * ((t + BM - 1) / BM + d.slices - 1);
+  // at most ceil(R / BM) tiles per budget group (a half tile replaces a full one), plus
+  // the halved ones: at most P / 2, since halving requires 2 (F - P) + H <= P
+  const int P = resident_slots();
+  const int max_tiles = NT * ((t + BM - 1) / BM + d.slices - 1) + P / 2;
   dim3 grid(max_tiles), block(512);
   if (x_bf16)
-    hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, block, 0, stream, a, d.slices, offsets);
+    hipLaunchKernelGGL(prefill_mfma_kernel<true>, grid, block, 0, stream, a, d.slices, P, offsets);
   else
-    hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, block, 0, stream, a, d.slices, offsets);
+    hipLaunchKernelGGL(prefill_mfma_kernel<false>, grid, block, 0, stream, a, d.slices, P, offsets);
   return hipGetLastError();
 }
 
