@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MBQ_ABI_VERSION 1
+#define MBQ_ABI_VERSION 2
 
 typedef enum {
   MBQ_OK = 0,
@@ -62,6 +62,33 @@ typedef enum {
 } mbq_status;
 
 typedef enum { MBQ_F32 = 0, MBQ_BF16 = 1 } mbq_dtype;
+
+/*
+ * Kernel and tiling choices of the routed linear, for tests and tuning.  Every call that
+ * takes `const mbq_opts* opts` accepts NULL for "every field 0" (automatic choices).  A
+ * field outside its range is MBQ_ERR_ARG.  No choice changes what is computed beyond the
+ * stated precision of the multiply it selects.
+ */
+typedef enum {
+  MBQ_PATH_AUTO = 0,     /* the streaming decode (t <= 64) and the MFMA prefill (t > 64) where they apply */
+  MBQ_PATH_GENERIC = 1,  /* the generic decode and prefill kernels (those that serve slices or
+                            activations of 4 GiB and more) */
+} mbq_path;
+
+typedef enum {
+  MBQ_MUL_AUTO = 0,      /* the plan's choice (see mbq_route_linear) */
+  MBQ_MUL_BF16 = 1,      /* codes as bfloat16 (o + q) values, activations as they are: exact products */
+  MBQ_MUL_FP8_FP4 = 2,   /* codes as e2m1, activations as an exact e4m3 hi + lo pair per 128 inputs */
+} mbq_mul;
+
+typedef struct {
+  int32_t path;           /* mbq_path */
+  int32_t decode_mul;     /* mbq_mul of the one-launch decode step (mbq_route_linear) */
+  int32_t prefill_slots;  /* workgroups the MFMA prefill's tile plan assumes run at once
+                             (0: the device's compute units); it decides which full tiles are
+                             split in two, never the results */
+  int32_t reserved;       /* 0 */
+} mbq_opts;
 
 /*
  * Geometry of one packed weight (the "one checkpoint for every precision" of the
@@ -230,15 +257,16 @@ mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dty
  * (t > 64) runs an MFMA GEMM over tiles of one budget group each: the summed slices are
  * dequantized to bfloat16 MFMA operands once per 256-token tile and shared between the
  * two waves of a SIMD through LDS.  Full tiles past the first round of workgroups (one
- * per CU) are split into 128-token tiles when that lets the second round fit; the
- * environment variable MBQ_PREFILL_SLOTS sets the workgroup count that rule assumes (it
- * changes which tiles are split, not what is computed).  Rows whose perm entry is outside
- * [0, t) are not written; offsets outside [0, t] are clamped (no access outside x, y, perm).
+ * per CU) are split into 128-token tiles when that lets the second round fit
+ * (opts->prefill_slots sets the workgroup count that rule assumes).  Rows whose perm entry
+ * is outside [0, t) are not written; offsets outside [0, t] are clamped (no access outside
+ * x, y, perm).
+ *   opts:    NULL or kernel choices (mbq_opts); opts->decode_mul is ignored here.
  */
 mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                       mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                       void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
-                      hipStream_t stream);
+                      const mbq_opts* opts, hipStream_t stream);
 
 /*
  * One decode step in one call: MoBiRoute (linear-argmax form) and the routed linear
@@ -258,14 +286,16 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
  * slices, that kernel multiplies on the fp8 x fp4 matrix instruction instead of bf16:
  * codes enter exactly, the activations as an exact e4m3 pair per 128 inputs, and the
  * instruction's own sum adds an error of about 1e-5 of the sum of |products| (y stays
- * within 1e-3 per token of the bf16 multiply); the environment variable MBQ_DECODE_F4=1
- * or =0 forces the choice.  Otherwise the two calls run in sequence.  Errors as in the
- * two calls.
+ * within 1e-3 per token of the bf16 multiply); opts->decode_mul forces either multiply
+ * (a blob of one slice always takes the bf16 multiply).
+ * Otherwise (or with opts->path == MBQ_PATH_GENERIC) the two calls run in sequence.
+ * Errors as in the two calls.
  */
 mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                             mbq_dtype x_dtype, const float* wr, float* logits, int32_t* budget,
                             int32_t* perm, int32_t* offsets, void* y, mbq_dtype y_dtype,
-                            void* workspace, size_t ws_bytes, hipStream_t stream);
+                            void* workspace, size_t ws_bytes, const mbq_opts* opts,
+                            hipStream_t stream);
 
 /* Host only: bytes of device workspace mbq_linear_lowrank needs: u as c float32 partials
  * over chunks of K ([c x t x rank], c <= 8 chosen from t and k; rounded up to 256 bytes)
@@ -283,7 +313,7 @@ mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dty
  *   b:     [n x rank] bfloat16 bit patterns, row-major, 16-byte aligned.
  *   rank:  a multiple of 8 in [8, 32] (MBQ_ERR_UNSUPPORTED otherwise).
  *   workspace: at least mbq_linear_lowrank_workspace() bytes, 16-byte aligned.
- *   Other arguments as in mbq_linear.
+ *   Other arguments (opts too) as in mbq_linear.
  * u = x . A^T is computed first (float32 accumulation over k; float32 x as a bf16 hi + lo
  * pair), then the linear kernels add u . B^T to their float32 accumulators before the one
  * rounding to y (u enters their MFMAs as a bf16 hi + lo pair).  Kernels without that
@@ -294,7 +324,7 @@ mbq_status mbq_linear_lowrank(const mbq_desc* desc, const void* packed, int32_t 
                               mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                               const uint16_t* a, const uint16_t* b, int32_t rank, void* y,
                               mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
-                              hipStream_t stream);
+                              const mbq_opts* opts, hipStream_t stream);
 
 /* Static string for a status code. */
 const char* mbq_status_str(mbq_status status);

@@ -32,7 +32,7 @@ def test_exports_match_header():
     assert set(names) == set(lib_mod.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.mbq_abi_version() == 1
+    assert L.mbq_abi_version() == 2
 
 
 def test_status_strings():
@@ -136,7 +136,7 @@ def test_linear_lowrank_workspace(N, K, G, S, t, rank, uchunks, chunks):
     need = ub + (chunks * t * N * 4 if chunks > 1 else 0)
     for ws, wsb in ((None, 0), (f, need - 1), (P(FAKE + 8), need)):
         assert L.mbq_linear_lowrank(ctypes.byref(d), f, t, f, BF16, f, f, f, f, rank, f, BF16, ws, wsb,
-                                    None) == WS
+                                    None, None) == WS
 
 
 def test_linear_lowrank_validation():
@@ -145,10 +145,10 @@ def test_linear_lowrank_validation():
     n = ctypes.c_size_t(0)
     for r in (0, 4, 12, 40, -8):
         assert L.mbq_linear_lowrank_workspace(dp, 16, BF16, r, ctypes.byref(n)) == UNSUP
-        assert L.mbq_linear_lowrank(dp, f, 16, f, BF16, f, f, f, f, r, f, BF16, f, 1 << 30, None) == UNSUP
+        assert L.mbq_linear_lowrank(dp, f, 16, f, BF16, f, f, f, f, r, f, BF16, f, 1 << 30, None, None) == UNSUP
 
     def call(a=f, b=f, t=16):
-        return L.mbq_linear_lowrank(dp, f, t, f, BF16, f, f, a, b, 16, f, BF16, f, 1 << 30, None)
+        return L.mbq_linear_lowrank(dp, f, t, f, BF16, f, f, a, b, 16, f, BF16, f, 1 << 30, None, None)
 
     assert call(a=None) == ARG and call(b=None) == ARG
     assert call(a=P(FAKE + 8)) == ARG and call(b=P(FAKE + 2)) == ARG
@@ -182,12 +182,14 @@ def test_route_linear_validation():
         a = dict(desc=dp, packed=f, t=16, x=f, xd=BF16, wr=f, lg=f, b=f, perm=f, off=f, y=f, yd=BF16)
         a.update(kw)
         return L.mbq_route_linear(a["desc"], a["packed"], a["t"], a["x"], a["xd"], a["wr"], a["lg"], a["b"],
-                                  a["perm"], a["off"], a["y"], a["yd"], None, 0, None)
+                                  a["perm"], a["off"], a["y"], a["yd"], None, 0, a.get("o"), None)
 
     assert call(desc=None) == ARG
     assert call(t=-1) == SHAPE and call(t=1 << 25) == SHAPE
     assert call(xd=7) == ARG and call(yd=7) == ARG
     assert call(off=None) == ARG
+    assert call(o=ctypes.byref(lib_mod.MbqOpts(0, 5, 0, 0))) == ARG
+    assert call(o=ctypes.byref(lib_mod.MbqOpts(3, 0, 0, 0))) == ARG
     for k in ("packed", "x", "wr", "lg", "b", "perm", "y"):
         assert call(**{k: None}) == ARG, k
     assert call(packed=P(FAKE + 64)) == ARG
@@ -261,9 +263,9 @@ def test_linear_validation_and_workspace():
     assert L.mbq_linear_workspace(dp, 1, BF16, None) == ARG
     assert L.mbq_linear_workspace(dp, 1, 5, ctypes.byref(n)) == ARG
     args = lambda **kw: dict(dict(desc=dp, packed=f, t=16, x=f, xd=BF16, perm=f, off=f, y=f,
-                                  yd=BF16, ws=None, wsb=0, s=None), **kw)
+                                  yd=BF16, ws=None, wsb=0, o=None, s=None), **kw)
     call = lambda a: L.mbq_linear(a["desc"], a["packed"], a["t"], a["x"], a["xd"], a["perm"],
-                                  a["off"], a["y"], a["yd"], a["ws"], a["wsb"], a["s"])
+                                  a["off"], a["y"], a["yd"], a["ws"], a["wsb"], a["o"], a["s"])
     assert call(args(desc=None)) == ARG
     assert call(args(packed=None)) == ARG
     assert call(args(packed=P(FAKE + 64))) == ARG
@@ -279,6 +281,14 @@ def test_linear_validation_and_workspace():
     assert call(args(desc=ctypes.byref(bad))) == SHAPE
     # nothing to do: every t-sized pointer may be NULL and nothing is launched
     assert call(args(t=0, x=None, perm=None, off=None, y=None, packed=None)) == OK
+    # kernel choices: a field out of range is an argument error, found before any launch
+    Opts = lib_mod.MbqOpts
+    for o in (Opts(2, 0, 0, 0), Opts(-1, 0, 0, 0), Opts(0, 3, 0, 0), Opts(0, -1, 0, 0),
+              Opts(0, 0, -1, 0), Opts(0, 0, 0, 1)):
+        assert call(args(o=ctypes.byref(o))) == ARG
+        assert call(args(o=ctypes.byref(o), t=0, x=None, perm=None, off=None, y=None, packed=None)) == ARG
+    assert call(args(o=ctypes.byref(Opts(1, 2, 300, 0)), t=0, x=None, perm=None, off=None, y=None,
+                     packed=None)) == OK
 
 
 @pytest.mark.parametrize("N,K,G,S,t,dt,chunks", [
@@ -309,4 +319,4 @@ def test_decode_split_k_workspace(N, K, G, S, t, dt, chunks):
     if chunks > 1:  # a missing or short workspace is refused before any launch
         f = P(FAKE)
         for ws, wsb in ((None, 0), (f, n.value - 1)):
-            assert L.mbq_linear(ctypes.byref(d), f, t, f, dt, f, f, f, BF16, ws, wsb, None) == WS
+            assert L.mbq_linear(ctypes.byref(d), f, t, f, dt, f, f, f, BF16, ws, wsb, None, None) == WS

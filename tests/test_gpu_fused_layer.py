@@ -99,33 +99,5 @@ def test_fused_linear_parity(mbq, T):
         err = token_errors(yg[:, s0:s0 + W.shape[0]], yref)
         assert err.max() <= TOL
 
-
-def sample_rows(n, k, seed):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, k, replace=False)]))
-
-
-def test_full_layer14b_fused_workload(mbq):
-    """The 14B-like layer at T = 64 with q/k/v and gate/up fused: one router, four launches."""
-    cfg = inputs.make_config(4)
-    lin = {l["name"]: l for l in cfg["linears"]}
-    x0 = cfg["X_layer"]
-    xm = lin["gate"]["X"]
-    _, _, perm, off = mbq.route(to_dev(x0, torch.bfloat16), to_dev(cfg["Wr"], torch.float32))
-    torch.cuda.synchronize()
-    b = budget_from_perm(perm.cpu().numpy(), off.cpu().numpy())
-    groups = [(["q", "k", "v"], x0), (["o"], lin["o"]["X"]), (["gate", "up"], xm),
-              (["down"], lin["down"]["X"])]
-    for names, X in groups:
-        say(f"full layer14b fused {names}")
-        Ws = [lin[n]["W"] for n in names]
-        p, starts = mbq.pack_concat([to_dev(W, torch.bfloat16) for W in Ws], 128, 3)
-        y = mbq.linear(p, to_dev(X, torch.bfloat16), perm, off)
-        torch.cuda.synchronize()
-        yg = y.float().cpu().numpy()
-        for W, s0, n in zip(Ws, starts, names):
-            rows = sample_rows(W.shape[0], 12, len(n))
-            yref = oracle_linear_rows(W, X, b, 128, 3, rows)
-            err = token_errors(yg[:, s0 + rows], yref)
-            assert err.max() <= TOL, n
-        del p
+# (the 14B-like layer at full size, fused and separate, every output row:
+# tests/test_gpu_full_size.py)

@@ -37,15 +37,15 @@ def tdt(name):
     return torch.bfloat16 if name == "bf16" else torch.float32
 
 
-def run(mbq, N, K, G, S, T, dtype, rank, seed, rows=None):
+def run(mbq, N, K, G, S, T, dtype, rank, seed, rows=None, options=None):
     d = inputs.make_linear(seed, N, K, T, group=G, slices=S, dtype=dtype)
     lr = inputs.make_lowrank(seed + 1, N, K, rank=rank, b_scale=0.1)
     x = to_dev(d["X"], tdt(dtype))
     _, _, perm, off = mbq.route(x, to_dev(d["Wr"], torch.float32))
     p = mbq.pack(to_dev(d["W"], tdt(dtype)), group=G, slices=S)
     a, b = to_dev(lr["A"], torch.bfloat16), to_dev(lr["B"], torch.bfloat16)
-    y = mbq.linear_lowrank(p, x, perm, off, a, b, out_dtype=torch.float32)
-    y0 = mbq.linear(p, x, perm, off, out_dtype=torch.float32)
+    y = mbq.linear_lowrank(p, x, perm, off, a, b, out_dtype=torch.float32, options=options)
+    y0 = mbq.linear(p, x, perm, off, out_dtype=torch.float32, options=options)
     torch.cuda.synchronize()
     bud = budget_from_perm(perm.cpu().numpy(), off.cpu().numpy())
     W = d["W"] if rows is None else d["W"][rows]
@@ -99,28 +99,14 @@ def test_lowrank_every_decode_variant(mbq, G, S, dtype):
     check(*run(mbq, 96, 512, G, S, 24, dtype, 16, seed=G + 10 * S))
 
 
-@pytest.mark.parametrize("env,T", [("MBQ_GENERIC_DECODE", 16), ("MBQ_GENERIC_PREFILL", 100)])
-def test_lowrank_generic_kernels(mbq, monkeypatch, env, T):
-    """The generic kernels add the side path to y afterwards; same contract."""
-    monkeypatch.setenv(env, "1")
-    say(f"lowrank generic {env} T={T}")
-    check(*run(mbq, 160, 768, 128, 3, T, "bf16", 16, seed=7))
+@pytest.mark.parametrize("T", [16, 100])
+def test_lowrank_generic_kernels(mbq, T):
+    """The generic kernels (decode at 16 tokens, prefill at 100) add the side path to y
+    afterwards; same contract."""
+    say(f"lowrank generic T={T}")
+    check(*run(mbq, 160, 768, 128, 3, T, "bf16", 16, seed=7, options=mbq.opts(path="generic")))
 
 
 def test_lowrank_generic_decode_g64_s4_f32(mbq):
     """Group 64, 4 slices, float32 activations: only the generic decode takes it."""
     check(*run(mbq, 64, 512, 64, 4, 16, "f32", 16, seed=8))
-
-
-def test_lowrank_full_decode_workload(mbq):
-    """18944 x 3584, G128, S3, T = 16, rank 16; sampled rows against the oracle."""
-    rows = np.unique(np.concatenate([[0, 18943], np.random.default_rng(3).choice(18944, 40, replace=False)]))
-    say("lowrank full decode 18944x3584 T=16")
-    check(*run(mbq, 18944, 3584, 128, 3, 16, "bf16", 16, seed=2, rows=rows))
-
-
-def test_lowrank_full_prefill_workload(mbq):
-    """11008 x 4096, G128, S3, T = 2048, rank 16; sampled rows against the oracle."""
-    rows = np.unique(np.concatenate([[0, 11007], np.random.default_rng(4).choice(11008, 24, replace=False)]))
-    say("lowrank full prefill 11008x4096 T=2048")
-    check(*run(mbq, 11008, 4096, 128, 3, 2048, "bf16", 16, seed=3, rows=rows))

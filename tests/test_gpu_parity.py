@@ -195,7 +195,7 @@ def test_regroup_forced_mix(mbq):
 
 
 # ------------------------------------------------------------------------------ linear
-def run_linear(mbq, d, budget=None, out_dtype=None, rows=None):
+def run_linear(mbq, d, budget=None, out_dtype=None, rows=None, options=None):
     """GPU pack + route/regroup + linear; returns (y_gpu, y_ref [T, rows], budget)."""
     G, S, dt = d["group"], d["slices"], d["dtype"]
     p, st = gpu_pack(mbq, d["W"], G, S, dt)
@@ -205,7 +205,7 @@ def run_linear(mbq, d, budget=None, out_dtype=None, rows=None):
         _, _, perm, off = mbq.route(x, to_dev(d["Wr"], torch.float32))
     else:
         perm, off = mbq.regroup(to_dev(budget, torch.int32), S)
-    y = mbq.linear(p, x, perm, off, out_dtype=out_dtype or tdt(dt))
+    y = mbq.linear(p, x, perm, off, out_dtype=out_dtype or tdt(dt), options=options)
     torch.cuda.synchronize()
     b = budget_from_perm(perm.cpu().numpy(), off.cpu().numpy())
     if budget is not None:
@@ -293,16 +293,15 @@ def test_prefill_fp32_output(mbq):
     assert token_errors(yg, yref).max() <= TOL
 
 
-def test_prefill_generic_kernel(mbq, monkeypatch):
+def test_prefill_generic_kernel(mbq):
     """The plain LDS prefill kernel (kept for activations or slices of 4 GiB and more)."""
-    monkeypatch.setenv("MBQ_GENERIC_PREFILL", "1")
     d = inputs.make_linear(7, 200, 640, 300, dtype="bf16", n_outliers=2, outlier_scale=10.0)
-    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", 300, 3, 3))
+    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", 300, 3, 3), options=mbq.opts(path="generic"))
     assert token_errors(yg, yref).max() <= TOL
 
 
 @pytest.mark.parametrize("slots", [9, 10, 11, 12])
-def test_prefill_halved_tail_tiles(mbq, monkeypatch, slots):
+def test_prefill_halved_tail_tiles(mbq, slots):
     """Full tiles past the first round of workgroups halved into 128-token tiles.  With
     budget groups of 300 / 600 / 200 tokens and 600 outputs (3 column tiles) there are 12
     full tiles and 6 half tiles: 10 or 11 workgroup slots halve the last 2 or 1 (the last
@@ -312,22 +311,19 @@ def test_prefill_halved_tail_tiles(mbq, monkeypatch, slots):
                            outlier_scale=10.0)
     b = np.repeat(np.arange(1, 4, dtype=np.int32), [300, 600, 200])
     b = b[np.random.default_rng(8).permutation(1100)]
-    monkeypatch.delenv("MBQ_PREFILL_SLOTS", raising=False)
     base, _, _ = run_linear(mbq, d, b, out_dtype=torch.float32)
-    monkeypatch.setenv("MBQ_PREFILL_SLOTS", str(slots))
     say(f"prefill halved tail tiles, {slots} slots")
-    yg, yref, _ = run_linear(mbq, d, b, out_dtype=torch.float32)
+    yg, yref, _ = run_linear(mbq, d, b, out_dtype=torch.float32, options=mbq.opts(prefill_slots=slots))
     assert token_errors(yg, yref).max() <= TOL
     assert token_errors(yg, base.astype(np.float64)).max() <= 1e-6
 
 
 @pytest.mark.parametrize("T,K,dtype", [(16, 640, "bf16"), (40, 5120, "bf16"), (9, 2304, "f32")])
-def test_decode_generic_kernel(mbq, monkeypatch, T, K, dtype):
+def test_decode_generic_kernel(mbq, T, K, dtype):
     """The generic decode kernel (kept for slices of 4 GiB and more) against the oracle."""
-    monkeypatch.setenv("MBQ_GENERIC_DECODE", "1")
     say(f"generic decode N=120 K={K} T={T} {dtype}")
     d = inputs.make_linear(7 + T, 120, K, T, group=128, slices=3, dtype=dtype)
-    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", T, 3, T))
+    yg, yref, _ = run_linear(mbq, d, budgets_for("mix", T, 3, T), options=mbq.opts(path="generic"))
     assert token_errors(yg, yref).max() <= TOL
 
 
@@ -368,67 +364,8 @@ def test_linear_empty_batch(mbq):
     assert y.shape == (0, 64)
 
 
-# ------------------------------------------------------------------------------ full sizes
-def sample_rows(N, seed, k=48):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([rng.choice(N, k, replace=False), [0, N - 1]]))
-
-
-@pytest.mark.parametrize("T", [1, 4, 16, 17, 64])
-def test_full_decode_workload(mbq, T):
-    say(f"full decode 18944x3584 T={T}")
-    d = inputs.make_config(2)
-    d = dict(d, X=d["X"][:T], T=T)
-    rows = sample_rows(d["N"], T)
-    yg, yref, _ = run_linear(mbq, d, None, rows=rows)
-    err = token_errors(yg, yref)
-    say(f"  max token error {err.max():.3e}")
-    assert err.max() <= TOL
-
-
-def test_full_prefill_workload(mbq):
-    say("full prefill 11008x4096 T=2048 mix 614/1024/410")
-    d = inputs.make_config(3)
-    rows = sample_rows(d["N"], 3, k=24)
-    yg, yref, _ = run_linear(mbq, d, d["budget"], rows=rows)
-    err = token_errors(yg, yref)
-    say(f"  max token error {err.max():.3e}")
-    assert err.max() <= TOL
-
-
-@pytest.mark.parametrize("T,mode", [(32, "all1"), (32, "router"), (1024, "allS"), (1024, "router")])
-def test_full_sweep_workload(mbq, T, mode):
-    say(f"full sweep 14336x4096 T={T} {mode}")
-    d = inputs.make_config(5)
-    d = dict(d, X=d["X"][:T], T=T)
-    rows = sample_rows(d["N"], T, k=24)
-    yg, yref, _ = run_linear(mbq, d, budgets_for(mode, T, 3, 0), rows=rows)
-    err = token_errors(yg, yref)
-    say(f"  max token error {err.max():.3e}")
-    assert err.max() <= TOL
-
-
-def test_full_layer14b_workload(mbq):
-    """Seven linears of the 14B-like layer, one router on the layer input, T = 64."""
-    cfg = inputs.make_config(4)
-    x0 = to_dev(cfg["X_layer"], torch.bfloat16)
-    _, _, perm, off = mbq.route(x0, to_dev(cfg["Wr"], torch.float32))
-    torch.cuda.synchronize()
-    b = budget_from_perm(perm.cpu().numpy(), off.cpu().numpy())
-    for lin in cfg["linears"]:
-        say(f"full layer14b {lin['name']} {lin['W'].shape}")
-        W = lin["W"]
-        p, st = gpu_pack(mbq, W, 128, 3, "bf16")
-        assert st == 0
-        y = mbq.linear(p, to_dev(lin["X"], torch.bfloat16), perm, off)
-        torch.cuda.synchronize()
-        rows = sample_rows(W.shape[0], 4, k=16)
-        yref = oracle_linear_rows(W, lin["X"], b, 128, 3, rows)
-        err = token_errors(y.float().cpu().numpy()[:, rows], yref)
-        assert err.max() <= TOL
-        del p
-
-
+# ------------------------------------------------------------------------------ variants
+# (the five workloads at full size, every output row: tests/test_gpu_full_size.py)
 @pytest.mark.parametrize("G", [64, 128, 256])
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -445,12 +382,11 @@ def test_decode_every_variant(mbq, G, S, dtype, K, T):
 @pytest.mark.parametrize("G", [64, 128, 256])
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_generic_decode_every_variant(mbq, monkeypatch, G, S, dtype):
+def test_generic_decode_every_variant(mbq, G, S, dtype):
     """The generic decode kernel over every group / slice count / activation type."""
-    monkeypatch.setenv("MBQ_GENERIC_DECODE", "1")
     say(f"generic decode variant G={G} S={S} {dtype}")
     d = inputs.make_linear(G + S + 7, 96, 512, 24, group=G, slices=S, dtype=dtype)
-    yg, yref, _ = run_linear(mbq, d)
+    yg, yref, _ = run_linear(mbq, d, options=mbq.opts(path="generic"))
     assert token_errors(yg, yref).max() <= TOL
 
 
@@ -458,14 +394,12 @@ def test_generic_decode_every_variant(mbq, monkeypatch, G, S, dtype):
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("generic", [False, True])
-def test_prefill_every_variant(mbq, monkeypatch, G, S, dtype, generic):
+def test_prefill_every_variant(mbq, G, S, dtype, generic):
     """The MFMA prefill (and the generic one) over every group / slice count / activation
     type, router-mixed budgets over 300 tokens (full and half tiles, ragged rows)."""
-    if generic:
-        monkeypatch.setenv("MBQ_GENERIC_PREFILL", "1")
     say(f"prefill variant G={G} S={S} {dtype} generic={generic}")
     d = inputs.make_linear(G + S + 11, 200, 768, 300, group=G, slices=S, dtype=dtype)
-    yg, yref, _ = run_linear(mbq, d)
+    yg, yref, _ = run_linear(mbq, d, options=mbq.opts(path="generic" if generic else None))
     assert token_errors(yg, yref).max() <= TOL
 
 

@@ -9,8 +9,8 @@ Bars (as for mbq_route and mbq_linear called apart):
   * y within the per-token bar of 1e-2 against the float64 oracle on those budgets.
 Where budgets agree with the two-call path (mbq_route, then mbq_linear), y must equal its
 y bit for bit (the in-kernel routing changes where budgets come from, not the products),
-except on the fp8 x fp4 multiply (MBQ_DECODE_F4, chosen by the plan from 4 row blocks per
-workgroup), a different summation whose y must stay within 1e-3 per token of it.
+except on the fp8 x fp4 multiply (mbq_opts decode_mul, chosen by the plan from 4 row blocks
+per workgroup), a different summation whose y must stay within 1e-3 per token of it.
 """
 import numpy as np
 import pytest
@@ -42,12 +42,16 @@ def tdt(name):
     return torch.bfloat16 if name == "bf16" else torch.float32
 
 
-def run_case(mbq, N, K, G, S, T, dtype, seed, rows=None, f4=False):
-    d = inputs.make_linear(seed, N, K, T, group=G, slices=S, dtype=dtype)
-    x = to_dev(d["X"], tdt(dtype))
+def run_case(mbq, N, K, G, S, T, dtype, seed, rows=None, f4=False, mul="bf16", d=None):
+    """mul: the one-launch step's multiply (decode_mul; None lets the plan choose); f4: the
+    call is expected to take the fp8 x fp4 multiply."""
+    if d is None:
+        d = inputs.make_linear(seed, N, K, T, group=G, slices=S, dtype=dtype)
+    x = to_dev(d["X"][:T], tdt(dtype))
     wr = to_dev(d["Wr"], torch.float32)
     p = mbq.pack(to_dev(d["W"], tdt(dtype)), group=G, slices=S)
-    y, lg, b, perm, off = mbq.route_linear(p, x, wr, out_dtype=torch.float32)
+    y, lg, b, perm, off = mbq.route_linear(p, x, wr, out_dtype=torch.float32,
+                                           options=mbq.opts(decode_mul=mul))
     # the two-call path on the same inputs
     lg2, b2, perm2, off2 = mbq.route(x, wr)
     y2 = mbq.linear(p, x, perm2, off2, out_dtype=torch.float32)
@@ -100,41 +104,33 @@ FALLBACK = [
 ]
 
 
-@pytest.fixture
-def bf16_mul(monkeypatch):
-    monkeypatch.setenv("MBQ_DECODE_F4", "0")
-
-
 @pytest.mark.parametrize("N,K,G,S,T,dtype", FUSED + FALLBACK)
-def test_route_linear_parity(mbq, bf16_mul, N, K, G, S, T, dtype):
+def test_route_linear_parity(mbq, N, K, G, S, T, dtype):
     say(f"route_linear N={N} K={K} G={G} S={S} T={T} {dtype}")
     run_case(mbq, N, K, G, S, T, dtype, seed=N + 7 * T)
 
 
 @pytest.mark.parametrize("N,K,G,S,T,dtype", FUSED)
-def test_route_linear_parity_f4(mbq, monkeypatch, N, K, G, S, T, dtype):
-    """The same cases on the fp8 x fp4 multiply (forced on)."""
-    monkeypatch.setenv("MBQ_DECODE_F4", "1")
+def test_route_linear_parity_f4(mbq, N, K, G, S, T, dtype):
+    """The same cases on the fp8 x fp4 multiply (forced on; one slice keeps bf16)."""
     say(f"route_linear f4 N={N} K={K} G={G} S={S} T={T}")
-    run_case(mbq, N, K, G, S, T, dtype, seed=N + 7 * T, f4=True)
+    run_case(mbq, N, K, G, S, T, dtype, seed=N + 7 * T, f4=S > 1, mul="fp8fp4")
 
 
 @pytest.mark.parametrize("G", [64, 128, 256])
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
 @pytest.mark.parametrize("f4", [False, True])
-def test_route_linear_every_variant(mbq, monkeypatch, G, S, f4):
+def test_route_linear_every_variant(mbq, G, S, f4):
     """Every group / slice count of the in-kernel routing, with two k tiles per wave
     (K = 2560: 10 tiles over 8 waves) and a router that mixes budgets, on either multiply."""
-    monkeypatch.setenv("MBQ_DECODE_F4", "1" if f4 else "0")
     say(f"route_linear variant G={G} S={S} f4={f4}")
-    run_case(mbq, 80, 2560, G, S, 16, "bf16", seed=G + S, f4=f4)
+    run_case(mbq, 80, 2560, G, S, 16, "bf16", seed=G + S, f4=f4 and S > 1, mul="fp8fp4" if f4 else "bf16")
 
 
 @pytest.mark.parametrize("f4", [False, True])
-def test_route_linear_one_tile_per_wave(mbq, monkeypatch, f4):
+def test_route_linear_one_tile_per_wave(mbq, f4):
     """K of 8 tiles: one tile per wave."""
-    monkeypatch.setenv("MBQ_DECODE_F4", "1" if f4 else "0")
-    run_case(mbq, 120, 2048, 128, 3, 16, "bf16", seed=3, f4=f4)
+    run_case(mbq, 120, 2048, 128, 3, 16, "bf16", seed=3, f4=f4, mul="fp8fp4" if f4 else "bf16")
 
 
 def test_route_linear_uniform_budgets(mbq):
@@ -178,17 +174,3 @@ def test_route_linear_empty(mbq):
     torch.cuda.synchronize()
     assert off.cpu().tolist() == [0, 0, 0, 0]
     assert y.shape == (0, 32)
-
-
-@pytest.mark.parametrize("f4", [None, False])
-def test_route_linear_full_decode_workload(mbq, monkeypatch, f4):
-    """18944 x 3584, G128, S3, T = 16 (the one-launch path: 4.6 row blocks per workgroup,
-    so the plan takes the fp4 multiply; then forced off); sampled rows against the oracle."""
-    if f4 is not None:
-        monkeypatch.setenv("MBQ_DECODE_F4", "0")
-    else:
-        monkeypatch.delenv("MBQ_DECODE_F4", raising=False)
-    rows = np.unique(np.concatenate([[0, 18943], np.random.default_rng(5).choice(18944, 40, replace=False)]))
-    say(f"route_linear full decode 18944x3584 T=16 f4={f4}")
-    b = run_case(mbq, 18944, 3584, 128, 3, 16, "bf16", seed=2, rows=rows, f4=f4 is None)
-    assert len(set(b.tolist())) >= 2   # the router mixes budgets here

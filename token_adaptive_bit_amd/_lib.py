@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmbq.so")
 
 MBQ_F32, MBQ_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANGE",
           -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}
@@ -34,6 +34,16 @@ class MbqDesc(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+MBQ_PATH_AUTO, MBQ_PATH_GENERIC = 0, 1
+MBQ_MUL_AUTO, MBQ_MUL_BF16, MBQ_MUL_FP8_FP4 = 0, 1, 2
+
+
+class MbqOpts(ctypes.Structure):
+    """Kernel and tiling choices of the routed linear (mbq_opts in include/mbq.h)."""
+    _fields_ = [("path", ctypes.c_int32), ("decode_mul", ctypes.c_int32),
+                ("prefill_slots", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class MbqError(RuntimeError):
@@ -66,12 +76,13 @@ def _load() -> ctypes.CDLL:
     lib.mbq_route_mlp.argtypes = [I32, I32, I32, I32, VP, I32, VP, VP, VP, VP, ctypes.c_double,
                                   VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
     lib.mbq_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
-    lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, VP]
+    O = P(MbqOpts)
+    lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, O, VP]
     lib.mbq_route_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP,
-                                     ctypes.c_size_t, VP]
+                                     ctypes.c_size_t, O, VP]
     lib.mbq_linear_lowrank_workspace.argtypes = [D, I32, I32, I32, P(ctypes.c_size_t)]
     lib.mbq_linear_lowrank.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, I32, VP, I32, VP,
-                                       ctypes.c_size_t, VP]
+                                       ctypes.c_size_t, O, VP]
     lib.mbq_status_str.argtypes = [I32]
     lib.mbq_status_str.restype = ctypes.c_char_p
     lib.mbq_abi_version.argtypes = []

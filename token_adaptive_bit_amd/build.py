@@ -22,19 +22,14 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmbq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-# gfx950: the compiler leaves too few wait states around 16x16x32 bf16 MFMAs for the
-# decode kernels' dependent chains (wrong products in some variants, exact once the
-# distances grew); these files are built with MFMA-to-MFMA padding.
-MFMA_PAD = ["-mllvm", "-amdgpu-mfma-padding-ratio=100"]
-
 SOURCES = {
     "api.hip": [],
     "pack.hip": ["-ffp-contract=off"],
     "route.hip": [],
     "route_mlp.hip": [],
     "lowrank.hip": [],
-    "decode.hip": MFMA_PAD,
-    "decode_stream.hip": MFMA_PAD,
+    "decode.hip": [],
+    "decode_stream.hip": [],
     "prefill.hip": [],
     "prefill_mfma.hip": [],
 }

@@ -212,12 +212,27 @@ size_t u_bytes(int32_t t, int32_t k, int32_t rank) {
 
 bool rank_ok(int32_t rank) { return rank >= 8 && rank <= 32 && rank % 8 == 0; }
 
+const mbq_opts kDefaultOpts{};
+
+// NULL means every field 0; a field out of range is an argument error.
+const mbq_opts* checked_opts(const mbq_opts* o) {
+  if (!o) return &kDefaultOpts;
+  if (o->path < MBQ_PATH_AUTO || o->path > MBQ_PATH_GENERIC) return nullptr;
+  if (o->decode_mul < MBQ_MUL_AUTO || o->decode_mul > MBQ_MUL_FP8_FP4) return nullptr;
+  if (o->prefill_slots < 0 || o->reserved != 0) return nullptr;
+  return o;
+}
+
 mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                        mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                        const uint16_t* a, const uint16_t* b, int32_t rank, void* y,
-                       mbq_dtype y_dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                       mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
+                       const mbq_opts* opts_in, hipStream_t stream) {
   mbq_status st = check_desc(desc);
   if (st != MBQ_OK) return st;
+  const mbq_opts* opts = checked_opts(opts_in);
+  if (!opts) return MBQ_ERR_ARG;
+  const bool generic = opts->path == MBQ_PATH_GENERIC;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
   if (rank && !rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
@@ -238,16 +253,15 @@ mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, cons
     st = launched(mbq::launch_lowrank_u(t, desc->k, x, xb, a, rank, u, stream));
     if (st != MBQ_OK) return st;
   }
-  // MBQ_GENERIC_DECODE forces the generic decode kernel (kept for slices of 4 GiB and more,
-  // which the streaming kernel's 32-bit buffer offsets cannot reach)
-  if (mbq::decode_stream_supported(*desc, t, xb, lr) && !std::getenv("MBQ_GENERIC_DECODE"))
+  // the generic kernels serve slices of 4 GiB and more (and activations of 4 GiB and more
+  // in prefill), which the streaming decode's and the MFMA prefill's 32-bit buffer offsets
+  // cannot reach; MBQ_PATH_GENERIC selects them for any size
+  if (!generic && mbq::decode_stream_supported(*desc, t, xb, lr))
     return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb, lws, u,
                                               ksu, b, rank, stream));
-  // MBQ_GENERIC_PREFILL forces the plain LDS kernel (kept for activations of 4 GiB and more
-  // or slices of 4 GiB and more, which the MFMA kernel's 32-bit buffer offsets cannot reach)
-  if (t > 64 && mbq::prefill_mfma_supported(*desc, t, x, xb) && !std::getenv("MBQ_GENERIC_PREFILL"))
+  if (!generic && t > 64 && mbq::prefill_mfma_supported(*desc, t, x, xb))
     return launched(mbq::launch_prefill_mfma(*desc, packed, t, x, xb, perm, offsets, y, yb, u, ksu, b,
-                                             rank, stream));
+                                             rank, opts->prefill_slots, stream));
   // the generic kernels: the side path is added to y afterwards
   if (t <= 64)
     st = launched(mbq::launch_decode(*desc, packed, t, x, xb, perm, offsets, y, yb, lws, stream));
@@ -272,33 +286,37 @@ mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dty
 mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                       mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                       void* y, mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
-                      hipStream_t stream) {
+                      const mbq_opts* opts, hipStream_t stream) {
   return linear_impl(desc, packed, t, x, x_dtype, perm, offsets, nullptr, nullptr, 0, y, y_dtype,
-                     workspace, ws_bytes, stream);
+                     workspace, ws_bytes, opts, stream);
 }
 
 mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                             mbq_dtype x_dtype, const float* wr, float* logits, int32_t* budget,
                             int32_t* perm, int32_t* offsets, void* y, mbq_dtype y_dtype,
-                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+                            void* workspace, size_t ws_bytes, const mbq_opts* opts_in,
+                            hipStream_t stream) {
   mbq_status st = check_desc(desc);
   if (st != MBQ_OK) return st;
+  const mbq_opts* opts = checked_opts(opts_in);
+  if (!opts) return MBQ_ERR_ARG;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
   if (!offsets) return MBQ_ERR_ARG;
   if (t > 0 && (!packed || !x || !wr || !logits || !budget || !perm || !y)) return MBQ_ERR_ARG;
-  if (t > 0 && x_dtype == MBQ_BF16 && mbq::decode_route_supported(*desc, t) &&
-      !std::getenv("MBQ_GENERIC_DECODE")) {
+  if (t > 0 && x_dtype == MBQ_BF16 && opts->path != MBQ_PATH_GENERIC &&
+      mbq::decode_route_supported(*desc, t)) {
     if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) ||
         !aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4))
       return MBQ_ERR_ARG;
     if (aligned(wr, 16))
       return launched(mbq::launch_decode_route(*desc, packed, t, x, wr, logits, budget, perm, offsets,
-                                               y, y_dtype == MBQ_BF16, stream));
+                                               y, y_dtype == MBQ_BF16, opts->decode_mul, stream));
   }
   st = mbq_route(t, desc->k, desc->slices, x, x_dtype, wr, logits, budget, perm, offsets, stream);
   if (st != MBQ_OK) return st;
-  return mbq_linear(desc, packed, t, x, x_dtype, perm, offsets, y, y_dtype, workspace, ws_bytes, stream);
+  return mbq_linear(desc, packed, t, x, x_dtype, perm, offsets, y, y_dtype, workspace, ws_bytes, opts,
+                    stream);
 }
 
 mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
@@ -316,10 +334,10 @@ mbq_status mbq_linear_lowrank(const mbq_desc* desc, const void* packed, int32_t 
                               mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                               const uint16_t* a, const uint16_t* b, int32_t rank, void* y,
                               mbq_dtype y_dtype, void* workspace, size_t ws_bytes,
-                              hipStream_t stream) {
+                              const mbq_opts* opts, hipStream_t stream) {
   if (!rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
   return linear_impl(desc, packed, t, x, x_dtype, perm, offsets, a, b, rank, y, y_dtype, workspace,
-                     ws_bytes, stream);
+                     ws_bytes, opts, stream);
 }
 
 }  // extern "C"

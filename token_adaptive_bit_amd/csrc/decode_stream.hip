@@ -26,7 +26,6 @@
 // Token perm[i] (sorted position i) has budget b with offsets[b-1] <= i < offsets[b].
 // With RT (the one-launch decode step, mbq_route_linear) the kernel computes perm and
 // offsets itself: see RouteIO below.
-#include <cstdlib>
 #include <type_traits>
 
 #include "mbq_internal.h"
@@ -39,29 +38,36 @@ constexpr int kMaxTokens = 64;  // tokens per launch (16 per workgroup row)
 constexpr uint32_t kNeg128 = 0xC300C300u, kNeg32 = 0xC200C200u, kNeg8 = 0xC100C100u;
 constexpr uint32_t kOnes = 0x3F803F80u;
 
-// (a & mask) | magic in one instruction.  gfx9 VOP3 takes no literal constants, so written
-// as C the compiler emits an AND and an OR with literals; here the mask comes from a
-// scalar register and the magic exponent from a vector register (one constant-bus read).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-  return r;
-}
-
+// Masks in scalar registers and the bf16 exponent patterns in vector registers, so that
+// (a & mask) | magic is one v_and_or_b32 (gfx9 VOP3 takes no literal constants and reads
+// at most one scalar operand).  Plain C: the compiler sees every producer of an MFMA
+// operand and inserts whatever wait states the hardware needs.
 struct Magic {
   uint32_t m128, m32, m8;  // bf16 pairs 128, 32 and 8 (vector registers)
+  uint32_t k3, kc, k30;    // field masks 0x00030003, 0x000C000C, 0x00300030 (scalar registers)
 };
+
+__device__ __forceinline__ Magic make_magic() {
+  Magic mg{0x43004300u, 0x42004200u, 0x41004100u, 0u, 0u, 0u};
+  // keep the patterns in vector registers (as constants they would compete with the mask
+  // for the one scalar operand and split every AND-OR in two)
+  asm volatile("" : "+v"(mg.m128), "+v"(mg.m32), "+v"(mg.m8));
+  mg.k3 = __builtin_amdgcn_readfirstlane(0x00030003u);
+  mg.kc = __builtin_amdgcn_readfirstlane(0x000C000Cu);
+  mg.k30 = __builtin_amdgcn_readfirstlane(0x00300030u);
+  return mg;
+}
 
 __device__ __forceinline__ void unpack_word(uint32_t w, const Magic& mg, u32x4_t& b0, u32x4_t& b1) {
   const uint32_t w6 = w >> 6, w12 = w >> 12;
-  b0[0] = and_or(w, 0x00030003u, mg.m128);    // 128 + q: inputs 0, 1
-  b0[1] = and_or(w, 0x000C000Cu, mg.m32);     //  32 + q: inputs 2, 3
-  b0[2] = and_or(w, 0x00300030u, mg.m8);      //   8 + q: inputs 4, 5
-  b0[3] = and_or(w6, 0x00030003u, mg.m128);   // 128 + q: inputs 6, 7
-  b1[0] = and_or(w6, 0x000C000Cu, mg.m32);    //  32 + q: inputs 8, 9
-  b1[1] = and_or(w6, 0x00300030u, mg.m8);     //   8 + q: inputs 10, 11
-  b1[2] = and_or(w12, 0x00030003u, mg.m128);  // 128 + q: inputs 12, 13
-  b1[3] = and_or(w12, 0x000C000Cu, mg.m32);   //  32 + q: inputs 14, 15
+  b0[0] = (w & mg.k3) | mg.m128;     // 128 + q: inputs 0, 1
+  b0[1] = (w & mg.kc) | mg.m32;      //  32 + q: inputs 2, 3
+  b0[2] = (w & mg.k30) | mg.m8;      //   8 + q: inputs 4, 5
+  b0[3] = (w6 & mg.k3) | mg.m128;    // 128 + q: inputs 6, 7
+  b1[0] = (w6 & mg.kc) | mg.m32;     //  32 + q: inputs 8, 9
+  b1[1] = (w6 & mg.k30) | mg.m8;     //   8 + q: inputs 10, 11
+  b1[2] = (w12 & mg.k3) | mg.m128;   // 128 + q: inputs 12, 13
+  b1[3] = (w12 & mg.kc) | mg.m32;    //  32 + q: inputs 14, 15
 }
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -69,19 +75,10 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// On gfx950 the compiler's wait states between a 16x16x32 bf16 MFMA and the VALU or LDS
-// instructions that read its result fall short: with the results read 9 wait states
-// after the last MFMA, decode variants (group 128 with 1 or 4 slices, group 64 with 4)
-// produced garbage or stale products, and doubling every distance made all of them exact.
-// Each MFMA chain is therefore followed by this fence (8 more wait states; 4, 8 and 32
-// all made every variant exact) before its result is read, and the file is built with
-// MFMA-to-MFMA padding (-amdgpu-mfma-padding-ratio=100), without which group 128 with 4
-// slices stayed wrong.
-__device__ __forceinline__ void mfma_result_fence() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// Each MFMA chain is followed by a scheduling fence before its results are read: it keeps
+// the compiler from interleaving the next group's chains with this group's epilogue,
+// which would lengthen live ranges past the 256 registers of a wave and spill.
+__device__ __forceinline__ void chain_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // ---- F4: bfloat16 activations on the scaled fp8 x fp4 matrix instruction
 // (v_mfma_scale_f32_16x16x128_f8f6f4), which takes the codes almost as stored.
@@ -198,13 +195,30 @@ struct LrRows {
 template <>
 struct LrRows<false> {};
 
+// One row block's loads for one wave: its tiles' code words and, per slice, the float16
+// (scale, zero) pairs of its NE (tile, group) units with one 4-byte load per 64 lanes:
+// lane 16 q + r of pw[j][h] holds unit 4 h + q of row r (spread to every lane of the
+// row by bcast_rows before use), instead of one load per unit.
 template <int G, int S, int TPW, bool LR = false>
 struct Codes {
-  static constexpr int GPT = 256 / G;
+  static constexpr int GPT = 256 / G, NE = TPW * GPT, PH = (NE + 3) / 4;
   u32x4_t cw[TPW][S];
-  uint32_t pv[TPW][S][GPT];
+  uint32_t pw[S][PH];
   LrRows<LR> lr;
 };
+
+// Row q (lanes 16 q .. 16 q + 15) of v copied to every row, for q = 0 .. 3: one swap of
+// the wave's halves and two of alternate rows (gfx950 v_permlane32_swap /
+// v_permlane16_swap).
+__device__ __forceinline__ void bcast_rows(uint32_t v, uint32_t (&o)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);        // rows 0 1 0 1 | 2 3 2 3
+  const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);  // rows 0 0 0 0 | 1 1 1 1
+  const auto c = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);  // rows 2 2 2 2 | 3 3 3 3
+  o[0] = b[0];
+  o[1] = b[1];
+  o[2] = c[0];
+  o[3] = c[1];
+}
 
 // Raw buffer loads: one scalar resource per slice, a scalar tile offset and one per-lane
 // offset that never changes, so the loop needs no vector address arithmetic.  (Buffer
@@ -213,22 +227,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint8_t* base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, int(bytes), 0x00020000);
 }
 
+// lane_pv[h]: the lane's byte offset of unit 4 h + (lane >> 4), row lane & 15, within a
+// row block's params (past the slice for units the wave does not have).
 template <int G, int S, int TPW, bool LR>
 __device__ __forceinline__ void load_codes(Codes<G, S, TPW, LR>& C, const __amdgpu_buffer_rsrc_t (&rs)[S],
                                            int nb, const int (&kt)[TPW], int KB, int NG,
-                                           uint32_t po, uint32_t lane_code, uint32_t lane_par) {
-  constexpr int GPT = 256 / G;
+                                           uint32_t po, uint32_t lane_code,
+                                           const uint32_t (&lane_pv)[Codes<G, S, TPW, LR>::PH]) {
+  constexpr int PH = Codes<G, S, TPW, LR>::PH;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp) {
       const uint32_t tile = uint32_t(nb * KB + kt[tp]) * kTileBytes;
       C.cw[tp][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs[j], lane_code, tile, 0));
-      const uint32_t par = po + uint32_t(nb * NG + kt[tp] * GPT) * 64;
-#pragma unroll
-      for (int gi = 0; gi < GPT; ++gi)
-        C.pv[tp][j][gi] = __builtin_amdgcn_raw_buffer_load_b32(rs[j], lane_par, par + gi * 64, 0);
     }
+    const uint32_t par = po + uint32_t(nb * NG) * 64;
+#pragma unroll
+    for (int h = 0; h < PH; ++h) C.pw[j][h] = __builtin_amdgcn_raw_buffer_load_b32(rs[j], lane_pv[h], par, 0);
   }
 }
 
@@ -425,7 +441,13 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     }
     __syncthreads();
   };
-  const uint32_t lane_code = 16u * lane, lane_par = 4u * (lane & 15);
+  const uint32_t lane_code = 16u * lane;
+  uint32_t lane_pv[Codes<G, S, TPW, LR>::PH];
+#pragma unroll
+  for (int h = 0; h < Codes<G, S, TPW, LR>::PH; ++h) {
+    const int u = 4 * h + (lane >> 4);
+    lane_pv[h] = u < TPW * GPT ? uint32_t(kt[u / GPT] * GPT + u % GPT) * 64u + 4u * (lane & 15) : 0x80000000u;
+  }
 
   // ---- 3. A operands (float32 inputs split into bf16 high and low parts) and the seeds
   // -sum x*o, sum x per group.  Computed inside the streaming loop, after the first weight
@@ -484,7 +506,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           xs4 = mfma_f4<127>(af[tp][m].hi, ones, af[tp][m].sc, xs4);
           xs4 = mfma_f4<127>(af[tp][m].lo, ones, af[tp][m].sc, xs4);
         }
-        mfma_result_fence();
+        chain_fence();
         if (r == 0) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) xsT[wave][0][tp * GPT + gi][4 * c + v] = xs4[v];
@@ -540,7 +562,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
               xs4 = mfma(aop(b, tp, i, 0, pa), ones, xs4);
               xs4 = mfma(aop(b, tp, i, 1, pa), ones, xs4);
             }
-          mfma_result_fence();
+          chain_fence();
           gnb[b][tp][gi] = nb4;
           // lanes (0, c) hold X of tokens 4c + v (every row n sees the same sums)
           if (r == 0) {
@@ -567,7 +589,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // ---- stream the row blocks.  One buffer resource per slice; a slice no token needs
   // gets an empty range, so its loads return zeros without any memory traffic (and its
   // MFMAs and epilogues are skipped).
-  const Magic mg{0x43004300u, 0x42004200u, 0x41004100u};
+  const Magic mg = make_magic();
   __amdgpu_buffer_rsrc_t rs[S];
 #pragma unroll
   for (int j = 0; j < S; ++j) rs[j] = slice_rsrc(packed + uint64_t(j) * ss, j < jmax ? uint32_t(ss) : 0u);
@@ -579,20 +601,34 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // Multiplies one row block.  JM, the slices processed, is a compile-time count, so the
   // MFMA chains and epilogues of a group form one straight-line block that the compiler
   // interleaves (a runtime test per slice or tile would split it into small blocks and
-  // expose every MFMA's latency).  JM is S, or 1 when no token of the batch uses more;
-  // slices in [jmax, JM) read zeros (empty buffer range) and so add exactly zero, and a
-  // wave without one of its tiles zeroes that tile's scales and zeros.
+  // expose every MFMA's latency).  JM is jmax, the number of slices some token of the
+  // batch uses (the loop has one instantiation per value; with the side path only 1 and
+  // S, so JM may exceed jmax there); slices past jmax are loaded with
+  // an empty buffer range (zeros, no memory traffic) and not multiplied, and a wave
+  // without one of its tiles zeroes that tile's scales and zeros.
   auto process = [&](auto jm, const Codes<G, S, TPW, LR>& C, int nb, int buf, Codes<G, S, TPW, LR>& Cn,
                      int nbn) __attribute__((always_inline)) {
     constexpr int JM = decltype(jm)::value;
     // the next buffer's loads (row block nbn) go out first: two row blocks stay in flight
-    load_codes(Cn, rs, nbn, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    load_codes(Cn, rs, nbn, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
     load_lr(Cn, nbn);
     f32x4_t acc[TB][JM];
 #pragma unroll
     for (int b = 0; b < TB; ++b)
 #pragma unroll
       for (int j = 0; j < JM; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // this row block's (scale, zero) pairs, unit u of slice j in every lane of row r
+    constexpr int PH = Codes<G, S, TPW, LR>::PH;
+    uint32_t prm[JM][4 * PH];
+#pragma unroll
+    for (int j = 0; j < JM; ++j)
+#pragma unroll
+      for (int h = 0; h < PH; ++h) {
+        uint32_t o4[4];
+        bcast_rows(C.pw[j][h], o4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) prm[j][4 * h + q] = o4[q];
+      }
     // One (tile, group) unit at a time: the slices' MFMA chains (one per token block, all
     // fed by the same unpacked codes) are independent and are issued interleaved, then
     // the unit's epilogue scales them into the accumulators.
@@ -652,7 +688,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           }
         }
       }
-      mfma_result_fence();
+      chain_fence();
       // the wave wrote this table itself, so its own in-order LDS accesses suffice
       f32x4_t X4[TB];
 #pragma unroll
@@ -660,8 +696,8 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
 #pragma unroll
       for (int j = 0; j < JM; ++j) {
         // scale and zero converted once each, then plain fmas (no mixed-precision fma)
-        float sc = __half2float(__ushort_as_half(uint16_t(C.pv[tp][j][gi] & 0xFFFFu)));
-        float zc = __half2float(__ushort_as_half(uint16_t(C.pv[tp][j][gi] >> 16)));
+        float sc = __half2float(__ushort_as_half(uint16_t(prm[j][u] & 0xFFFFu)));
+        float zc = __half2float(__ushort_as_half(uint16_t(prm[j][u] >> 16)));
         asm volatile("" : "+v"(sc), "+v"(zc));
 #pragma unroll
         for (int b = 0; b < TB; ++b)
@@ -683,7 +719,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       if constexpr (LR) {
         f32x4_t L = mfma(Uop[0], C.lr.v, f32x4_t{0.f, 0.f, 0.f, 0.f});
         L = mfma(Uop[1], C.lr.v, L);
-        mfma_result_fence();
+        chain_fence();
         out[0] += bud.x > 0 ? L[0] : 0.f;
         out[1] += bud.y > 0 ? L[1] : 0.f;
         out[2] += bud.z > 0 ? L[2] : 0.f;
@@ -718,7 +754,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // into buffer (m + 2) % 3 and then multiplies row block m from buffer m % 3, so two row
   // blocks are always in flight.  The prologue loads row blocks 0 and 1, with
   // the seeds and the budgets computed in between (no loads in either).  The loop is
-  // instantiated once per slice count (S, and 1 when no token of the batch uses more), so
+  // instantiated once per slice count read (1 .. S), so
   // inside each copy every path into the loop header carries the same pending loads in
   // the same order, which keeps the compiler's waits on the in-order load counter exact.
   // A load past the end re-reads the workgroup's first row block (cached), so every load
@@ -729,7 +765,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // wait below covers exactly the loads it needs)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!RT) {
-    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
     load_lr(c0, rb0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -780,7 +816,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
         }
       f4_tile(tp);
     }
-    mfma_result_fence();
+    chain_fence();
     const f32x4_t L = (Lp[2] + Lp[1]) + Lp[0];
     if (c == 0) {
 #pragma unroll
@@ -795,11 +831,11 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     // (row block 0 goes out here with routing: until now the activation and Wr loads of
     // every wave had the CU's memory queue to themselves)
     __builtin_amdgcn_sched_barrier(0);
-    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
   }
   if constexpr (kThreeBuffers) {
     __builtin_amdgcn_sched_barrier(0);
-    load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_par);
+    load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
     load_lr(c1, nbl(1));
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -871,10 +907,15 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       }
     }
   };
-  if (S > 1 && jmax == 1)
-    stream(std::integral_constant<int, 1>{});
-  else
-    stream(std::integral_constant<int, S>{});
+  // one instantiation per slice count read, so the time follows the slices the batch needs
+  // (with the side path, whose registers leave no room for more copies, 1 and S only)
+  if constexpr (S >= 2)
+    if (jmax == 1) return stream(std::integral_constant<int, 1>{});
+  if constexpr (S >= 3 && !LR)
+    if (jmax == 2) return stream(std::integral_constant<int, 2>{});
+  if constexpr (S >= 4 && !LR)
+    if (jmax == 3) return stream(std::integral_constant<int, 3>{});
+  stream(std::integral_constant<int, S>{});
 }
 
 // Sums the k chunks' float32 partials in a fixed order (deterministic) and writes y.
@@ -1080,15 +1121,16 @@ bool decode_route_supported(const mbq_desc& d, int32_t t) {
 
 hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                const float* wr, float* logits, int32_t* budget, int32_t* perm,
-                               int32_t* offsets, void* y, bool y_bf16, hipStream_t stream) {
+                               int32_t* offsets, void* y, bool y_bf16, int mul, hipStream_t stream) {
   const RouteIO rio{wr, logits, budget, perm, offsets};
   const Plan pl = make_plan(d, t, true, false);
   // The fp8 x fp4 multiply saves ~1/4 of a row block's time but its activation split
   // costs every workgroup about two row blocks' worth up front: taken from 4 row blocks
-  // per workgroup and 2 slices on (MBQ_DECODE_F4=1 / =0 forces it on / off).
+  // per workgroup and 2 slices on, unless the caller chooses (mul).
   const int grid = std::min(d.row_blocks, std::max(8, cu_count() & ~7));
   bool f4 = d.slices >= 2 && (d.row_blocks + grid - 1) / grid >= 4;
-  if (const char* e = std::getenv("MBQ_DECODE_F4")) f4 = e[0] == '1';
+  if (mul == MBQ_MUL_BF16) f4 = false;
+  if (mul == MBQ_MUL_FP8_FP4) f4 = true;
   switch (d.group) {
     case 64: return launch_route_g<64>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
     case 128: return launch_route_g<128>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);

@@ -58,9 +58,10 @@ size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool l
 // Decode with the routing in the kernel (bfloat16 x, 1 <= t <= 16, K within one
 // workgroup): writes logits, budget, perm and offsets as launch_route does, and y.
 bool decode_route_supported(const mbq_desc& d, int32_t t);
+// mul: an mbq_mul (MBQ_MUL_AUTO lets the plan choose).
 hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                const float* wr, float* logits, int32_t* budget, int32_t* perm,
-                               int32_t* offsets, void* y, bool y_bf16, hipStream_t stream);
+                               int32_t* offsets, void* y, bool y_bf16, int mul, hipStream_t stream);
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
                                 void* y, bool y_bf16, void* ws, const float* lr_u, int32_t lr_ks,
@@ -69,10 +70,11 @@ hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, cons
                           bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                           bool y_bf16, hipStream_t stream);
 bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_bf16);
+// slots: workgroups the tile plan assumes run at once (0: the device's compute units).
 hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                                bool y_bf16, const float* lr_u, int32_t lr_ks, const uint16_t* lr_b,
-                               int32_t lr_r, hipStream_t stream);
+                               int32_t lr_r, int32_t slots, hipStream_t stream);
 hipError_t launch_lowrank_u(int32_t t, int32_t k, const void* x, bool x_bf16, const uint16_t* a,
                             int32_t rank, float* u, hipStream_t stream);
 int lowrank_u_chunks(int32_t t, int32_t k);

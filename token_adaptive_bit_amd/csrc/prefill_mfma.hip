@@ -28,7 +28,6 @@
 // fenced around half of the dequantization of chunk q + 1, so one wave's VALU work runs
 // in the shadow of the other wave's MFMAs; codes, params and activations of chunk q + 2
 // load during chunk q, so the loop has no load it waits on at once.
-#include <cstdlib>
 
 #include "mbq_internal.h"
 
@@ -578,13 +577,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(TileArgs a, int S, in
   }
 }
 
-// Workgroups of the kernel that run at once: one per CU.  MBQ_PREFILL_SLOTS overrides the
-// count (it only changes which full tiles are halved, never the results' definition).
-int resident_slots() {
-  if (const char* e = std::getenv("MBQ_PREFILL_SLOTS")) {
-    const int v = std::atoi(e);
-    if (v > 0) return v;
-  }
+// Workgroups of the kernel that run at once: one per CU, unless the caller states a count
+// (it only changes which full tiles are halved, never the results' definition).
+int resident_slots(int32_t slots) {
+  if (slots > 0) return slots;
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -603,7 +599,7 @@ bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_
 hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                                bool y_bf16, const float* lr_u, int32_t lr_ks, const uint16_t* lr_b,
-                               int32_t lr_r, hipStream_t stream) {
+                               int32_t lr_r, int32_t slots, hipStream_t stream) {
   const int BM = x_bf16 ? 256 : 128;
   TileArgs a{};
   a.packed = static_cast<const uint8_t*>(packed);
@@ -629,7 +625,7 @@ hipError_t launch_prefill_mfma(const mbq_desc& d, const void* packed, int32_t t,
   const int NT = (d.n + kBN - 1) / kBN;
   // at most ceil(R / BM) tiles per budget group (a half tile replaces a full one), plus
   // the halved ones: at most P / 2, since halving requires 2 (F - P) + H <= P
-  const int P = resident_slots();
+  const int P = resident_slots(slots);
   const int max_tiles = NT * ((t + BM - 1) / BM + d.slices - 1) + P / 2;
   dim3 grid(max_tiles), block(512);
   if (x_bf16)
