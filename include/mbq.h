@@ -269,6 +269,27 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
                       const mbq_opts* opts, hipStream_t stream);
 
 /*
+ * mbq_linear for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same routed linear
+ * (same kernels, same results), with the split-K partials of the streaming decode kept in
+ * a buffer of MBQ_STATIC_SCRATCH_BYTES that the library holds in the device memory of every
+ * GPU it runs on (reserved with the library's code, held until the process ends) instead
+ * of a caller workspace.  The call allocates nothing and frees nothing.
+ *   Arguments as in mbq_linear, without workspace and ws_bytes.
+ *   Returns MBQ_ERR_WORKSPACE, launching nothing, when mbq_linear_workspace() for these
+ *   arguments exceeds MBQ_STATIC_SCRATCH_BYTES (e.g. 64 tokens of a 18944 x 13824 weight).
+ *   The first call on each device resolves that device's buffer address
+ *   (hipGetSymbolAddress, with the device current); MBQ_ERR_DEVICE if that fails.
+ *   All calls on one GPU share its one buffer, which keeps the last call's partials:
+ *   calls that overlap in time on the same GPU (two streams, or two host threads) race,
+ *   and the caller must serialize them.
+ */
+#define MBQ_STATIC_SCRATCH_BYTES (16u << 20)
+mbq_status mbq_linear_static(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                             mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
+                             void* y, mbq_dtype y_dtype, const mbq_opts* opts, hipStream_t stream);
+
+/*
  * One decode step in one call: MoBiRoute (linear-argmax form) and the routed linear
  * (English page sections 2.A, 2.B and 3).  Results are those of mbq_route(t, desc->k,
  * desc->slices, x, x_dtype, wr, logits, budget, perm, offsets) followed by

@@ -291,6 +291,23 @@ def test_linear_validation_and_workspace():
                      packed=None)) == OK
 
 
+def test_linear_static_limits():
+    """The no-allocation linear refuses, before touching a device, any call whose split-K
+    partials exceed the library's static buffer; an empty batch needs none."""
+    assert lib_mod.STATIC_SCRATCH_BYTES == 16 << 20
+    f = P(FAKE)
+    st, d = desc(18944, 13824, 128, 3)     # 64 tokens: 7 chunks x 64 x 18944 x 4 bytes
+    n = ctypes.c_size_t(0)
+    assert L.mbq_linear_workspace(ctypes.byref(d), 64, BF16, ctypes.byref(n)) == OK
+    assert n.value > lib_mod.STATIC_SCRATCH_BYTES
+    assert L.mbq_linear_static(ctypes.byref(d), f, 64, f, BF16, f, f, f, BF16, None, None) == WS
+    assert L.mbq_linear_static(ctypes.byref(d), f, 0, None, BF16, None, None, None, BF16, None, None) == OK
+    assert L.mbq_linear_static(None, f, 16, f, BF16, f, f, f, BF16, None, None) == ARG
+    assert L.mbq_linear_static(ctypes.byref(d), f, -1, f, BF16, f, f, f, BF16, None, None) == SHAPE
+    bad = lib_mod.MbqOpts(0, 0, 0, 7)
+    assert L.mbq_linear_static(ctypes.byref(d), f, 16, f, BF16, f, f, f, BF16, ctypes.byref(bad), None) == ARG
+
+
 @pytest.mark.parametrize("N,K,G,S,t,dt,chunks", [
     (18944, 3584, 128, 3, 16, BF16, 1),   # 14 k tiles: two per wave, one workgroup
     (18944, 3584, 128, 3, 16, F32, 2),    # float32 activations: one tile per wave, 7 + 7

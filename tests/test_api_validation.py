@@ -82,6 +82,8 @@ def test_linear_refuses_mismatch(rec, field, bad, exc):
     g[field] = bad
     with pytest.raises(exc):
         api.linear(packed(), g["x"], g["perm"], g["off"], y=g["y"])
+    with pytest.raises(exc):
+        api.linear_static(packed(), g["x"], g["perm"], g["off"], y=g["y"])
     assert rec.calls == []
 
 

@@ -13,13 +13,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmbq.so")
 
 MBQ_F32, MBQ_BF16 = 0, 1
+STATIC_SCRATCH_BYTES = 16 << 20      # MBQ_STATIC_SCRATCH_BYTES
 ABI_VERSION = 2
 
 STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANGE",
           -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}
 
 EXPORTS = ("mbq_describe", "mbq_pack", "mbq_pack_rows", "mbq_pack_bitplane", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
-           "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_route_linear", "mbq_linear_lowrank_workspace",
+           "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_linear_static", "mbq_route_linear",
+           "mbq_linear_lowrank_workspace",
            "mbq_linear_lowrank", "mbq_status_str", "mbq_abi_version")
 
 
@@ -78,6 +80,7 @@ def _load() -> ctypes.CDLL:
     lib.mbq_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
     O = P(MbqOpts)
     lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, O, VP]
+    lib.mbq_linear_static.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, O, VP]
     lib.mbq_route_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP,
                                      ctypes.c_size_t, O, VP]
     lib.mbq_linear_lowrank_workspace.argtypes = [D, I32, I32, I32, P(ctypes.c_size_t)]

@@ -19,7 +19,7 @@ from ._lib import (MBQ_BF16, MBQ_F32, MBQ_MUL_AUTO, MBQ_MUL_BF16, MBQ_MUL_FP8_FP
 __all__ = ["PackedLinear", "pack", "pack_bitplane", "pack_concat", "route", "route_from_logits", "regroup", "linear",
            "linear_workspace", "describe", "MbqError", "MlpRouter", "route_mlp",
            "route_mlp_from_scores", "route_mlp_workspace", "linear_lowrank",
-           "linear_lowrank_workspace", "route_linear", "opts"]
+           "linear_lowrank_workspace", "route_linear", "linear_static", "opts"]
 
 _FLOATS = (torch.float32, torch.bfloat16)
 
@@ -364,6 +364,18 @@ def linear(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets: torch.
     check(_lib.LIB.mbq_linear(ctypes.byref(p.desc), _p(p.blob), t, _p(x), _dtype(x), _p(perm),
                               _p(offsets), _p(y), _dtype(y), _p(workspace), ws_bytes, _optp(options),
                               _stream()), "mbq_linear")
+    return y
+
+
+def linear_static(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor,
+                  out_dtype: torch.dtype | None = None, y: torch.Tensor | None = None,
+                  options: MbqOpts | None = None) -> torch.Tensor:
+    """The routed linear without a workspace (mbq_linear_static): for callers that cannot
+    allocate; y must then be given.  Calls that overlap on one GPU race (one shared buffer)."""
+    t, y = _linear_args(p, x, perm, offsets, out_dtype, y)
+    check(_lib.LIB.mbq_linear_static(ctypes.byref(p.desc), _p(p.blob), t, _p(x), _dtype(x), _p(perm),
+                                     _p(offsets), _p(y), _dtype(y), _optp(options), _stream()),
+          "mbq_linear_static")
     return y
 
 

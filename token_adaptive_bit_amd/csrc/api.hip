@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "mbq_internal.h"
 
@@ -271,6 +272,33 @@ mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, cons
   return launched(mbq::launch_lowrank_update(t, desc->n, u, ksu, b, rank, y, yb, stream));
 }
 
+// The buffer of mbq_linear_static: file-scope device memory, one copy on every GPU the
+// library runs on.  In host code `scratch` names a host-side stand-in, not a device
+// address: its address on a device comes from hipGetSymbolAddress with that device
+// current, resolved once per device and kept here; only that pointer reaches a kernel.
+constexpr size_t kStaticScratchBytes = MBQ_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+mbq_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MBQ_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      if (std::getenv("MBQ_DEBUG")) std::fprintf(stderr, "libmbq: hipGetSymbolAddress failed: %s\n", hipGetErrorString(e));
+      return MBQ_ERR_DEVICE;
+    }
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MBQ_OK;
+}
+
 }  // namespace
 
 mbq_status mbq_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
@@ -289,6 +317,25 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
                       const mbq_opts* opts, hipStream_t stream) {
   return linear_impl(desc, packed, t, x, x_dtype, perm, offsets, nullptr, nullptr, 0, y, y_dtype,
                      workspace, ws_bytes, opts, stream);
+}
+
+mbq_status mbq_linear_static(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
+                             mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
+                             void* y, mbq_dtype y_dtype, const mbq_opts* opts, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (!checked_opts(opts)) return MBQ_ERR_ARG;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
+  const size_t need = t > 0 ? linear_ws(*desc, t, x_dtype == MBQ_BF16, false) : 0;
+  if (need > kStaticScratchBytes) return MBQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = static_scratch(&ws);
+    if (st != MBQ_OK) return st;
+  }
+  return linear_impl(desc, packed, t, x, x_dtype, perm, offsets, nullptr, nullptr, 0, y, y_dtype, ws,
+                     need > 0 ? kStaticScratchBytes : 0, opts, stream);
 }
 
 mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
