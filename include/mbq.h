@@ -82,12 +82,14 @@ typedef enum {
 } mbq_mul;
 
 typedef struct {
-  int32_t path;           /* mbq_path */
-  int32_t decode_mul;     /* mbq_mul of the one-launch decode step (mbq_route_linear) */
-  int32_t prefill_slots;  /* workgroups the MFMA prefill's tile plan assumes run at once
-                             (0: the device's compute units); it decides which full tiles are
-                             split in two, never the results */
-  int32_t reserved;       /* 0 */
+  int32_t path;            /* mbq_path */
+  int32_t decode_mul;      /* mbq_mul of the routed decode step (mbq_route_linear) */
+  int32_t prefill_slots;   /* workgroups the MFMA prefill's tile plan assumes run at once
+                              (0: the device's compute units); it decides which full tiles are
+                              split in two, never the results */
+  int32_t decode_launches; /* launches of the fp8 x fp4 decode step (mbq_route_linear): 0 the
+                              plan's choice, 1 one, 2 two (operands prepared once, in the
+                              workspace) */
 } mbq_opts;
 
 /*
@@ -288,6 +290,12 @@ mbq_status mbq_linear(const mbq_desc* desc, const void* packed, int32_t t, const
 mbq_status mbq_linear_static(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                              mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                              void* y, mbq_dtype y_dtype, const mbq_opts* opts, hipStream_t stream);
+
+/* Host only: bytes of device workspace mbq_route_linear can use for t tokens: the
+ * prepared operands of its two-launch fp8 x fp4 step (see there), or the routed linear's
+ * (mbq_linear_workspace), whichever is larger.  Depends only on desc, t and x_dtype. */
+mbq_status mbq_route_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
+                                      size_t* bytes);
 
 /*
  * One decode step in one call: MoBiRoute (linear-argmax form) and the routed linear

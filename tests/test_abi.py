@@ -190,6 +190,12 @@ def test_route_linear_validation():
     assert call(off=None) == ARG
     assert call(o=ctypes.byref(lib_mod.MbqOpts(0, 5, 0, 0))) == ARG
     assert call(o=ctypes.byref(lib_mod.MbqOpts(3, 0, 0, 0))) == ARG
+    # two launches need the prepared operands' workspace (mbq_route_linear_workspace)
+    n = ctypes.c_size_t(0)
+    assert L.mbq_route_linear_workspace(dp, 16, BF16, ctypes.byref(n)) == OK
+    assert n.value == 3 * (8192 + 512 + 2 * 64 + 256)     # 3 k tiles of 256 inputs, group 128
+    assert call(o=ctypes.byref(lib_mod.MbqOpts(0, 2, 0, 2))) == WS
+    assert L.mbq_route_linear_workspace(dp, 16, F32, ctypes.byref(n)) == OK and n.value == 0
     for k in ("packed", "x", "wr", "lg", "b", "perm", "y"):
         assert call(**{k: None}) == ARG, k
     assert call(packed=P(FAKE + 64)) == ARG
@@ -284,7 +290,7 @@ def test_linear_validation_and_workspace():
     # kernel choices: a field out of range is an argument error, found before any launch
     Opts = lib_mod.MbqOpts
     for o in (Opts(2, 0, 0, 0), Opts(-1, 0, 0, 0), Opts(0, 3, 0, 0), Opts(0, -1, 0, 0),
-              Opts(0, 0, -1, 0), Opts(0, 0, 0, 1)):
+              Opts(0, 0, -1, 0), Opts(0, 0, 0, 3), Opts(0, 0, 0, -1)):
         assert call(args(o=ctypes.byref(o))) == ARG
         assert call(args(o=ctypes.byref(o), t=0, x=None, perm=None, off=None, y=None, packed=None)) == ARG
     assert call(args(o=ctypes.byref(Opts(1, 2, 300, 0)), t=0, x=None, perm=None, off=None, y=None,
@@ -304,7 +310,7 @@ def test_linear_static_limits():
     assert L.mbq_linear_static(ctypes.byref(d), f, 0, None, BF16, None, None, None, BF16, None, None) == OK
     assert L.mbq_linear_static(None, f, 16, f, BF16, f, f, f, BF16, None, None) == ARG
     assert L.mbq_linear_static(ctypes.byref(d), f, -1, f, BF16, f, f, f, BF16, None, None) == SHAPE
-    bad = lib_mod.MbqOpts(0, 0, 0, 7)
+    bad = lib_mod.MbqOpts(0, 0, 0, 7)      # decode_launches out of range
     assert L.mbq_linear_static(ctypes.byref(d), f, 16, f, BF16, f, f, f, BF16, ctypes.byref(bad), None) == ARG
 
 

@@ -14,7 +14,7 @@ from token_adaptive_bit_amd import _lib, api   # noqa: E402
 
 
 class Recorder:
-    HOST = {"mbq_describe", "mbq_linear_workspace", "mbq_linear_lowrank_workspace",
+    HOST = {"mbq_describe", "mbq_linear_workspace", "mbq_linear_lowrank_workspace", "mbq_route_linear_workspace",
             "mbq_route_mlp_workspace", "mbq_status_str", "mbq_abi_version"}
 
     def __init__(self, lib):
@@ -153,8 +153,8 @@ def test_pack_refuses_bad_weights(rec):
 
 
 def test_opts_values():
-    o = api.opts(path="generic", decode_mul="fp8fp4", prefill_slots=12)
-    assert (o.path, o.decode_mul, o.prefill_slots, o.reserved) == (1, 2, 12, 0)
-    for kw in (dict(path="fast"), dict(decode_mul="fp8"), dict(prefill_slots=-1)):
+    o = api.opts(path="generic", decode_mul="fp8fp4", prefill_slots=12, decode_launches=2)
+    assert (o.path, o.decode_mul, o.prefill_slots, o.decode_launches) == (1, 2, 12, 2)
+    for kw in (dict(path="fast"), dict(decode_mul="fp8"), dict(prefill_slots=-1), dict(decode_launches=3)):
         with pytest.raises(ValueError):
             api.opts(**kw)

@@ -94,15 +94,15 @@ def test_cfg2_blob_bitexact(cfg2):
 
 
 @pytest.mark.parametrize("T", [1, 4, 16])
-@pytest.mark.parametrize("mul", [None, "bf16", "fp8fp4"])
-def test_cfg2_route_linear_every_row(mbq, cfg2, T, mul):
+@pytest.mark.parametrize("mul,launches", [(None, 0), ("bf16", 1), ("fp8fp4", 1), ("fp8fp4", 2)])
+def test_cfg2_route_linear_every_row(mbq, cfg2, T, mul, launches):
     """The decode step in one call (the benchmark's step) on the workload's own inputs, on
-    the plan's multiply and on each multiply forced."""
+    the plan's choices and on each multiply and launch count forced."""
     d, pw = cfg2
-    say(f"cfg2 route_linear T={T} decode_mul={mul}")
+    say(f"cfg2 route_linear T={T} decode_mul={mul} launches={launches}")
     X = d["X"][:T]
     y, lg, b, perm, off = mbq.route_linear(pw.p, to_dev(X, torch.bfloat16), to_dev(d["Wr"], torch.float32),
-                                           options=mbq.opts(decode_mul=mul))
+                                           options=mbq.opts(decode_mul=mul, decode_launches=launches))
     torch.cuda.synchronize()
     wb = check_routes(lg, b, perm, off, X, d["Wr"], 3)
     compare(y, pw.yref(X, wb), what=f"T={T} {mul}")

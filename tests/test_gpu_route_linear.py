@@ -42,16 +42,17 @@ def tdt(name):
     return torch.bfloat16 if name == "bf16" else torch.float32
 
 
-def run_case(mbq, N, K, G, S, T, dtype, seed, rows=None, f4=False, mul="bf16", d=None):
-    """mul: the one-launch step's multiply (decode_mul; None lets the plan choose); f4: the
-    call is expected to take the fp8 x fp4 multiply."""
+def run_case(mbq, N, K, G, S, T, dtype, seed, rows=None, f4=False, mul="bf16", d=None, launches=0):
+    """mul: the routed step's multiply (decode_mul; None lets the plan choose); f4: the
+    call is expected to take the fp8 x fp4 multiply; launches: decode_launches (0 lets the
+    plan choose, 2 prepares the fp8 operands once in a first launch)."""
     if d is None:
         d = inputs.make_linear(seed, N, K, T, group=G, slices=S, dtype=dtype)
     x = to_dev(d["X"][:T], tdt(dtype))
     wr = to_dev(d["Wr"], torch.float32)
     p = mbq.pack(to_dev(d["W"], tdt(dtype)), group=G, slices=S)
     y, lg, b, perm, off = mbq.route_linear(p, x, wr, out_dtype=torch.float32,
-                                           options=mbq.opts(decode_mul=mul))
+                                           options=mbq.opts(decode_mul=mul, decode_launches=launches))
     # the two-call path on the same inputs
     lg2, b2, perm2, off2 = mbq.route(x, wr)
     y2 = mbq.linear(p, x, perm2, off2, out_dtype=torch.float32)
@@ -110,27 +111,33 @@ def test_route_linear_parity(mbq, N, K, G, S, T, dtype):
     run_case(mbq, N, K, G, S, T, dtype, seed=N + 7 * T)
 
 
+@pytest.mark.parametrize("launches", [1, 2])
 @pytest.mark.parametrize("N,K,G,S,T,dtype", FUSED)
-def test_route_linear_parity_f4(mbq, N, K, G, S, T, dtype):
-    """The same cases on the fp8 x fp4 multiply (forced on; one slice keeps bf16)."""
-    say(f"route_linear f4 N={N} K={K} G={G} S={S} T={T}")
-    run_case(mbq, N, K, G, S, T, dtype, seed=N + 7 * T, f4=S > 1, mul="fp8fp4")
+def test_route_linear_parity_f4(mbq, N, K, G, S, T, dtype, launches):
+    """The same cases on the fp8 x fp4 multiply (forced on; one slice keeps bf16), in one
+    launch and in two (operands prepared once)."""
+    say(f"route_linear f4 N={N} K={K} G={G} S={S} T={T} launches={launches}")
+    run_case(mbq, N, K, G, S, T, dtype, seed=N + 7 * T, f4=S > 1, mul="fp8fp4", launches=launches)
 
 
 @pytest.mark.parametrize("G", [64, 128, 256])
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
-@pytest.mark.parametrize("f4", [False, True])
-def test_route_linear_every_variant(mbq, G, S, f4):
-    """Every group / slice count of the in-kernel routing, with two k tiles per wave
-    (K = 2560: 10 tiles over 8 waves) and a router that mixes budgets, on either multiply."""
-    say(f"route_linear variant G={G} S={S} f4={f4}")
-    run_case(mbq, 80, 2560, G, S, 16, "bf16", seed=G + S, f4=f4 and S > 1, mul="fp8fp4" if f4 else "bf16")
+@pytest.mark.parametrize("mode", ["bf16", "f4_one", "f4_two"])
+def test_route_linear_every_variant(mbq, G, S, mode):
+    """Every group / slice count of the routed step, with two k tiles per wave (K = 2560:
+    10 tiles over 8 waves) and a router that mixes budgets, on the bf16 multiply and on the
+    fp8 x fp4 one in one launch and in two."""
+    say(f"route_linear variant G={G} S={S} {mode}")
+    f4 = mode != "bf16"
+    run_case(mbq, 80, 2560, G, S, 16, "bf16", seed=G + S, f4=f4 and S > 1, mul="fp8fp4" if f4 else "bf16",
+             launches={"bf16": 1, "f4_one": 1, "f4_two": 2}[mode])
 
 
 @pytest.mark.parametrize("f4", [False, True])
 def test_route_linear_one_tile_per_wave(mbq, f4):
-    """K of 8 tiles: one tile per wave."""
-    run_case(mbq, 120, 2048, 128, 3, 16, "bf16", seed=3, f4=f4, mul="fp8fp4" if f4 else "bf16")
+    """K of 8 tiles: one tile per wave (the fp8 x fp4 multiply in two launches)."""
+    run_case(mbq, 120, 2048, 128, 3, 16, "bf16", seed=3, f4=f4, mul="fp8fp4" if f4 else "bf16",
+             launches=2 if f4 else 1)
 
 
 def test_route_linear_uniform_budgets(mbq):

@@ -21,6 +21,7 @@ STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANG
 
 EXPORTS = ("mbq_describe", "mbq_pack", "mbq_pack_rows", "mbq_pack_bitplane", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
            "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_linear_static", "mbq_route_linear",
+           "mbq_route_linear_workspace",
            "mbq_linear_lowrank_workspace",
            "mbq_linear_lowrank", "mbq_status_str", "mbq_abi_version")
 
@@ -45,7 +46,7 @@ MBQ_MUL_AUTO, MBQ_MUL_BF16, MBQ_MUL_FP8_FP4 = 0, 1, 2
 class MbqOpts(ctypes.Structure):
     """Kernel and tiling choices of the routed linear (mbq_opts in include/mbq.h)."""
     _fields_ = [("path", ctypes.c_int32), ("decode_mul", ctypes.c_int32),
-                ("prefill_slots", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("prefill_slots", ctypes.c_int32), ("decode_launches", ctypes.c_int32)]
 
 
 class MbqError(RuntimeError):
@@ -80,6 +81,7 @@ def _load() -> ctypes.CDLL:
     lib.mbq_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
     O = P(MbqOpts)
     lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, O, VP]
+    lib.mbq_route_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
     lib.mbq_linear_static.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, O, VP]
     lib.mbq_route_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP,
                                      ctypes.c_size_t, O, VP]
@@ -119,6 +121,13 @@ def workspace_bytes(desc: MbqDesc, t: int, x_dtype: int) -> int:
     n = ctypes.c_size_t(0)
     check(LIB.mbq_linear_workspace(ctypes.byref(desc), t, x_dtype, ctypes.byref(n)),
           "mbq_linear_workspace")
+    return int(n.value)
+
+
+def route_linear_workspace_bytes(desc: MbqDesc, t: int, x_dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    check(LIB.mbq_route_linear_workspace(ctypes.byref(desc), t, x_dtype, ctypes.byref(n)),
+          "mbq_route_linear_workspace")
     return int(n.value)
 
 

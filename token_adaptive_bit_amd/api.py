@@ -19,7 +19,7 @@ from ._lib import (MBQ_BF16, MBQ_F32, MBQ_MUL_AUTO, MBQ_MUL_BF16, MBQ_MUL_FP8_FP
 __all__ = ["PackedLinear", "pack", "pack_bitplane", "pack_concat", "route", "route_from_logits", "regroup", "linear",
            "linear_workspace", "describe", "MbqError", "MlpRouter", "route_mlp",
            "route_mlp_from_scores", "route_mlp_workspace", "linear_lowrank",
-           "linear_lowrank_workspace", "route_linear", "linear_static", "opts"]
+           "linear_lowrank_workspace", "route_linear", "route_linear_workspace", "linear_static", "opts"]
 
 _FLOATS = (torch.float32, torch.bfloat16)
 
@@ -81,17 +81,21 @@ _PATHS = {None: MBQ_PATH_AUTO, "auto": MBQ_PATH_AUTO, "generic": MBQ_PATH_GENERI
 _MULS = {None: MBQ_MUL_AUTO, "auto": MBQ_MUL_AUTO, "bf16": MBQ_MUL_BF16, "fp8fp4": MBQ_MUL_FP8_FP4}
 
 
-def opts(path: str | None = None, decode_mul: str | None = None, prefill_slots: int = 0) -> MbqOpts:
+def opts(path: str | None = None, decode_mul: str | None = None, prefill_slots: int = 0,
+         decode_launches: int = 0) -> MbqOpts:
     """Kernel choices (mbq_opts): path 'auto' | 'generic'; decode_mul 'auto' | 'bf16' |
-    'fp8fp4' (the one-launch decode step's multiply); prefill_slots, the workgroups the
-    MFMA prefill's tile plan assumes run at once (0: the device's compute units)."""
+    'fp8fp4' (the routed decode step's multiply); prefill_slots, the workgroups the MFMA
+    prefill's tile plan assumes run at once (0: the device's compute units);
+    decode_launches 0 (the plan's choice), 1 or 2 for the fp8 x fp4 decode step."""
     if path not in _PATHS:
         raise ValueError(f"path must be one of {sorted(k for k in _PATHS if k)}")
     if decode_mul not in _MULS:
         raise ValueError(f"decode_mul must be one of {sorted(k for k in _MULS if k)}")
     if int(prefill_slots) < 0:
         raise ValueError("prefill_slots must be >= 0")
-    return MbqOpts(_PATHS[path], _MULS[decode_mul], int(prefill_slots), 0)
+    if int(decode_launches) not in (0, 1, 2):
+        raise ValueError("decode_launches must be 0, 1 or 2")
+    return MbqOpts(_PATHS[path], _MULS[decode_mul], int(prefill_slots), int(decode_launches))
 
 
 def _optp(o: MbqOpts | None):
@@ -379,6 +383,10 @@ def linear_static(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets:
     return y
 
 
+def route_linear_workspace(p: PackedLinear, t: int, x_dtype=torch.bfloat16) -> int:
+    return _lib.route_linear_workspace_bytes(p.desc, t, MBQ_BF16 if x_dtype == torch.bfloat16 else MBQ_F32)
+
+
 def route_linear(p: PackedLinear, x: torch.Tensor, wr: torch.Tensor, out_dtype: torch.dtype | None = None,
                  y: torch.Tensor | None = None, logits=None, budget=None, perm=None, offsets=None,
                  workspace: torch.Tensor | None = None, options: MbqOpts | None = None):
@@ -399,7 +407,7 @@ def route_linear(p: PackedLinear, x: torch.Tensor, wr: torch.Tensor, out_dtype: 
         y = torch.empty((t, p.n), dtype=out_dtype, device=dev)
     _arg(y, "y", (t, p.n), _FLOATS, dev)
     logits, budget, perm, offsets = _route_outputs(t, s, dev, logits, budget, perm, offsets)
-    need = linear_workspace(p, t, x.dtype)
+    need = route_linear_workspace(p, t, x.dtype)
     _workspace(workspace, "workspace", need, dev)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

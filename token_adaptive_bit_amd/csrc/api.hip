@@ -220,7 +220,7 @@ const mbq_opts* checked_opts(const mbq_opts* o) {
   if (!o) return &kDefaultOpts;
   if (o->path < MBQ_PATH_AUTO || o->path > MBQ_PATH_GENERIC) return nullptr;
   if (o->decode_mul < MBQ_MUL_AUTO || o->decode_mul > MBQ_MUL_FP8_FP4) return nullptr;
-  if (o->prefill_slots < 0 || o->reserved != 0) return nullptr;
+  if (o->prefill_slots < 0 || o->decode_launches < 0 || o->decode_launches > 2) return nullptr;
   return o;
 }
 
@@ -356,14 +356,27 @@ mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t,
     if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) ||
         !aligned(budget, 4) || !aligned(perm, 4) || !aligned(offsets, 4))
       return MBQ_ERR_ARG;
+    if (workspace && !aligned(workspace, 16)) return MBQ_ERR_WORKSPACE;
+    if (opts->decode_launches == 2 && ws_bytes < mbq::decode_route_workspace(*desc, t)) return MBQ_ERR_WORKSPACE;
     if (aligned(wr, 16))
       return launched(mbq::launch_decode_route(*desc, packed, t, x, wr, logits, budget, perm, offsets,
-                                               y, y_dtype == MBQ_BF16, opts->decode_mul, stream));
+                                               y, y_dtype == MBQ_BF16, opts->decode_mul,
+                                               opts->decode_launches, workspace, ws_bytes, stream));
   }
   st = mbq_route(t, desc->k, desc->slices, x, x_dtype, wr, logits, budget, perm, offsets, stream);
   if (st != MBQ_OK) return st;
   return mbq_linear(desc, packed, t, x, x_dtype, perm, offsets, y, y_dtype, workspace, ws_bytes, opts,
                     stream);
+}
+
+mbq_status mbq_route_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype, size_t* bytes) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (!bytes || !valid_dtype(x_dtype)) return MBQ_ERR_ARG;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  const size_t lin = linear_ws(*desc, t, x_dtype == MBQ_BF16, false);
+  *bytes = x_dtype == MBQ_BF16 ? std::max(lin, mbq::decode_route_workspace(*desc, t)) : lin;
+  return MBQ_OK;
 }
 
 mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,

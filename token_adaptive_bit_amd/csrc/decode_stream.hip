@@ -270,9 +270,27 @@ struct RouteIO {
   int32_t* budget;  // [T]
   int32_t* perm;    // [T]
   int32_t* offsets; // [S + 1]
+  const uint8_t* prep;  // PA: decode_prep_kernel's output (layout: PrepLayout)
 };
 
-template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT, bool F4>
+// The prepared activations of one decode step (PA; written by decode_prep_kernel, one
+// record per k tile of 256 inputs, 16 tokens): the fp8 x fp4 multiply's A operands as
+// register images (8 chunks of 64 lanes x 16 bytes: e4m3 hi of block 0, lo of block 0, hi
+// of block 1, lo of block 1, two chunks each), their e8m0 scales (64 lanes x 2 words),
+// the per-group activation sums (GPT x 16 floats) and the tile's partial router logits
+// (16 tokens x 4 floats).  Sections are contiguous over the k tiles.
+struct PrepLayout {
+  uint32_t a, sc, xs, lg, bytes;
+  __host__ __device__ PrepLayout(int KB, int G) {
+    a = 0;
+    sc = a + uint32_t(KB) * 8192u;
+    xs = sc + uint32_t(KB) * 512u;
+    lg = xs + uint32_t(KB) * uint32_t(256 / G) * 64u;
+    bytes = lg + uint32_t(KB) * 256u;
+  }
+};
+
+template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT, bool F4, bool PA = false>
 __global__ __launch_bounds__(512) void decode_stream_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, uint64_t ss,
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
@@ -282,6 +300,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   static_assert(!LR || TB == 1, "the side path is built for one token block per workgroup");
   static_assert(!RT || (TB == 1 && !LR), "in-kernel routing takes one token block, no side path");
   static_assert(!F4 || (NA == 1 && TB == 1 && !LR), "fp4 operands: bfloat16 activations, one token block");
+  static_assert(!PA || (RT && F4), "prepared activations: the routed fp8 x fp4 step");
   // Every kernel argument is read in one batch behind one wait: loaded lazily, they come
   // from up to three scalar cache lines in turn, each a round trip before the first
   // activation load can be issued.
@@ -289,6 +308,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   asm volatile("" ::"s"(N), "s"(K), "s"(KB), "s"(NG), "s"(NB), "s"(ss), "s"(po), "s"(T), "s"(y_bf16),
                "s"(kchunk), "s"(lr_ks), "s"(lr_r));
   if constexpr (RT) asm volatile("" ::"s"(rio.wr), "s"(rio.logits), "s"(rio.budget), "s"(rio.perm), "s"(rio.offsets));
+  if constexpr (PA) asm volatile("" ::"s"(rio.prep));
   constexpr int GPT = 256 / G, WPG = G / 64;
   __shared__ f32x4_t red[2][kMaxWaves][TB][64];
   const int NW = blockDim.x >> 6;
@@ -380,7 +400,40 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // second one's loads are still arriving (Wr ahead of the activations delays what
   // everything else waits for); rows past K read zeros
   u32x4_t wld[RT ? TPW : 1][RT ? S : 1];
-  if constexpr (RT) {
+  // PA: the prepared operands of this wave's tiles instead (16-byte loads, 1 KiB of
+  // consecutive bytes per instruction); a tile the wave does not have reads zeros
+  u32x4_t pa_x[PA ? TPW : 1][8];
+  uint32_t pa_sc[PA ? TPW : 1][2], pa_xs[PA ? TPW : 1];
+  u32x4_t pa_lg[PA ? TPW : 1];
+  if constexpr (PA) {
+    const PrepLayout pl(KB, G);
+    const __amdgpu_buffer_rsrc_t ra = slice_rsrc(rio.prep + pl.a, pl.sc - pl.a);
+    const __amdgpu_buffer_rsrc_t rsc = slice_rsrc(rio.prep + pl.sc, pl.xs - pl.sc);
+    const __amdgpu_buffer_rsrc_t rxs = slice_rsrc(rio.prep + pl.xs, pl.lg - pl.xs);
+    const __amdgpu_buffer_rsrc_t rlg = slice_rsrc(rio.prep + pl.lg, pl.bytes - pl.lg);
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp) {
+      const uint32_t t = uint32_t(kt[tp]), none = 0x80000000u;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        pa_x[tp][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                          ra, live[tp] ? ((t * 8 + q) * 64 + lane) * 16 : none, 0, 0));
+      const auto scv = __builtin_amdgcn_raw_buffer_load_b64(rsc, live[tp] ? (t * 64 + lane) * 8 : none, 0, 0);
+      pa_sc[tp][0] = uint32_t(scv[0]);
+      pa_sc[tp][1] = uint32_t(scv[1]);
+      pa_xs[tp] = __builtin_amdgcn_raw_buffer_load_b32(rxs, live[tp] && lane < 16 * GPT ? (t * GPT * 16 + lane) * 4 : none, 0, 0);
+      pa_lg[tp] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                      rlg, live[tp] && lane < 16 ? (t * 16 + lane) * 16 : none, 0, 0));
+    }
+    // Row blocks 0 and 1 go out once every wave of the workgroup has issued its prepared
+    // loads (a barrier on the issue, not the data): the second wave on each SIMD can issue
+    // only when the first one's loads return, and codes queued in front of it would delay
+    // its operands by another round trip.  Every slice's range: the budgets are not known
+    // yet, and slices past jmax add nothing (no budget reaches them).
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (RT) {
     const __amdgpu_buffer_rsrc_t rw = slice_rsrc(reinterpret_cast<const uint8_t*>(rio.wr), uint32_t(K) * S * 4);
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp) {
@@ -769,9 +822,40 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     load_lr(c0, rb0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (RT) {
-    // Row blocks 0 and 1 go out after this, before the budgets are known, with every
-    // slice's range; slices past jmax add nothing there, since no budget reaches them.
+  if constexpr (PA) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kThreeBuffers) load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+    __builtin_amdgcn_sched_barrier(0);
+    // the prepared operands as they are: A images and scales into the fp8 registers, the
+    // group sums into the wave's LDS table, the tiles' partial logits added in tile order
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          af[tp][m].hi[e] = int(pa_x[tp][4 * m][e]);
+          af[tp][m].hi[4 + e] = int(pa_x[tp][4 * m + 1][e]);
+          af[tp][m].lo[e] = int(pa_x[tp][4 * m + 2][e]);
+          af[tp][m].lo[4 + e] = int(pa_x[tp][4 * m + 3][e]);
+        }
+        af[tp][m].sc = pa_sc[tp][m];
+      }
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+      if (lane < 16 * GPT) xsT[wave][0][tp * GPT + (lane >> 4)][lane & 15] = __uint_as_float(pa_xs[tp]);
+    if (lane < 16) {
+      f32x4_t lg4 = __builtin_bit_cast(f32x4_t, pa_lg[0]);
+#pragma unroll
+      for (int tp = 1; tp < TPW; ++tp) lg4 += __builtin_bit_cast(f32x4_t, pa_lg[tp]);
+#pragma unroll
+      for (int j = 0; j < S; ++j) lgp[wave][lane][j] = lg4[j];
+    }
+  } else if constexpr (RT) {
+    // Row blocks 0 and 1 go out in here, before the budgets are known, with every slice's
+    // range; slices past jmax add nothing there, since no budget reaches them.
     // Wr as three bfloat16 planes (hi + mid + lo = the float32 value: each plane takes the
     // previous one's exact remainder), column-major per tile: wrp[wave][tile][plane][j][k]
     // logits^T = Wr^T x^T on the matrix cores: the activation registers (lane (r, c): token r,
@@ -805,6 +889,20 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           wrp[wave][tp][1][(f + 1) % S][(f + 1) / S] = uint16_t(p1 >> 16);
           wrp[wave][tp][2][(f + 1) % S][(f + 1) / S] = uint16_t(p2 >> 16);
         }
+      // Row blocks 0 and 1 go out once this tile's activations and Wr rows are in (the
+      // planes above waited for them), so their HBM round trip runs under the routing
+      // MFMAs and the fp8 split; issued earlier, in front of the activation loads of the
+      // CU's other waves, they would delay those by a round trip.
+      if (tp == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kThreeBuffers && tp == TPW - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -827,13 +925,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     setup_zero();
     setup_a();
   }
-  if constexpr (RT) {
-    // (row block 0 goes out here with routing: until now the activation and Wr loads of
-    // every wave had the CU's memory queue to themselves)
-    __builtin_amdgcn_sched_barrier(0);
-    load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
-  }
-  if constexpr (kThreeBuffers) {
+  if constexpr (kThreeBuffers && !RT) {
     __builtin_amdgcn_sched_barrier(0);
     load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
     load_lr(c1, nbl(1));
@@ -918,6 +1010,108 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   stream(std::integral_constant<int, S>{});
 }
 
+// The first launch of the two-launch decode step (PA): one wave per k tile of 256 inputs
+// prepares what every workgroup of the streaming kernel would otherwise derive from the
+// raw activations on its own: the tile's fp8 A operands (prep_a_f4), their group sums
+// (the same instruction against all-ones codes) and the tile's partial router logits
+// (Wr as three exact bfloat16 planes on the bf16 matrix instruction, as in the in-kernel
+// routing).  bfloat16 x [t x K], t <= 16; tokens past t repeat the last one (their rows
+// are never used).  Output layout: PrepLayout.
+template <int G, int S>
+__global__ __launch_bounds__(64) void decode_prep_kernel(const uint8_t* __restrict__ x, int T, int K, int KB,
+                                                         const float* __restrict__ wr, uint8_t* __restrict__ prep) {
+  asm volatile("" ::"s"(x), "s"(wr), "s"(prep), "s"(T), "s"(K), "s"(KB));
+  constexpr int GPT = 256 / G;
+  const int t = blockIdx.x, lane = threadIdx.x, r = lane & 15, c = lane >> 4;
+  const int xr = min(r, T - 1);
+  auto xk = [&](int i, int h) { return 128 * (i >> 1) + 64 * (c & 1) + 16 * (c >> 1) + 32 * (i & 1) + 8 * h; };
+  u32x4_t a[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = t * 256 + xk(i, h);
+      a[i][h] = ldg16(x + (size_t(xr) * K + (k < K ? k : 0)) * 2);   // past K: zeroed below
+    }
+  const __amdgpu_buffer_rsrc_t rw = slice_rsrc(reinterpret_cast<const uint8_t*>(wr), uint32_t(K) * S * 4);
+  u32x4_t wl[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q)
+    wl[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t(t) * 256 * S + (64 * q + lane) * 4) * 4, 0, 0));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (t * 256 + xk(i, h) >= K) a[i][h] = u32x4_t{0u, 0u, 0u, 0u};
+  // Wr rows of the tile as three bf16 planes, column-major (plane, logit, input), in LDS;
+  // logits^T = Wr^T x^T with the activations as the B operand (see the in-kernel routing)
+  __shared__ __align__(16) uint16_t wrp[3][4][256 + 8];
+#pragma unroll
+  for (int q = 0; q < S; ++q)
+#pragma unroll
+    for (int u = 0; u < 4; u += 2) {
+      const int f = 4 * (64 * q + lane) + u;
+      const float a0 = __uint_as_float(wl[q][u]), b0 = __uint_as_float(wl[q][u + 1]);
+      const uint32_t p0 = pk_bf16(a0, b0);
+      const float a1 = a0 - __uint_as_float(p0 << 16), b1 = b0 - __uint_as_float(p0 & 0xFFFF0000u);
+      const uint32_t p1 = pk_bf16(a1, b1);
+      const uint32_t p2 = pk_bf16(a1 - __uint_as_float(p1 << 16), b1 - __uint_as_float(p1 & 0xFFFF0000u));
+      wrp[0][f % S][f / S] = uint16_t(p0);
+      wrp[1][f % S][f / S] = uint16_t(p1);
+      wrp[2][f % S][f / S] = uint16_t(p2);
+      wrp[0][(f + 1) % S][(f + 1) / S] = uint16_t(p0 >> 16);
+      wrp[1][(f + 1) % S][(f + 1) / S] = uint16_t(p1 >> 16);
+      wrp[2][(f + 1) % S][(f + 1) / S] = uint16_t(p2 >> 16);
+    }
+  const int jr = min(r & 3, S - 1);
+  f32x4_t Lp[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+        Lp[pl] = mfma(*reinterpret_cast<const u32x4_t*>(&wrp[pl][jr][xk(i, h)]), a[i][h], Lp[pl]);
+  // fp8 pairs and scales of the two 128-input blocks, then their group sums
+  AF4 af[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) af[m] = prep_a_f4(a[2 * m][0], a[2 * m][1], a[2 * m + 1][0], a[2 * m + 1][1]);
+  constexpr uint32_t kOne4 = 0x22222222u;
+  f32x4_t xs[GPT];
+#pragma unroll
+  for (int gi = 0; gi < GPT; ++gi) {
+    xs[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (G == 64 && m != (gi >> 1)) continue;
+      if (G == 128 && m != gi) continue;
+      const uint32_t lo = (G == 64 && (gi & 1)) ? 0u : kOne4, hi = (G == 64 && !(gi & 1)) ? 0u : kOne4;
+      const uint32_t ones[4] = {lo, lo, hi, hi};
+      xs[gi] = mfma_f4<127>(af[m].hi, ones, af[m].sc, xs[gi]);
+      xs[gi] = mfma_f4<127>(af[m].lo, ones, af[m].sc, xs[gi]);
+    }
+  }
+  chain_fence();
+  const f32x4_t L = (Lp[2] + Lp[1]) + Lp[0];
+  const PrepLayout pl(KB, G);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(prep + pl.a) + (size_t(t) * 8 + 4 * m) * 64 + lane;
+    dst[0] = u32x4_t{uint32_t(af[m].hi[0]), uint32_t(af[m].hi[1]), uint32_t(af[m].hi[2]), uint32_t(af[m].hi[3])};
+    dst[64] = u32x4_t{uint32_t(af[m].hi[4]), uint32_t(af[m].hi[5]), uint32_t(af[m].hi[6]), uint32_t(af[m].hi[7])};
+    dst[128] = u32x4_t{uint32_t(af[m].lo[0]), uint32_t(af[m].lo[1]), uint32_t(af[m].lo[2]), uint32_t(af[m].lo[3])};
+    dst[192] = u32x4_t{uint32_t(af[m].lo[4]), uint32_t(af[m].lo[5]), uint32_t(af[m].lo[6]), uint32_t(af[m].lo[7])};
+  }
+  reinterpret_cast<uint2*>(prep + pl.sc)[size_t(t) * 64 + lane] = make_uint2(af[0].sc, af[1].sc);
+  // lanes (0, c) hold the group sums of tokens 4c .. 4c + 3; lanes (n, 0) token n's logits
+  if (r == 0) {
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi)
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(prep + pl.xs) + (size_t(t) * GPT + gi) * 16 + 4 * c) = xs[gi];
+  }
+  if (c == 0) reinterpret_cast<f32x4_t*>(prep + pl.lg)[size_t(t) * 16 + r] = L;
+}
+
 // Sums the k chunks' float32 partials in a fixed order (deterministic) and writes y.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ks,
                                                             size_t tn, void* __restrict__ y,
@@ -1000,7 +1194,7 @@ struct LrArgs {
   int r;
 };
 
-template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT = false, bool F4 = false>
+template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT = false, bool F4 = false, bool PA = false>
 hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
                       const void* x, const int32_t* perm, const int32_t* offsets, void* y,
                       bool y_bf16, float* part, const LrArgs& lr, hipStream_t stream,
@@ -1012,7 +1206,7 @@ hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int
   // token groups by that XCD's L2.
   const int ty = (t + 16 * TB - 1) / (16 * TB);
   const int grid = std::min(d.row_blocks, std::max(8, (cu_count() / (ty * pl.ks)) & ~7));
-  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR, RT, F4>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
+  hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR, RT, F4, PA>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
                      0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
                      d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
                      offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.ks, lr.b, lr.r, rio);
@@ -1045,14 +1239,24 @@ hipError_t launch_gs(const mbq_desc& d, const Plan& pl, const void* packed, int3
 
 
 // In-kernel routing: bfloat16 activations, one token block, no side path, one k chunk.
-// f4 selects the fp8 x fp4 multiply (see above).
+// f4 selects the fp8 x fp4 multiply (see above); pa (with f4) the two-launch step:
+// decode_prep_kernel, then the streaming kernel on its prepared operands.
 template <int G, int S>
 hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
-                           const void* x, void* y, bool y_bf16, const RouteIO& rio, bool f4,
+                           const void* x, void* y, bool y_bf16, const RouteIO& rio, bool f4, bool pa,
                            hipStream_t stream) {
   if constexpr (stream_fits(G, S, 1)) {
+    if (f4 && pa) {
+      hipLaunchKernelGGL((decode_prep_kernel<G, S>), dim3(d.k_tiles), dim3(64), 0, stream,
+                         static_cast<const uint8_t*>(x), t, d.k, d.k_tiles, rio.wr, const_cast<uint8_t*>(rio.prep));
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     if constexpr (two_tiles_fit(G, S, 1)) {
       if (pl.tpw == 2) {
+        if (f4 && pa)
+          return launch_gsn<G, S, 1, 2, 1, false, true, true, true>(d, pl, packed, t, x, nullptr, nullptr, y,
+                                                                    y_bf16, nullptr, LrArgs{}, stream, rio);
         if (f4)
           return launch_gsn<G, S, 1, 2, 1, false, true, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
                                                               nullptr, LrArgs{}, stream, rio);
@@ -1060,6 +1264,9 @@ hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed
                                                       nullptr, LrArgs{}, stream, rio);
       }
     }
+    if (f4 && pa)
+      return launch_gsn<G, S, 1, 1, 1, false, true, true, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
+                                                                nullptr, LrArgs{}, stream, rio);
     if (f4)
       return launch_gsn<G, S, 1, 1, 1, false, true, true>(d, pl, packed, t, x, nullptr, nullptr, y, y_bf16,
                                                           nullptr, LrArgs{}, stream, rio);
@@ -1071,13 +1278,13 @@ hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed
 
 template <int G>
 hipError_t launch_route_g(const mbq_desc& d, const Plan& pl, const void* packed, int32_t t,
-                          const void* x, void* y, bool y_bf16, const RouteIO& rio, bool f4,
+                          const void* x, void* y, bool y_bf16, const RouteIO& rio, bool f4, bool pa,
                           hipStream_t stream) {
   switch (d.slices) {
-    case 1: return launch_route_gs<G, 1>(d, pl, packed, t, x, y, y_bf16, rio, false, stream);
-    case 2: return launch_route_gs<G, 2>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
-    case 3: return launch_route_gs<G, 3>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
-    default: return launch_route_gs<G, 4>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
+    case 1: return launch_route_gs<G, 1>(d, pl, packed, t, x, y, y_bf16, rio, false, false, stream);
+    case 2: return launch_route_gs<G, 2>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);
+    case 3: return launch_route_gs<G, 3>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);
+    default: return launch_route_gs<G, 4>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);
   }
 }
 
@@ -1119,10 +1326,20 @@ bool decode_route_supported(const mbq_desc& d, int32_t t) {
   return pl.ks == 1 && pl.tb == 1;
 }
 
+size_t decode_route_workspace(const mbq_desc& d, int32_t t) {
+  return decode_route_supported(d, t) ? PrepLayout(d.k_tiles, d.group).bytes : 0;
+}
+
 hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                const float* wr, float* logits, int32_t* budget, int32_t* perm,
-                               int32_t* offsets, void* y, bool y_bf16, int mul, hipStream_t stream) {
-  const RouteIO rio{wr, logits, budget, perm, offsets};
+                               int32_t* offsets, void* y, bool y_bf16, int mul, int launches, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  // Two launches (decode_prep_kernel prepares the fp8 operands, the partial logits and the
+  // group sums once, instead of in every workgroup) pay from about 8 tokens: below, the
+  // second launch costs more than the per-workgroup preparation it saves.
+  const bool room = ws && ws_bytes >= PrepLayout(d.k_tiles, d.group).bytes;
+  const bool pa = launches == 2 || (launches == 0 && t > 4 && room);
+  const RouteIO rio{wr, logits, budget, perm, offsets, static_cast<const uint8_t*>(ws)};
   const Plan pl = make_plan(d, t, true, false);
   // The fp8 x fp4 multiply saves ~1/4 of a row block's time but its activation split
   // costs every workgroup about two row blocks' worth up front: taken from 4 row blocks
@@ -1132,9 +1349,9 @@ hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t,
   if (mul == MBQ_MUL_BF16) f4 = false;
   if (mul == MBQ_MUL_FP8_FP4) f4 = true;
   switch (d.group) {
-    case 64: return launch_route_g<64>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
-    case 128: return launch_route_g<128>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
-    default: return launch_route_g<256>(d, pl, packed, t, x, y, y_bf16, rio, f4, stream);
+    case 64: return launch_route_g<64>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);
+    case 128: return launch_route_g<128>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);
+    default: return launch_route_g<256>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);
   }
 }
 

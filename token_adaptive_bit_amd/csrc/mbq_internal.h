@@ -58,10 +58,15 @@ size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool l
 // Decode with the routing in the kernel (bfloat16 x, 1 <= t <= 16, K within one
 // workgroup): writes logits, budget, perm and offsets as launch_route does, and y.
 bool decode_route_supported(const mbq_desc& d, int32_t t);
-// mul: an mbq_mul (MBQ_MUL_AUTO lets the plan choose).
+// mul: an mbq_mul (MBQ_MUL_AUTO lets the plan choose); launches: 0 (the plan's choice), 1
+// or 2.  The fp8 x fp4 step runs as two launches (the prepared operands in ws, which must
+// then hold decode_route_workspace() bytes) when asked to or, by default, above 4 tokens
+// with that much workspace; otherwise as one.
+size_t decode_route_workspace(const mbq_desc& d, int32_t t);
 hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                const float* wr, float* logits, int32_t* budget, int32_t* perm,
-                               int32_t* offsets, void* y, bool y_bf16, int mul, hipStream_t stream);
+                               int32_t* offsets, void* y, bool y_bf16, int mul, int launches, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
                                 void* y, bool y_bf16, void* ws, const float* lr_u, int32_t lr_ks,
