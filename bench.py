@@ -3,21 +3,23 @@
 Prints one JSON line.  A step is one pass of the per-batch hot path on the decode
 workload (Qwen2.5-7B-like up-projection, W 18944 x 3584 bf16 with 0.5% outlier columns,
 G = 128, 3 slices, a batch of 16 bf16 tokens): router logits + argmax + stable regroup
-and the routed decode linear, in one call (mbq_route_linear: the streaming decode kernel
-routes the batch itself, one launch per step).  Packing is an offline, once-per-weight
-step and is timed separately (reported under "extra").
+and the routed decode linear, in one call (mbq_route_linear with the plan's choices: at 16
+tokens two launches, the first preparing the fp8 operands and the partial router logits
+once, the second routing and streaming the weights on the fp8 x fp4 matrix instruction).
+Packing is an offline, once-per-weight step and is timed separately (under "extra").
 
 value = tokens / s over the timed steps (inputs resident in HBM), replayed from HIP graphs
 (one graph holding a step per weight copy, so neither the host's per-call overhead nor a
 per-replay submission gaps the kernels; the same steps launched one by one are reported as
-eager_ms_per_step, and the two-call form -- mbq_route's two kernels, then mbq_linear -- as
-two_call_ms_per_step).  The roofline object is for the dominant kernel (the step's one
-kernel): algorithmic bytes per launch (the slices the batch needs, activations, outputs,
-Wr and the routing outputs) over its average duration from HIP events on the launch
-stream around the timed replays (one launch per step, so this holds the kernel and the
-gap to the next launch; the committed rocprofv3 trace gives the kernel alone).  The packed
-weight is rotated over enough copies (> 512 MiB) that neither L2 nor the 256 MiB Infinity
-Cache can serve a repeat.
+eager_ms_per_step, and the step's other forms beside it: one launch on either multiply, and
+the two calls mbq_route then mbq_linear).  The roofline object is for the dominant kernel
+(the streaming linear): algorithmic bytes per launch (the slices the batch needs, the
+prepared operands or the activations, y, and the routing inputs and outputs) over its
+average duration, from HIP events on the launch stream around graph replays of that kernel
+alone (mbq_route_linear_prepared on prepared operands, one launch per step); the committed
+rocprofv3 trace of the same command gives the kernel's own duration.  The packed weight is
+rotated over enough copies (> 512 MiB) that neither L2 nor the 256 MiB Infinity Cache can
+serve a repeat.
 """
 from __future__ import annotations
 
@@ -69,14 +71,17 @@ def make_blobs(api, torch, W, group, slices, dev):
     return blobs
 
 
-def decode_bytes(p, T, jmax, router=False):
-    """Algorithmic bytes of one routed decode launch: needed slices + x + y + routing
-    (perm and offsets read; with the router in the launch, Wr read and logits, budget,
-    perm and offsets written instead)."""
+def decode_bytes(p, T, jmax, router=False, prep_bytes=0):
+    """Algorithmic bytes of one routed decode launch: the slices the batch needs, the
+    activations (or, on the prepared path, the prepared operands), y, and the routing
+    inputs and outputs (perm and offsets read; with the router in the launch, Wr or the
+    partial logits read and logits, budget, perm and offsets written)."""
     d = p.desc
-    base = jmax * int(d.slice_stride) + T * d.k * 2 + T * d.n * 2
+    xin = prep_bytes if prep_bytes else T * d.k * 2
+    base = jmax * int(d.slice_stride) + xin + T * d.n * 2
     if router:
-        return base + d.k * d.slices * 4 + T * d.slices * 4 + 2 * T * 4 + (d.slices + 1) * 4
+        wr = 0 if prep_bytes else d.k * d.slices * 4
+        return base + wr + T * d.slices * 4 + 2 * T * 4 + (d.slices + 1) * 4
     return base + T * 4 + (d.slices + 1) * 4
 
 
@@ -139,7 +144,47 @@ def traffic_from_profile(kernel_src: str, name: str):
         return None
 
 
-def bench_decode(api, torch, inputs, T, steps, warmup, dev):
+def graph_steps(torch, fn, nb, steps, warmup):
+    """Exactly `steps` calls fn(i) (i cycling over the nb weight copies) from HIP graphs: one
+    graph holding a call per copy, replayed steps // nb times, then one-call graphs for the
+    rest, so neither the host's launch overhead nor a per-replay submission gaps the
+    kernels.  Returns (s per call by the host clock, s per call from HIP events on the
+    replay stream)."""
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    big = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(big):
+        for c in range(nb):
+            fn(c)
+    single = []
+    for c in range(steps % nb):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(c)
+        single.append(g)
+    for _ in range(max(1, warmup // nb)):
+        big.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps // nb):
+        big.replay()
+    for g in single:
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, a.elapsed_time(b) / 1e3 / steps
+
+
+def bench_decode(api, torch, inputs, T, steps, warmup, dev, variants=True):
+    """The decode step on the 18944 x 3584 workload: route (logits, argmax, regroup) and the
+    routed linear through mbq_route_linear with the plan's choices; its dominant kernel (the
+    streaming linear) timed alone on prepared operands; and the step's other forms."""
     d = inputs.make_config(2)
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
@@ -152,17 +197,13 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev):
     perm = torch.empty(T, dtype=torch.int32, device=dev)
     off = torch.empty(4, dtype=torch.int32, device=dev)
     y = torch.empty((T, d["N"]), dtype=torch.bfloat16, device=dev)
-    ws_n = api.linear_workspace(blobs[0], T)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(api.route_linear_workspace(blobs[0], T), 1), dtype=torch.uint8, device=dev)
+    prep_bytes = api.route_prepare_workspace(blobs[0], T)
+    out = {"T": T, "copies": nb, "blob_bytes": int(blobs[0].blob.numel()), "N": d["N"], "K": d["K"]}
 
-    def step(i):
-        # one launch: routing inside the streaming decode kernel (mbq_route_linear)
+    def step(i, o=None):
         api.route_linear(blobs[i % nb], X, Wr, y=y, logits=logits, budget=budget, perm=perm, offsets=off,
-                         workspace=ws if ws_n else None)
-
-    def step_two_calls(i):
-        api.route(X, Wr, logits, budget, perm, off)
-        api.linear(blobs[i % nb], X, perm, off, y=y, workspace=ws if ws_n else None)
+                         workspace=ws, options=o)
 
     for i in range(warmup):
         step(i)
@@ -171,52 +212,34 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev):
     for i in range(steps):
         step(i)
     torch.cuda.synchronize()
-    eager_step_s = (time.perf_counter() - t0) / steps
-
-    def graph_steps(fn):
-        """Exactly `steps` steps (step i on weight copy i % nb) from HIP graphs: one graph
-        holding a step per copy, replayed steps // nb times, then one-step graphs for the
-        rest, so neither the host's launch overhead nor a per-replay submission gaps the
-        kernels.  Returns (s per step, s per step from HIP events around the replays)."""
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            fn(0)
-        torch.cuda.current_stream().wait_stream(cap)
-        torch.cuda.synchronize()
-        big = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(big):
-            for c in range(nb):
-                fn(c)
-        single = []
-        for c in range(steps % nb):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn(c)
-            single.append(g)
-        for _ in range(max(1, warmup // nb)):
-            big.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        a.record()
-        for _ in range(steps // nb):
-            big.replay()
-        for g in single:
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps, a.elapsed_time(b) / 1e3 / steps
-
-    two_call_step_s, _ = graph_steps(step_two_calls)
-    step_s, lin_s = graph_steps(step)   # last, so logits .. offsets hold this path's routes
+    out["eager_step_s"] = (time.perf_counter() - t0) / steps
+    if variants:
+        out["one_launch_fp8fp4_step_s"] = graph_steps(torch, lambda i: step(i, api.opts(decode_mul="fp8fp4", decode_launches=1)),
+                                                      nb, steps, warmup)[1]
+        out["one_launch_bf16_step_s"] = graph_steps(torch, lambda i: step(i, api.opts(decode_mul="bf16")),
+                                                    nb, steps, warmup)[1]
+        out["two_call_step_s"] = graph_steps(torch, lambda i: (api.route(X, Wr, logits, budget, perm, off),
+                                                               api.linear(blobs[i % nb], X, perm, off, y=y)),
+                                             nb, steps, warmup)[1]
+    out["step_s"], out["step_event_s"] = graph_steps(torch, step, nb, steps, warmup)
+    # the plan's path: two launches when the operands are prepared (prep_bytes > 0 and the
+    # fp8 x fp4 multiply), else one; the dominant kernel alone on prepared operands
+    two = prep_bytes > 0 and T > 4
+    out["launches"] = 2 if two else 1
+    if two:
+        prep = api.route_prepare(blobs[0], X, Wr)
+        out["prepare_s"] = graph_steps(torch, lambda i: api.route_prepare(blobs[0], X, Wr, prep=prep), nb, steps, warmup)[1]
+        out["kernel_s"] = graph_steps(torch, lambda i: api.route_linear_prepared(
+            blobs[i % nb], T, prep, y=y, logits=logits, budget=budget, perm=perm, offsets=off), nb, steps, warmup)[1]
+    else:
+        out["kernel_s"] = out["step_event_s"]
+    step(0)                              # last, so logits .. offsets hold the plan's routes
+    torch.cuda.synchronize()
     jmax = int((off[:3] < T).sum().item())      # slices with at least one token
-    counts = torch.diff(off).cpu().tolist()
-    return {"T": T, "step_s": step_s, "two_call_step_s": two_call_step_s, "eager_step_s": eager_step_s,
-            "linear_s": lin_s, "jmax": jmax,
-            "budget_counts": counts, "bytes": decode_bytes(blobs[0], T, jmax, router=True),
-            "weight_bytes": weight_bytes(blobs[0], jmax), "copies": nb,
-            "blob_bytes": int(blobs[0].blob.numel()), "N": d["N"], "K": d["K"]}
+    out.update({"jmax": jmax, "budget_counts": torch.diff(off).cpu().tolist(),
+                "bytes": decode_bytes(blobs[0], T, jmax, router=True, prep_bytes=prep_bytes if two else 0),
+                "weight_bytes": weight_bytes(blobs[0], jmax), "prep_bytes": prep_bytes if two else 0})
+    return out
 
 
 def bench_pack(api, torch, inputs, dev):
@@ -233,15 +256,16 @@ def bench_prefill(api, torch, inputs, dev, iters=20):
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     X = torch.from_numpy(d["X"]).to(dev, torch.bfloat16)
     budget = torch.from_numpy(d["budget"]).to(dev)
-    blobs = make_blobs(api, torch, W, 128, 3, dev)[:4]
+    blobs = make_blobs(api, torch, W, 128, 3, dev)   # > 512 MiB of copies: no cache serves a repeat
+    nb = len(blobs)
     perm, off = api.regroup(budget, 3)
     y = torch.empty((d["T"], d["N"]), dtype=torch.bfloat16, device=dev)
     for i in range(3):
-        api.linear(blobs[i % 4], X, perm, off, y=y)
+        api.linear(blobs[i % nb], X, perm, off, y=y)
     torch.cuda.synchronize()
-    s = time_events(torch, lambda i: api.linear(blobs[i % 4], X, perm, off, y=y), iters)
+    s = time_events(torch, lambda i: api.linear(blobs[i % nb], X, perm, off, y=y), iters)
     flops = 2.0 * d["T"] * d["N"] * d["K"]
-    return {"T": d["T"], "linear_s": s, "tflops": flops / s / 1e12,
+    return {"T": d["T"], "linear_s": s, "tflops": flops / s / 1e12, "copies": nb,
             "mfma_frac": flops / s / 1e12 / BF16_PEAK_TFLOPS, "budget_counts": torch.diff(off).cpu().tolist()}
 
 
@@ -425,43 +449,43 @@ def bench_layer(api, torch, inputs, dev, iters=20):
     _, _, perm, off = api.route(x0, Wr)
 
     def run(groups):
-        # groups: (weight names, activation name) sharing one blob and one launch
-        packs, xs, ys = [], [], []
+        # groups: (weight names, activation name) sharing one blob and one launch; two
+        # copies of the layer's blobs (2 x 267.6 MB, over 512 MiB) alternate between steps,
+        # so neither L2 nor the 256 MiB Infinity Cache serves a repeat
+        packs, xs, ys = [[], []], [], []
         for names, xn in groups:
             p, _ = api.pack_concat([Wd[n] for n in names], 128, 3)
-            packs.append(p)
+            packs[0].append(p)
+            packs[1].append(api.PackedLinear(p.desc, p.blob.clone()))
             xs.append(x0 if xn == "layer" else Xd[xn])
             ys.append(torch.empty((T, p.n), dtype=torch.bfloat16, device=dev))
         torch.cuda.synchronize()
 
         def step(i):
             api.route(x0, Wr, perm=perm, offsets=off)
-            for p, x, y in zip(packs, xs, ys):
+            for p, x, y in zip(packs[i % 2], xs, ys):
                 api.linear(p, x, perm, off, y=y)
 
-        for i in range(3):
-            step(i)
-        torch.cuda.synchronize()
-        s = time_events(torch, step, iters)
+        s = graph_steps(torch, step, 2, iters, 4)[1]
         counts = torch.diff(off).cpu().tolist()
         jmax = max(j + 1 for j in range(3) if counts[j] > 0)
-        nbytes = sum(decode_bytes(p, T, jmax) for p in packs)
-        return {"us": s * 1e6, "tokens_per_s": T / s, "launches": 1 + len(packs),
+        nbytes = sum(decode_bytes(p, T, jmax) for p in packs[0])
+        return {"us": s * 1e6, "tokens_per_s": T / s, "launches": 2 + len(groups), "layer_copies": 2,
                 "budget_counts": counts, "hbm_frac_incl_route": nbytes / s / 1e9 / HBM_PEAK_GBS}
 
     out = {"T": T}
     out["separate"] = run([([n], "layer" if n == "q" else n) for n in lin])
     out["fused_qkv_gateup"] = run([(["q", "k", "v"], "layer"), (["o"], "o"), (["gate", "up"], "gate"),
                                    (["down"], "down")])
-    out["note"] = ("weights are not rotated: the 7 packed linears (267 MB) exceed the 256 MiB cache; "
-                   "router logits are not fused into the previous op (norm and residual lie outside "
-                   "this path)")
+    out["note"] = ("steps replayed from HIP graphs over two copies of the layer's blobs (535 MB); the router "
+                   "(two launches) runs on the layer input once per step; its logits are not fused into "
+                   "the previous op (norm and residual lie outside this path)")
     return out
 
 
 def run_traffic(api, torch, inputs, dev, T, launches=20):
-    """For the counter passes: 3 copies of 1 GiB (known bytes), then `launches` decode
-    steps (mbq_route_linear) over rotated weight copies."""
+    """For the counter passes: a copy of 1 GiB (known bytes), then `launches` decode steps
+    (mbq_route_linear, the plan's path) over rotated weight copies."""
     bench_copy(torch, dev)
     d = inputs.make_config(2)
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
@@ -470,13 +494,15 @@ def run_traffic(api, torch, inputs, dev, T, launches=20):
     blobs = make_blobs(api, torch, W, 128, 3, dev)
     del W
     y = torch.empty((T, d["N"]), dtype=torch.bfloat16, device=dev)
-    for i in range(launches):          # the decode step as timed: one launch, routing inside
-        _, _, _, _, off = api.route_linear(blobs[i % len(blobs)], X, Wr, y=y)
+    ws = torch.empty(max(api.route_linear_workspace(blobs[0], T), 1), dtype=torch.uint8, device=dev)
+    for i in range(launches):          # the decode step as timed
+        _, _, _, _, off = api.route_linear(blobs[i % len(blobs)], X, Wr, y=y, workspace=ws)
     torch.cuda.synchronize()
     counts = torch.diff(off).cpu().tolist()
     jmax = max(j + 1 for j in range(3) if counts[j] > 0)
+    prep = api.route_prepare_workspace(blobs[0], T) if T > 4 else 0
     return {"workload": "traffic", "copy_bytes": 2 * (1 << 30),
-            "decode_bytes": decode_bytes(blobs[0], T, jmax, router=True), "launches": launches}
+            "decode_bytes": decode_bytes(blobs[0], T, jmax, router=True, prep_bytes=prep), "launches": launches}
 
 
 def cpu_baseline(inputs, T):
@@ -550,7 +576,8 @@ def main():
 
     log(f"decode T={args.tokens}: {args.warmup} warmup + {args.steps} timed steps")
     r = bench_decode(api, torch, inputs, args.tokens, args.steps, args.warmup, dev)
-    achieved = r["bytes"] / r["linear_s"] / 1e9
+    kernel = "decode_stream_kernel (prepared operands)" if r["launches"] == 2 else "decode_stream_kernel"
+    achieved = r["bytes"] / r["kernel_s"] / 1e9
     traffic = traffic_from_profile("decode_stream.hip", f"decode_stream_18944x3584_t{args.tokens}_traffic.txt")
     out = {
         "metric": METRIC,
@@ -563,20 +590,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 io; fp8 (e4m3 hi+lo) x fp4 (e2m1 codes) mfma, fp32 acc",
         "data": "synthetic",
         "config": {"workload": "decode GEMV 18944x3584 (Qwen2.5-7B-like up-proj), G128, S3, "
                                f"bf16, T{args.tokens}, router argmax",
                    "N": r["N"], "K": r["K"], "group": 128, "slices": 3, "tokens": args.tokens,
                    "budget_counts": r["budget_counts"], "slices_read": r["jmax"],
-                   "weight_copies_rotated": r["copies"]},
+                   "weight_copies_rotated": r["copies"], "launches_per_step": r["launches"],
+                   "multiply": "fp8 x fp4 (activations as exact e4m3 hi + lo pairs, one e8m0 scale per "
+                               "token and 128 inputs; codes as e2m1)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic},
-        "effective_weight_gbs": r["weight_bytes"] / r["linear_s"] / 1e9,
-        "linear_us": r["linear_s"] * 1e6,
-        "step_launch": "hip_graph, one kernel per step (mbq_route_linear)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": kernel, "kernel_us": r["kernel_s"] * 1e6,
+                     "algorithmic_bytes_per_launch": r["bytes"]},
+        "effective_weight_gbs": r["weight_bytes"] / r["kernel_s"] / 1e9,
+        "step_launch": f"hip_graph, {r['launches']} kernel(s) per step (mbq_route_linear)",
+        "step_us_events": r["step_event_s"] * 1e6,
+        "prepare_us": r.get("prepare_s", 0.0) * 1e6,
         "eager_ms_per_step": r["eager_step_s"] * 1e3,
+        "one_launch_fp8fp4_ms_per_step": r["one_launch_fp8fp4_step_s"] * 1e3,
+        "one_launch_bf16_ms_per_step": r["one_launch_bf16_step_s"] * 1e3,
         "two_call_ms_per_step": r["two_call_step_s"] * 1e3,
     }
     if not args.no_extra and args.only is None:  # (--only decode prints the headline line alone)
@@ -584,11 +617,12 @@ def main():
         for T in (1, 4):
             if T != args.tokens:
                 log(f"decode T={T}")
-                q = bench_decode(api, torch, inputs, T, 100, 10, dev)
-                extra[f"decode_t{T}"] = {"tokens_per_s": T / q["step_s"], "linear_us": q["linear_s"] * 1e6,
+                q = bench_decode(api, torch, inputs, T, 100, 10, dev, variants=False)
+                extra[f"decode_t{T}"] = {"tokens_per_s": T / q["step_s"], "step_us": q["step_event_s"] * 1e6,
+                                         "kernel_us": q["kernel_s"] * 1e6, "launches": q["launches"],
                                          "slices_read": q["jmax"],
-                                         "hbm_frac": q["bytes"] / q["linear_s"] / 1e9 / HBM_PEAK_GBS,
-                                         "effective_weight_gbs": q["weight_bytes"] / q["linear_s"] / 1e9}
+                                         "hbm_frac": q["bytes"] / q["kernel_s"] / 1e9 / HBM_PEAK_GBS,
+                                         "effective_weight_gbs": q["weight_bytes"] / q["kernel_s"] / 1e9}
         log("prefill 11008x4096 T=2048")
         pf = bench_prefill(api, torch, inputs, dev)
         extra["prefill_11008x4096_t2048"] = {"tflops": pf["tflops"], "mfma_frac": pf["mfma_frac"],

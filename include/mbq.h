@@ -291,6 +291,31 @@ mbq_status mbq_linear_static(const mbq_desc* desc, const void* packed, int32_t t
                              mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                              void* y, mbq_dtype y_dtype, const mbq_opts* opts, hipStream_t stream);
 
+/*
+ * The routed fp8 x fp4 decode step in two calls (English page sections 2.A, 2.B and 3; the
+ * same results as mbq_route_linear with that multiply): mbq_route_prepare turns t <= 16
+ * bfloat16 tokens into what every workgroup of the streaming kernel needs -- the
+ * activations as exact e4m3 hi + lo pairs with one power-of-two scale per token and 128
+ * inputs, their per-group sums, and per k tile of 256 inputs the partial router logits
+ * (Wr as three exact bfloat16 planes, float32 sums) -- and mbq_route_linear_prepared
+ * completes the routing (partial logits summed in tile order, first argmax, stable
+ * regroup; writes logits, budget, perm, offsets) and runs the routed linear on them.  One
+ * prepared buffer serves every weight with the same desc->k, group and slices.
+ *   prep, prep_bytes: device buffer of at least mbq_route_prepare_workspace() bytes,
+ *                     16-byte aligned (MBQ_ERR_WORKSPACE otherwise); written by prepare,
+ *                     read by prepared.
+ *   x: [t x desc->k] bfloat16, wr: [desc->k x desc->slices] float32, both 16-byte aligned.
+ *   Other arguments as in mbq_route_linear.  MBQ_ERR_UNSUPPORTED where mbq_route_linear
+ *   would not run the step as one kernel (t > 16, K beyond one workgroup) or for blobs of
+ *   one slice; mbq_route_prepare_workspace() returns 0 there.
+ */
+mbq_status mbq_route_prepare_workspace(const mbq_desc* desc, int32_t t, size_t* bytes);
+mbq_status mbq_route_prepare(const mbq_desc* desc, int32_t t, const void* x, const float* wr, void* prep,
+                             size_t prep_bytes, hipStream_t stream);
+mbq_status mbq_route_linear_prepared(const mbq_desc* desc, const void* packed, int32_t t, const void* prep,
+                                     size_t prep_bytes, float* logits, int32_t* budget, int32_t* perm,
+                                     int32_t* offsets, void* y, mbq_dtype y_dtype, hipStream_t stream);
+
 /* Host only: bytes of device workspace mbq_route_linear can use for t tokens: the
  * prepared operands of its two-launch fp8 x fp4 step (see there), or the routed linear's
  * (mbq_linear_workspace), whichever is larger.  Depends only on desc, t and x_dtype. */

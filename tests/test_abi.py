@@ -297,6 +297,35 @@ def test_linear_validation_and_workspace():
                      packed=None)) == OK
 
 
+def test_route_prepare_validation():
+    """The two calls of the prepared decode step refuse bad arguments before any launch."""
+    f = P(FAKE)
+    st, d = desc(200, 640, 128, 3)
+    dp = ctypes.byref(d)
+    n = ctypes.c_size_t(0)
+    assert L.mbq_route_prepare_workspace(dp, 16, ctypes.byref(n)) == OK
+    need = n.value
+    assert need == 3 * (8192 + 512 + 2 * 64 + 256)
+    assert L.mbq_route_prepare_workspace(dp, 17, ctypes.byref(n)) == OK and n.value == 0
+    assert L.mbq_route_prepare(dp, 16, f, f, f, need - 1, None) == WS
+    assert L.mbq_route_prepare(dp, 16, f, f, None, need, None) == WS
+    assert L.mbq_route_prepare(dp, 16, P(FAKE + 8), f, f, need, None) == ARG
+    assert L.mbq_route_prepare(dp, 16, f, None, f, need, None) == ARG
+    assert L.mbq_route_prepare(dp, 17, f, f, f, need, None) == UNSUP
+    assert L.mbq_route_prepare(dp, 0, None, None, None, 0, None) == OK
+    call = lambda **kw: L.mbq_route_linear_prepared(*[kw.get(k, v) for k, v in (
+        ("desc", dp), ("packed", f), ("t", 16), ("prep", f), ("pb", need), ("lg", f), ("b", f), ("perm", f),
+        ("off", f), ("y", f), ("yd", BF16), ("s", None))])
+    assert call(pb=need - 1) == WS
+    assert call(y=None) == ARG and call(off=None) == ARG and call(yd=5) == ARG
+    assert call(packed=P(FAKE + 64)) == ARG
+    assert call(t=17) == UNSUP
+    assert call(t=0, packed=None, prep=None, lg=None, b=None, perm=None, y=None) == OK
+    st1, d1 = desc(200, 640, 128, 1)            # one slice: no fp8 x fp4 step
+    assert L.mbq_route_prepare_workspace(ctypes.byref(d1), 16, ctypes.byref(n)) == OK and n.value == 0
+    assert L.mbq_route_prepare(ctypes.byref(d1), 16, f, f, f, need, None) == UNSUP
+
+
 def test_linear_static_limits():
     """The no-allocation linear refuses, before touching a device, any call whose split-K
     partials exceed the library's static buffer; an empty batch needs none."""

@@ -181,3 +181,29 @@ def test_route_linear_empty(mbq):
     torch.cuda.synchronize()
     assert off.cpu().tolist() == [0, 0, 0, 0]
     assert y.shape == (0, 32)
+
+
+@pytest.mark.parametrize("G,S,K,T", [(128, 3, 3584, 16), (64, 2, 1536, 9), (256, 4, 1280, 13)])
+def test_route_prepare_then_prepared(mbq, G, S, K, T):
+    """The two calls apart give exactly what mbq_route_linear does in two launches, and
+    one prepared buffer serves two weights with the same inputs (q / k -like)."""
+    say(f"route prepare G={G} S={S} K={K} T={T}")
+    d = inputs.make_linear(G + S + T, 144, K, T, group=G, slices=S)
+    d2 = inputs.make_linear(G + S + T + 1, 80, K, T, group=G, slices=S)
+    x, wr = to_dev(d["X"], torch.bfloat16), to_dev(d["Wr"], torch.float32)
+    p = mbq.pack(to_dev(d["W"], torch.bfloat16), group=G, slices=S)
+    p2 = mbq.pack(to_dev(d2["W"], torch.bfloat16), group=G, slices=S)
+    want = mbq.route_linear(p, x, wr, out_dtype=torch.float32,
+                            options=mbq.opts(decode_mul="fp8fp4", decode_launches=2))
+    prep = mbq.route_prepare(p, x, wr)
+    got = mbq.route_linear_prepared(p, T, prep, out_dtype=torch.float32)
+    got2 = mbq.route_linear_prepared(p2, T, prep, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in zip(want, got):
+        assert torch.equal(a, b)
+    b2 = got2[2].cpu().numpy()
+    assert np.array_equal(b2, got[2].cpu().numpy())        # same routes for the second weight
+    pk = O.pack(d2["W"], G, S)
+    deq = O.dequant_slices(pk["codes"], pk["scale"], pk["zero"], G)
+    assert token_errors(got2[0].cpu().numpy(), O.linear(d["X"], deq, b2)).max() <= TOL
+

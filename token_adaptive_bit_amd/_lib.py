@@ -21,7 +21,8 @@ STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANG
 
 EXPORTS = ("mbq_describe", "mbq_pack", "mbq_pack_rows", "mbq_pack_bitplane", "mbq_route", "mbq_regroup", "mbq_route_mlp_workspace",
            "mbq_route_mlp", "mbq_linear_workspace", "mbq_linear", "mbq_linear_static", "mbq_route_linear",
-           "mbq_route_linear_workspace",
+           "mbq_route_linear_workspace", "mbq_route_prepare_workspace", "mbq_route_prepare",
+           "mbq_route_linear_prepared",
            "mbq_linear_lowrank_workspace",
            "mbq_linear_lowrank", "mbq_status_str", "mbq_abi_version")
 
@@ -82,6 +83,9 @@ def _load() -> ctypes.CDLL:
     O = P(MbqOpts)
     lib.mbq_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, VP, ctypes.c_size_t, O, VP]
     lib.mbq_route_linear_workspace.argtypes = [D, I32, I32, P(ctypes.c_size_t)]
+    lib.mbq_route_prepare_workspace.argtypes = [D, I32, P(ctypes.c_size_t)]
+    lib.mbq_route_prepare.argtypes = [D, I32, VP, VP, VP, ctypes.c_size_t, VP]
+    lib.mbq_route_linear_prepared.argtypes = [D, VP, I32, VP, ctypes.c_size_t, VP, VP, VP, VP, VP, I32, VP]
     lib.mbq_linear_static.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, I32, O, VP]
     lib.mbq_route_linear.argtypes = [D, VP, I32, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP,
                                      ctypes.c_size_t, O, VP]

@@ -19,7 +19,8 @@ from ._lib import (MBQ_BF16, MBQ_F32, MBQ_MUL_AUTO, MBQ_MUL_BF16, MBQ_MUL_FP8_FP
 __all__ = ["PackedLinear", "pack", "pack_bitplane", "pack_concat", "route", "route_from_logits", "regroup", "linear",
            "linear_workspace", "describe", "MbqError", "MlpRouter", "route_mlp",
            "route_mlp_from_scores", "route_mlp_workspace", "linear_lowrank",
-           "linear_lowrank_workspace", "route_linear", "route_linear_workspace", "linear_static", "opts"]
+           "linear_lowrank_workspace", "route_linear", "route_linear_workspace", "linear_static", "opts",
+           "route_prepare", "route_prepare_workspace", "route_linear_prepared"]
 
 _FLOATS = (torch.float32, torch.bfloat16)
 
@@ -385,6 +386,48 @@ def linear_static(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets:
 
 def route_linear_workspace(p: PackedLinear, t: int, x_dtype=torch.bfloat16) -> int:
     return _lib.route_linear_workspace_bytes(p.desc, t, MBQ_BF16 if x_dtype == torch.bfloat16 else MBQ_F32)
+
+
+def route_prepare_workspace(p: PackedLinear, t: int) -> int:
+    n = ctypes.c_size_t(0)
+    check(_lib.LIB.mbq_route_prepare_workspace(ctypes.byref(p.desc), t, ctypes.byref(n)),
+          "mbq_route_prepare_workspace")
+    return int(n.value)
+
+
+def route_prepare(p: PackedLinear, x: torch.Tensor, wr: torch.Tensor, prep: torch.Tensor | None = None):
+    """First launch of the fp8 x fp4 decode step: prepared operands and partial logits of
+    x [t, k] (bfloat16, t <= 16) for weights shaped like p.  Returns the prepared buffer."""
+    _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [t, k]")
+    t = x.shape[0]
+    _arg(x, "x", (t, p.k), (torch.bfloat16,), x.device)
+    _arg(wr, "wr", (p.k, p.slices), (torch.float32,), x.device)
+    need = route_prepare_workspace(p, t)
+    if prep is None:
+        prep = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _workspace(prep, "prep", need, x.device)
+    check(_lib.LIB.mbq_route_prepare(ctypes.byref(p.desc), t, _p(x), _p(wr), _p(prep), prep.numel(), _stream()),
+          "mbq_route_prepare")
+    return prep
+
+
+def route_linear_prepared(p: PackedLinear, t: int, prep: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                          y: torch.Tensor | None = None, logits=None, budget=None, perm=None, offsets=None):
+    """Second launch: routing from the prepared partial logits and the routed linear on the
+    prepared operands.  Returns (y, logits, budget, perm, offsets)."""
+    dev = prep.device
+    _blob(p, dev)
+    _workspace(prep, "prep", route_prepare_workspace(p, t), dev)
+    if y is None:
+        y = torch.empty((t, p.n), dtype=out_dtype, device=dev)
+    _arg(y, "y", (t, p.n), _FLOATS, dev)
+    logits, budget, perm, offsets = _route_outputs(t, p.slices, dev, logits, budget, perm, offsets)
+    check(_lib.LIB.mbq_route_linear_prepared(ctypes.byref(p.desc), _p(p.blob), t, _p(prep), prep.numel(),
+                                             _p(logits), _p(budget), _p(perm), _p(offsets), _p(y), _dtype(y),
+                                             _stream()), "mbq_route_linear_prepared")
+    return y, logits, budget, perm, offsets
 
 
 def route_linear(p: PackedLinear, x: torch.Tensor, wr: torch.Tensor, out_dtype: torch.dtype | None = None,

@@ -379,6 +379,45 @@ mbq_status mbq_route_linear_workspace(const mbq_desc* desc, int32_t t, mbq_dtype
   return MBQ_OK;
 }
 
+mbq_status mbq_route_prepare_workspace(const mbq_desc* desc, int32_t t, size_t* bytes) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (!bytes) return MBQ_ERR_ARG;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  *bytes = mbq::decode_route_workspace(*desc, t);
+  return MBQ_OK;
+}
+
+mbq_status mbq_route_prepare(const mbq_desc* desc, int32_t t, const void* x, const float* wr, void* prep,
+                             size_t prep_bytes, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (t == 0) return MBQ_OK;
+  if (!mbq::decode_prepared_supported(*desc, t)) return MBQ_ERR_UNSUPPORTED;
+  if (!x || !wr || !aligned(x, 16) || !aligned(wr, 16)) return MBQ_ERR_ARG;
+  if (!prep || !aligned(prep, 16) || prep_bytes < mbq::decode_route_workspace(*desc, t)) return MBQ_ERR_WORKSPACE;
+  return launched(mbq::launch_decode_prepare(*desc, t, x, wr, prep, stream));
+}
+
+mbq_status mbq_route_linear_prepared(const mbq_desc* desc, const void* packed, int32_t t, const void* prep,
+                                     size_t prep_bytes, float* logits, int32_t* budget, int32_t* perm,
+                                     int32_t* offsets, void* y, mbq_dtype y_dtype, hipStream_t stream) {
+  mbq_status st = check_desc(desc);
+  if (st != MBQ_OK) return st;
+  if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
+  if (!valid_dtype(y_dtype) || !offsets || !aligned(offsets, 4)) return MBQ_ERR_ARG;
+  if (t == 0) return MBQ_OK;
+  if (!mbq::decode_prepared_supported(*desc, t)) return MBQ_ERR_UNSUPPORTED;
+  if (!packed || !logits || !budget || !perm || !y) return MBQ_ERR_ARG;
+  if (!aligned(packed, 256) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(budget, 4) ||
+      !aligned(perm, 4))
+    return MBQ_ERR_ARG;
+  if (!prep || !aligned(prep, 16) || prep_bytes < mbq::decode_route_workspace(*desc, t)) return MBQ_ERR_WORKSPACE;
+  return launched(mbq::launch_decode_prepared(*desc, packed, t, prep, logits, budget, perm, offsets, y,
+                                              y_dtype == MBQ_BF16, stream));
+}
+
 mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                         int32_t rank, size_t* bytes) {
   mbq_status st = check_desc(desc);

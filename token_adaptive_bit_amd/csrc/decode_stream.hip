@@ -1246,12 +1246,6 @@ hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed
                            const void* x, void* y, bool y_bf16, const RouteIO& rio, bool f4, bool pa,
                            hipStream_t stream) {
   if constexpr (stream_fits(G, S, 1)) {
-    if (f4 && pa) {
-      hipLaunchKernelGGL((decode_prep_kernel<G, S>), dim3(d.k_tiles), dim3(64), 0, stream,
-                         static_cast<const uint8_t*>(x), t, d.k, d.k_tiles, rio.wr, const_cast<uint8_t*>(rio.prep));
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
     if constexpr (two_tiles_fit(G, S, 1)) {
       if (pl.tpw == 2) {
         if (f4 && pa)
@@ -1274,6 +1268,20 @@ hipError_t launch_route_gs(const mbq_desc& d, const Plan& pl, const void* packed
                                                   nullptr, LrArgs{}, stream, rio);
   }
   return hipErrorInvalidValue;  // excluded by decode_route_supported
+}
+
+template <int G>
+hipError_t launch_prep_g(const mbq_desc& d, int32_t t, const void* x, const float* wr, void* prep,
+                         hipStream_t stream) {
+  const auto x8 = static_cast<const uint8_t*>(x);
+  auto p8 = static_cast<uint8_t*>(prep);
+  const dim3 grid(d.k_tiles), block(64);
+  switch (d.slices) {
+    case 2: hipLaunchKernelGGL((decode_prep_kernel<G, 2>), grid, block, 0, stream, x8, t, d.k, d.k_tiles, wr, p8); break;
+    case 3: hipLaunchKernelGGL((decode_prep_kernel<G, 3>), grid, block, 0, stream, x8, t, d.k, d.k_tiles, wr, p8); break;
+    default: hipLaunchKernelGGL((decode_prep_kernel<G, 4>), grid, block, 0, stream, x8, t, d.k, d.k_tiles, wr, p8); break;
+  }
+  return hipGetLastError();
 }
 
 template <int G>
@@ -1327,7 +1335,32 @@ bool decode_route_supported(const mbq_desc& d, int32_t t) {
 }
 
 size_t decode_route_workspace(const mbq_desc& d, int32_t t) {
-  return decode_route_supported(d, t) ? PrepLayout(d.k_tiles, d.group).bytes : 0;
+  return decode_prepared_supported(d, t) ? PrepLayout(d.k_tiles, d.group).bytes : 0;
+}
+
+bool decode_prepared_supported(const mbq_desc& d, int32_t t) {
+  return d.slices >= 2 && decode_route_supported(d, t);
+}
+
+hipError_t launch_decode_prepare(const mbq_desc& d, int32_t t, const void* x, const float* wr, void* prep,
+                                 hipStream_t stream) {
+  switch (d.group) {
+    case 64: return launch_prep_g<64>(d, t, x, wr, prep, stream);
+    case 128: return launch_prep_g<128>(d, t, x, wr, prep, stream);
+    default: return launch_prep_g<256>(d, t, x, wr, prep, stream);
+  }
+}
+
+hipError_t launch_decode_prepared(const mbq_desc& d, const void* packed, int32_t t, const void* prep,
+                                  float* logits, int32_t* budget, int32_t* perm, int32_t* offsets, void* y,
+                                  bool y_bf16, hipStream_t stream) {
+  const RouteIO rio{nullptr, logits, budget, perm, offsets, static_cast<const uint8_t*>(prep)};
+  const Plan pl = make_plan(d, t, true, false);
+  switch (d.group) {
+    case 64: return launch_route_g<64>(d, pl, packed, t, nullptr, y, y_bf16, rio, true, true, stream);
+    case 128: return launch_route_g<128>(d, pl, packed, t, nullptr, y, y_bf16, rio, true, true, stream);
+    default: return launch_route_g<256>(d, pl, packed, t, nullptr, y, y_bf16, rio, true, true, stream);
+  }
 }
 
 hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
@@ -1338,7 +1371,7 @@ hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t,
   // group sums once, instead of in every workgroup) pay from about 8 tokens: below, the
   // second launch costs more than the per-workgroup preparation it saves.
   const bool room = ws && ws_bytes >= PrepLayout(d.k_tiles, d.group).bytes;
-  const bool pa = launches == 2 || (launches == 0 && t > 4 && room);
+  bool pa = launches == 2 || (launches == 0 && t > 4 && room);
   const RouteIO rio{wr, logits, budget, perm, offsets, static_cast<const uint8_t*>(ws)};
   const Plan pl = make_plan(d, t, true, false);
   // The fp8 x fp4 multiply saves ~1/4 of a row block's time but its activation split
@@ -1348,6 +1381,12 @@ hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t,
   bool f4 = d.slices >= 2 && (d.row_blocks + grid - 1) / grid >= 4;
   if (mul == MBQ_MUL_BF16) f4 = false;
   if (mul == MBQ_MUL_FP8_FP4) f4 = true;
+  if (!f4 || d.slices < 2) pa = false;
+  if (pa) {
+    const hipError_t e = launch_decode_prepare(d, t, x, wr, ws, stream);
+    if (e != hipSuccess) return e;
+    return launch_decode_prepared(d, packed, t, ws, logits, budget, perm, offsets, y, y_bf16, stream);
+  }
   switch (d.group) {
     case 64: return launch_route_g<64>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);
     case 128: return launch_route_g<128>(d, pl, packed, t, x, y, y_bf16, rio, f4, pa, stream);

@@ -63,6 +63,14 @@ bool decode_route_supported(const mbq_desc& d, int32_t t);
 // then hold decode_route_workspace() bytes) when asked to or, by default, above 4 tokens
 // with that much workspace; otherwise as one.
 size_t decode_route_workspace(const mbq_desc& d, int32_t t);
+// The two launches apart: the prepared operands (decode_prep_kernel), and the streaming
+// kernel that routes from their partial logits.  Blobs of 2 or more slices.
+bool decode_prepared_supported(const mbq_desc& d, int32_t t);
+hipError_t launch_decode_prepare(const mbq_desc& d, int32_t t, const void* x, const float* wr, void* prep,
+                                 hipStream_t stream);
+hipError_t launch_decode_prepared(const mbq_desc& d, const void* packed, int32_t t, const void* prep,
+                                  float* logits, int32_t* budget, int32_t* perm, int32_t* offsets, void* y,
+                                  bool y_bf16, hipStream_t stream);
 hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                const float* wr, float* logits, int32_t* budget, int32_t* perm,
                                int32_t* offsets, void* y, bool y_bf16, int mul, int launches, void* ws,
