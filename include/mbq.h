@@ -28,14 +28,17 @@
  *
  * Conventions for every call:
  *   - All pointers except `mbq_desc*`, `bytes` and `out` are DEVICE pointers owned by the
- *     caller.  The library allocates nothing and keeps no global state: calls are
- *     re-entrant and thread-safe.
+ *     caller.  The library allocates nothing and keeps no global state (except
+ *     mbq_linear_static's fixed device buffer, below): calls are re-entrant and
+ *     thread-safe.
  *   - Every call only enqueues work on `stream` and never synchronizes the host.
  *   - Argument, shape and alignment checks happen before any launch; failures return a
  *     negative mbq_status and launch nothing.  A failed launch returns MBQ_ERR_DEVICE.
  *   - Alignment: the packed blob 256 bytes, x / y / workspace 16 bytes, others 4 bytes.
- *   - Supported: bits == 2, 1 <= slices <= 4, group in {64, 128, 256}, K % group == 0,
- *     N >= 1, K >= group, T >= 0.  With T == 0 nothing is launched except that
+ *   - Supported: bits == 2, 1 <= slices <= 4, group in {32, 64, 128, 256}, K % group == 0,
+ *     N >= 1, K >= group, T >= 0.  Groups of 32 inputs run on the generic kernels only
+ *     (a lane's 16-input code words pair up into one group, which the streaming decode
+ *     and the MFMA prefill tiles do not split); the other groups run on either.  With T == 0 nothing is launched except that
  *     mbq_route / mbq_regroup still write offsets; T-sized pointers may then be NULL.
  */
 #ifndef MBQ_H

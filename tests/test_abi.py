@@ -50,7 +50,8 @@ def desc(n, k, g, s):
 def test_describe_geometry_matches_format():
     from oracle import mbq_oracle as O   # the format description, written independently
     for (n, k, g, s) in [(512, 256, 64, 3), (18944, 3584, 128, 3), (11008, 4096, 128, 3),
-                         (200, 640, 128, 2), (5120, 13824, 128, 3), (17, 768, 256, 4)]:
+                         (200, 640, 128, 2), (5120, 13824, 128, 3), (17, 768, 256, 4),
+                         (40, 96, 32, 3), (130, 544, 32, 4)]:
         st, d = desc(n, k, g, s)
         assert st == OK
         geo = O.blob_geometry(n, k, g, s)
@@ -62,7 +63,8 @@ def test_describe_geometry_matches_format():
 
 
 @pytest.mark.parametrize("n,k,g,s,want", [
-    (16, 256, 32, 3, UNSUP), (16, 256, 96, 3, UNSUP), (16, 256, 64, 0, UNSUP),
+    (16, 256, 16, 3, UNSUP), (16, 256, 96, 3, UNSUP), (16, 256, 64, 0, UNSUP),
+    (16, 48, 32, 3, SHAPE),
     (16, 256, 64, 5, UNSUP), (0, 256, 64, 3, SHAPE), (16, 100, 64, 3, SHAPE),
     (16, 32, 64, 1, SHAPE), (-3, 256, 64, 1, SHAPE)])
 def test_describe_rejects(n, k, g, s, want):

@@ -57,7 +57,7 @@ const char* mbq_status_str(mbq_status s) {
 
 mbq_status mbq_describe(int32_t n, int32_t k, int32_t group, int32_t slices, mbq_desc* out) {
   if (!out) return MBQ_ERR_ARG;
-  if (group != 64 && group != 128 && group != 256) return MBQ_ERR_UNSUPPORTED;
+  if (group != 32 && group != 64 && group != 128 && group != 256) return MBQ_ERR_UNSUPPORTED;
   if (slices < 1 || slices > 4) return MBQ_ERR_UNSUPPORTED;
   if (n < 1 || k < group || (k % group) != 0) return MBQ_ERR_SHAPE;
   if (n > (1 << 28) || k > (1 << 28)) return MBQ_ERR_SHAPE;

@@ -53,17 +53,18 @@ __device__ __forceinline__ u32x4_t ldg16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// One k tile's worth of loads for one wave.
-template <int TB, int RB, int SMAX, bool XF32>
+// One k tile's worth of loads for one wave.  G32: groups of 32 inputs (8 per tile).
+template <int TB, int RB, int SMAX, bool XF32, bool G32>
 struct Bundle {
+  static constexpr int GPT = G32 ? 8 : 4;
   u32x4_t cw[SMAX][RB];                 // 64 codes per lane per (slice, row block)
-  uint32_t pv[SMAX][RB][4];             // (scale, zero) per group in the tile (<= 4)
+  uint32_t pv[SMAX][RB][GPT];           // (scale, zero) per group in the tile
   u32x4_t a[TB][XF32 ? 16 : 8];         // A: word i, half h -> [2i + h] (bf16) or raw f32
 };
 
-template <int TB, int RB, int SMAX, bool XF32>
-__device__ __forceinline__ void load_bundle(Bundle<TB, RB, SMAX, XF32>& B, int kt,
-                                            const uint8_t* __restrict__ packed, int KB, int NG,
+template <int TB, int RB, int SMAX, bool XF32, bool G32>
+__device__ __forceinline__ void load_bundle(Bundle<TB, RB, SMAX, XF32, G32>& B, int kt,
+                                            const uint8_t* __restrict__ packed, int K, int KB, int NG,
                                             int NB, int gpt, int nb0, int jmax,
                                             uint64_t slice_stride, uint64_t params_offset,
                                             const char* const (&xrow)[TB], const bool (&xlive)[TB],
@@ -79,12 +80,12 @@ __device__ __forceinline__ void load_bundle(Bundle<TB, RB, SMAX, XF32>& B, int k
         B.cw[j][rb] = ldg16(sl + (size_t(nb) * KB + kt) * kTileBytes + 16 * lane);
         const uint8_t* pp = sl + params_offset + ((size_t(nb) * NG + size_t(kt) * gpt) * 16 + r) * 4;
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
+        for (int gi = 0; gi < B.GPT; ++gi)
           B.pv[j][rb][gi] = (gi < gpt) ? *reinterpret_cast<const uint32_t*>(pp + gi * 64) : 0u;
       } else {
         B.cw[j][rb] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) B.pv[j][rb][gi] = 0u;
+        for (int gi = 0; gi < B.GPT; ++gi) B.pv[j][rb][gi] = 0u;
       }
     }
   }
@@ -95,13 +96,15 @@ __device__ __forceinline__ void load_bundle(Bundle<TB, RB, SMAX, XF32>& B, int k
     for (int i = 0; i < 4; ++i) {
       const size_t k = size_t(kt) * 256 + 64 * i + 16 * c;
       const char* p = xrow[tb] + k * kEl;
+      // K is a multiple of 16: a lane's 16 inputs lie wholly inside or wholly past the row
+      const bool in = xlive[tb] && k < size_t(K);
       if (XF32) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          B.a[tb][4 * i + q] = xlive[tb] ? ldg16(p + 16 * q) : u32x4_t{0u, 0u, 0u, 0u};
+          B.a[tb][4 * i + q] = in ? ldg16(p + 16 * q) : u32x4_t{0u, 0u, 0u, 0u};
       } else {
-        B.a[tb][2 * i] = xlive[tb] ? ldg16(p) : u32x4_t{0u, 0u, 0u, 0u};
-        B.a[tb][2 * i + 1] = xlive[tb] ? ldg16(p + 16) : u32x4_t{0u, 0u, 0u, 0u};
+        B.a[tb][2 * i] = in ? ldg16(p) : u32x4_t{0u, 0u, 0u, 0u};
+        B.a[tb][2 * i + 1] = in ? ldg16(p + 16) : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
   }
@@ -126,9 +129,9 @@ __device__ __forceinline__ void split_f32(const u32x4_t& q0, const u32x4_t& q1, 
   }
 }
 
-template <int TB, int RB, int SMAX, bool XF32>
-__device__ __forceinline__ void compute_bundle(const Bundle<TB, RB, SMAX, XF32>& B, int wpg,
-                                               int jmax, const int (&jlim)[TB],
+template <int TB, int RB, int SMAX, bool XF32, bool G32>
+__device__ __forceinline__ void compute_bundle(const Bundle<TB, RB, SMAX, XF32, G32>& B, int wpg,
+                                               int jmax, const int (&jlim)[TB], int c,
                                                f32x4_t (&acc)[SMAX][TB][RB]) {
   const u32x4_t bneg0{kNeg128, kNeg32, kNeg8, kNeg128};   // -o for inputs 0..7
   const u32x4_t bneg1{kNeg32, kNeg8, kNeg128, kNeg32};    // -o for inputs 8..15
@@ -156,6 +159,61 @@ __device__ __forceinline__ void compute_bundle(const Bundle<TB, RB, SMAX, XF32>&
 
   f32x4_t P[SMAX][TB][RB];
   f32x4_t gxs[TB];
+  if constexpr (G32) {
+    // Word i holds groups 2i (lanes c = 0, 1) and 2i + 1 (c = 2, 3) of the tile: each group
+    // runs the MFMAs on an A operand with the other group's lanes zeroed.
+    const u32x4_t z4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        const bool mine = (c >> 1) == sg;
+        u32x4_t Am[TB][2][NA];
+        f32x4_t gnb[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          gnb[tb] = zero4;
+          gxs[tb] = zero4;
+#pragma unroll
+          for (int pa = 0; pa < NA; ++pa) {
+            Am[tb][0][pa] = mine ? A[tb][i][0][pa] : z4;
+            Am[tb][1][pa] = mine ? A[tb][i][1][pa] : z4;
+            gnb[tb] = mfma(Am[tb][0][pa], bneg0, gnb[tb]);
+            gnb[tb] = mfma(Am[tb][1][pa], bneg1, gnb[tb]);
+            gxs[tb] = mfma(Am[tb][0][pa], ones, gxs[tb]);
+            gxs[tb] = mfma(Am[tb][1][pa], ones, gxs[tb]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j) {
+          if (j >= jmax) break;
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            u32x4_t b0, b1;
+            unpack_word(B.cw[j][rb][i], b0, b1);
+            const uint32_t pv = B.pv[j][rb][2 * i + sg];
+            const float s = __half2float(__ushort_as_half(uint16_t(pv & 0xFFFFu)));
+            const float z = __half2float(__ushort_as_half(uint16_t(pv >> 16)));
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+              if (j < jlim[tb]) {
+                f32x4_t p = gnb[tb];
+#pragma unroll
+                for (int pa = 0; pa < NA; ++pa) {
+                  p = mfma(Am[tb][0][pa], b0, p);
+                  p = mfma(Am[tb][1][pa], b1, p);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  acc[j][tb][rb][v] = fmaf(s, p[v], fmaf(z, gxs[tb][v], acc[j][tb][rb][v]));
+              }
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i % wpg == 0) {
@@ -229,7 +287,7 @@ __device__ __forceinline__ void compute_bundle(const Bundle<TB, RB, SMAX, XF32>&
   }
 }
 
-template <int TB, int RB, int SMAX, bool XF32>
+template <int TB, int RB, int SMAX, bool XF32, bool G32>
 __global__ __launch_bounds__(512) void decode_kernel(
     const uint8_t* __restrict__ packed, int N, int K, int KB, int NG, int NB, int G,
     uint64_t slice_stride, uint64_t params_offset, const void* __restrict__ x, int T,
@@ -280,17 +338,17 @@ __global__ __launch_bounds__(512) void decode_kernel(
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) acc[j][tb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  Bundle<TB, RB, SMAX, XF32> b0, b1;
+  Bundle<TB, RB, SMAX, XF32, G32> b0, b1;
   if (kt0 < kt1)
-    load_bundle(b0, kt0, packed, KB, NG, NB, gpt, nb0, jmax, slice_stride, params_offset, xrow, xlive, lane);
+    load_bundle(b0, kt0, packed, K, KB, NG, NB, gpt, nb0, jmax, slice_stride, params_offset, xrow, xlive, lane);
   for (int kt = kt0; kt < kt1; kt += 2) {
     if (kt + 1 < kt1)
-      load_bundle(b1, kt + 1, packed, KB, NG, NB, gpt, nb0, jmax, slice_stride, params_offset, xrow, xlive, lane);
-    compute_bundle(b0, wpg, jmax, jlim, acc);
+      load_bundle(b1, kt + 1, packed, K, KB, NG, NB, gpt, nb0, jmax, slice_stride, params_offset, xrow, xlive, lane);
+    compute_bundle(b0, wpg, jmax, jlim, c, acc);
     if (kt + 1 < kt1) {
       if (kt + 2 < kt1)
-        load_bundle(b0, kt + 2, packed, KB, NG, NB, gpt, nb0, jmax, slice_stride, params_offset, xrow, xlive, lane);
-      compute_bundle(b1, wpg, jmax, jlim, acc);
+        load_bundle(b0, kt + 2, packed, K, KB, NG, NB, gpt, nb0, jmax, slice_stride, params_offset, xrow, xlive, lane);
+      compute_bundle(b1, wpg, jmax, jlim, c, acc);
     }
   }
 
@@ -347,10 +405,16 @@ hipError_t launch_k(const mbq_desc& d, const void* packed, int32_t t, const void
                     hipStream_t stream) {
   const int nw = waves_for(d.k_tiles);
   dim3 grid((d.row_blocks + RB - 1) / RB), block(64 * nw);
-  hipLaunchKernelGGL((decode_kernel<TB, RB, SMAX, XF32>), grid, block, 0, stream,
-                     static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles, d.groups_padded,
-                     d.row_blocks, d.group, d.slice_stride, d.params_offset, x, t, perm,
-                     offsets, y, int(y_bf16));
+  if (d.group == 32)
+    hipLaunchKernelGGL((decode_kernel<TB, RB, SMAX, XF32, true>), grid, block, 0, stream,
+                       static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles, d.groups_padded,
+                       d.row_blocks, d.group, d.slice_stride, d.params_offset, x, t, perm,
+                       offsets, y, int(y_bf16));
+  else
+    hipLaunchKernelGGL((decode_kernel<TB, RB, SMAX, XF32, false>), grid, block, 0, stream,
+                       static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles, d.groups_padded,
+                       d.row_blocks, d.group, d.slice_stride, d.params_offset, x, t, perm,
+                       offsets, y, int(y_bf16));
   return hipGetLastError();
 }
 

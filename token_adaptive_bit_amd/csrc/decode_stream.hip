@@ -235,16 +235,23 @@ __device__ __forceinline__ void load_codes(Codes<G, S, TPW, LR>& C, const __amdg
                                            uint32_t po, uint32_t lane_code,
                                            const uint32_t (&lane_pv)[Codes<G, S, TPW, LR>::PH]) {
   constexpr int PH = Codes<G, S, TPW, LR>::PH;
+  // nb < 0: a row block past the workgroup's last one.  Its loads still go out (every
+  // path keeps the same loads in flight) but at an offset past every buffer's range
+  // (slices end below 2^32 - 256), so they return zeros without a memory request.
+  const bool dead = nb < 0;
+  constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
+  const uint32_t vc = dead ? kPastEnd : lane_code;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp) {
-      const uint32_t tile = uint32_t(nb * KB + kt[tp]) * kTileBytes;
-      C.cw[tp][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs[j], lane_code, tile, 0));
+      const uint32_t tile = dead ? 0u : uint32_t(nb * KB + kt[tp]) * kTileBytes;
+      C.cw[tp][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs[j], vc, tile, 0));
     }
-    const uint32_t par = po + uint32_t(nb * NG) * 64;
+    const uint32_t par = dead ? 0u : po + uint32_t(nb * NG) * 64;
 #pragma unroll
-    for (int h = 0; h < PH; ++h) C.pw[j][h] = __builtin_amdgcn_raw_buffer_load_b32(rs[j], lane_pv[h], par, 0);
+    for (int h = 0; h < PH; ++h)
+      C.pw[j][h] = __builtin_amdgcn_raw_buffer_load_b32(rs[j], dead ? kPastEnd : lane_pv[h], par, 0);
   }
 }
 
@@ -462,7 +469,8 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   auto load_lr = [&](Codes<G, S, TPW, LR>& C, int nb) __attribute__((always_inline)) {
     if constexpr (LR)
       C.lr.v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                   rlr_b, lr_lane == 0x80000000u ? lr_lane : lr_lane + uint32_t(nb) * 16u * lr_r * 2, 0, 0));
+                   rlr_b, (lr_lane == 0x80000000u || nb < 0) ? 0x80000000u : lr_lane + uint32_t(nb) * 16u * lr_r * 2,
+                   0, 0));
   };
 
   // Budgets of this block's tokens, published in LDS right before the first row block is
@@ -810,10 +818,9 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // instantiated once per slice count read (1 .. S), so
   // inside each copy every path into the loop header carries the same pending loads in
   // the same order, which keeps the compiler's waits on the in-order load counter exact.
-  // A load past the end re-reads the workgroup's first row block (cached), so every load
-  // is unconditional.
+  // A load past the end (row block -1) goes out of range: zeros, no memory traffic.
   const int rb0 = blockIdx.x;
-  auto nbl = [&](int m) { const int n = rb0 + m * step; return n < NB ? n : rb0; };
+  auto nbl = [&](int m) { const int n = rb0 + m * step; return n < NB ? n : -1; };
   // (scheduling fences keep the issue order perm, x, row block 0, row block 1, so each
   // wait below covers exactly the loads it needs)
   __builtin_amdgcn_sched_barrier(0);
@@ -1324,7 +1331,8 @@ hipError_t launch_g(const mbq_desc& d, const Plan& pl, const void* packed, int32
 bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16, bool lr) {
   // buffer offsets are 32-bit: a slice must stay below 4 GiB
   const int na = x_bf16 ? 1 : 2;
-  return t >= 1 && t <= kMaxTokens && d.slice_stride < (uint64_t(1) << 32) &&
+  // groups of 32 inputs split a lane's code word in two: served by the generic kernel
+  return t >= 1 && t <= kMaxTokens && d.group >= 64 && d.slice_stride < (uint64_t(1) << 32) &&
          (lr ? lr_fits(d.group, d.slices, na) : stream_fits(d.group, d.slices, na));
 }
 
@@ -1376,9 +1384,11 @@ hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t,
   const Plan pl = make_plan(d, t, true, false);
   // The fp8 x fp4 multiply saves ~1/4 of a row block's time but its activation split
   // costs every workgroup about two row blocks' worth up front: taken from 4 row blocks
-  // per workgroup and 2 slices on, unless the caller chooses (mul).
+  // per workgroup, 2 slices and 4 tokens on (with fewer tokens fewer slices tend to be
+  // read, and a one-token step on the 18944 x 3584 weight measured faster in bf16: 13.2
+  // against 14.3 us), unless the caller chooses (mul).
   const int grid = std::min(d.row_blocks, std::max(8, cu_count() & ~7));
-  bool f4 = d.slices >= 2 && (d.row_blocks + grid - 1) / grid >= 4;
+  bool f4 = d.slices >= 2 && t >= 4 && (d.row_blocks + grid - 1) / grid >= 4;
   if (mul == MBQ_MUL_BF16) f4 = false;
   if (mul == MBQ_MUL_FP8_FP4) f4 = true;
   if (!f4 || d.slices < 2) pa = false;

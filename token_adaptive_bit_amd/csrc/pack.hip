@@ -8,8 +8,10 @@
 // One wave per packed tile (16 rows x 256 inputs).  Lane l = 16c + r owns row r of the
 // tile and inputs 64i + 16c + e (i = 0..3, e = 0..15): exactly the 64 codes it stores as
 // one 16-byte vector, so the codes of every slice leave the kernel as one coalesced
-// 1 KiB store per wave.  A group of G inputs of one row is spread over the 4 lanes
-// r, r+16, r+32, r+48 (G/64 words each), so its min and max need two cross-lane steps.
+// 1 KiB store per wave.  A group of G >= 64 inputs of one row is spread over the 4 lanes
+// r, r+16, r+32, r+48 (G/64 words each), so its min and max need two cross-lane steps; a
+// group of 32 is word i of the lane pair c = 2h, 2h+1 (group 2i + h of the tile) and
+// needs one.
 // The residual of all 64 inputs stays in registers across the slices.
 //
 // Bit-exactness: every float32 operation is rounded on its own (this file is built with
@@ -29,8 +31,11 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
                                                   uint64_t params_offset, int nb0, int NBT,
                                                   uint8_t* __restrict__ packed,
                                                   int32_t* __restrict__ status) {
-  constexpr int kWordsPerGroup = G / 64;
+  // G = 32: one pass per word, each lane pair holding a group of its own
+  constexpr bool kPair = G == 32;
+  constexpr int kWordsPerGroup = kPair ? 1 : G / 64;
   constexpr int kGroupsPerTile = 256 / G;
+  constexpr int kPasses = kPair ? 4 : kGroupsPerTile;
   const int kb = blockIdx.x, nb = nb0 + blockIdx.y;
   const int lane = threadIdx.x, r = lane & 15, c = lane >> 4;
   const int n = blockIdx.y * 16 + r;  // row of w
@@ -53,7 +58,7 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
     uint8_t* slice = packed + uint64_t(j) * slice_stride;
     uint32_t word[4];
 #pragma unroll
-    for (int gi = 0; gi < kGroupsPerTile; ++gi) {
+    for (int gi = 0; gi < kPasses; ++gi) {
       float lo = R[gi * kWordsPerGroup][0], hi = lo;
 #pragma unroll
       for (int ii = 0; ii < kWordsPerGroup; ++ii) {
@@ -65,8 +70,10 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
       }
       lo = fminf(lo, __shfl_xor(lo, 16));
       hi = fmaxf(hi, __shfl_xor(hi, 16));
-      lo = fminf(lo, __shfl_xor(lo, 32));
-      hi = fmaxf(hi, __shfl_xor(hi, 32));
+      if (!kPair) {
+        lo = fminf(lo, __shfl_xor(lo, 32));
+        hi = fmaxf(hi, __shfl_xor(hi, 32));
+      }
       lo = __fadd_rn(lo, 0.0f);  // a signed-zero minimum is stored as +0
       const float span = __fsub_rn(hi, lo);
       const float step = __fdiv_rn(span, 3.0f);
@@ -94,9 +101,9 @@ __global__ __launch_bounds__(64) void pack_kernel(const void* __restrict__ w, in
         }
         word[i] = wd;
       }
-      if (c == 0) {
+      if (kPair ? (c & 1) == 0 : c == 0) {
         const uint32_t pv = uint32_t(__half_as_ushort(hs)) | (uint32_t(__half_as_ushort(hz)) << 16);
-        const size_t g = size_t(kb) * kGroupsPerTile + gi;
+        const size_t g = size_t(kb) * kGroupsPerTile + (kPair ? 2 * gi + (c >> 1) : gi);
         *reinterpret_cast<uint32_t*>(slice + params_offset + ((size_t(nb) * NG + g) * 16 + r) * 4) = pv;
       }
     }
@@ -126,8 +133,10 @@ __global__ __launch_bounds__(64) void pack_bitplane_kernel(const void* __restric
                                                            uint64_t params_offset, int NBT,
                                                            uint8_t* __restrict__ packed,
                                                            int32_t* __restrict__ status) {
-  constexpr int kWordsPerGroup = G / 64;
+  constexpr bool kPair = G == 32;
+  constexpr int kWordsPerGroup = kPair ? 1 : G / 64;
   constexpr int kGroupsPerTile = 256 / G;
+  constexpr int kPasses = kPair ? 4 : kGroupsPerTile;
   const int kb = blockIdx.x, nb = blockIdx.y;
   const int lane = threadIdx.x, r = lane & 15, c = lane >> 4;
   const int n = nb * 16 + r;
@@ -146,9 +155,9 @@ __global__ __launch_bounds__(64) void pack_bitplane_kernel(const void* __restric
       if (!__builtin_isfinite(v)) bad |= 1;
       V[i][e] = v;
     }
-  float sfv[kGroupsPerTile], zfv[kGroupsPerTile];
+  float sfv[kPasses], zfv[kPasses];
 #pragma unroll
-  for (int gi = 0; gi < kGroupsPerTile; ++gi) {
+  for (int gi = 0; gi < kPasses; ++gi) {
     float lo = V[gi * kWordsPerGroup][0], hi = lo;
 #pragma unroll
     for (int ii = 0; ii < kWordsPerGroup; ++ii)
@@ -159,8 +168,10 @@ __global__ __launch_bounds__(64) void pack_bitplane_kernel(const void* __restric
       }
     lo = fminf(lo, __shfl_xor(lo, 16));
     hi = fmaxf(hi, __shfl_xor(hi, 16));
-    lo = fminf(lo, __shfl_xor(lo, 32));
-    hi = fmaxf(hi, __shfl_xor(hi, 32));
+    if (!kPair) {
+      lo = fminf(lo, __shfl_xor(lo, 32));
+      hi = fmaxf(hi, __shfl_xor(hi, 32));
+    }
     lo = __fadd_rn(lo, 0.0f);  // a signed-zero minimum is stored as +0
     const float step = __fdiv_rn(__fsub_rn(hi, lo), levels);
     const float sf = __half2float(__float2half_rn(step));
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(64) void pack_bitplane_kernel(const void* __restric
       word[i] = wd;
     }
 #pragma unroll
-    for (int gi = 0; gi < kGroupsPerTile; ++gi) {
+    for (int gi = 0; gi < kPasses; ++gi) {
       const float sf = sfv[gi];
       // slice b = j + 1: 4^(S-b) = 2^shift; c_b and c_(b-1) (the latter used for b > 1)
       const float cj = __fmul_rn(sf, float((1 << shift) - 1) * 0.5f);
@@ -200,9 +211,9 @@ __global__ __launch_bounds__(64) void pack_bitplane_kernel(const void* __restric
       const __half hs = __float2half_rn(__fmul_rn(sf, float(1 << shift)));
       const __half hz = __float2half_rn(j == 0 ? __fadd_rn(zfv[gi], cj) : __fsub_rn(cj, cp));
       if (__hisinf(hs) || __hisinf(hz) || __hisnan(hs) || __hisnan(hz)) bad |= 2;
-      if (c == 0) {
+      if (kPair ? (c & 1) == 0 : c == 0) {
         const uint32_t pv = uint32_t(__half_as_ushort(hs)) | (uint32_t(__half_as_ushort(hz)) << 16);
-        const size_t g = size_t(kb) * kGroupsPerTile + gi;
+        const size_t g = size_t(kb) * kGroupsPerTile + (kPair ? 2 * gi + (c >> 1) : gi);
         *reinterpret_cast<uint32_t*>(slice + params_offset + ((size_t(nb) * NG + g) * 16 + r) * 4) = pv;
       }
     }
@@ -254,6 +265,7 @@ hipError_t launch_g(const mbq_desc& d, int32_t row0, int32_t rows, const void* w
 hipError_t launch_pack_bitplane(const mbq_desc& d, const void* w, bool w_bf16, void* packed,
                                 int32_t* st, hipStream_t stream) {
   switch (d.group) {
+    case 32: return launch_bp<32>(d, w, w_bf16, packed, st, stream);
     case 64: return launch_bp<64>(d, w, w_bf16, packed, st, stream);
     case 128: return launch_bp<128>(d, w, w_bf16, packed, st, stream);
     default: return launch_bp<256>(d, w, w_bf16, packed, st, stream);
@@ -263,6 +275,7 @@ hipError_t launch_pack_bitplane(const mbq_desc& d, const void* w, bool w_bf16, v
 hipError_t launch_pack(const mbq_desc& d, int32_t row0, int32_t rows, const void* w, bool w_bf16,
                        void* packed, int32_t* st, hipStream_t stream) {
   switch (d.group) {
+    case 32: return launch_g<32>(d, row0, rows, w, w_bf16, packed, st, stream);
     case 64: return launch_g<64>(d, row0, rows, w, w_bf16, packed, st, stream);
     case 128: return launch_g<128>(d, row0, rows, w, w_bf16, packed, st, stream);
     default: return launch_g<256>(d, row0, rows, w, w_bf16, packed, st, stream);

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     // ---- A tile: gather token rows, round to bf16
     {
       uint32_t pk[16];
-      if (src >= 0) {
+      if (src >= 0 && k0 + acol < K) {   // K is a multiple of 32: the 32 inputs are all in or all past
         if (XBF16) {
           const u32x4_t* p = reinterpret_cast<const u32x4_t*>(
               static_cast<const uint16_t*>(x) + size_t(src) * K + k0 + acol);
@@ -100,11 +100,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     }
     // ---- B tile: W^(b) for 128 rows x 64 inputs, summed in float32, rounded to bf16
     {
-      const int kb = k0 >> 8, wi = (k0 & 255) >> 6, g = k0 / G;
+      const int kb = k0 >> 8, wi = (k0 & 255) >> 6;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int L = 2 * (tid & 31) + u;
         const int r = L & 15, c = L >> 4;
+        const int g = (k0 + 16 * c) / G;   // the lane's 16 inputs lie in one group (G >= 32)
         float v[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) v[e] = 0.f;

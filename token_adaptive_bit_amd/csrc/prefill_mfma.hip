@@ -592,7 +592,8 @@ int resident_slots(int32_t slots) {
 
 bool prefill_mfma_supported(const mbq_desc& d, int32_t t, const void* x, bool x_bf16) {
   const uint64_t x_bytes = uint64_t(t) * d.k * (x_bf16 ? 2 : 4);
-  return t > 0 && d.slice_stride < (1ull << 32) && x_bytes < (1ull << 32) &&
+  // groups of 32 inputs are served by the generic kernel
+  return t > 0 && d.group >= 64 && d.slice_stride < (1ull << 32) && x_bytes < (1ull << 32) &&
          (reinterpret_cast<uintptr_t>(x) & 15) == 0;
 }
 
