@@ -62,9 +62,15 @@ typedef enum {
   MBQ_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than mbq_linear_workspace() */
   MBQ_ERR_DEVICE = -5,       /* the HIP launch failed (hipGetLastError) */
   MBQ_ERR_UNSUPPORTED = -6,  /* group, slices, bits or ABI version not supported */
+  /* range markers, never returned: they make every int32 value a valid mbq_status, so a
+     caller's unknown code reaches mbq_status_str without undefined behaviour */
+  MBQ_STATUS_MIN_ = INT32_MIN,
+  MBQ_STATUS_MAX_ = INT32_MAX
 } mbq_status;
 
-typedef enum { MBQ_F32 = 0, MBQ_BF16 = 1 } mbq_dtype;
+/* Element types.  Any other int32 value is MBQ_ERR_ARG (the range markers make it a valid
+   mbq_dtype, so the check itself is defined). */
+typedef enum { MBQ_F32 = 0, MBQ_BF16 = 1, MBQ_DTYPE_MIN_ = INT32_MIN, MBQ_DTYPE_MAX_ = INT32_MAX } mbq_dtype;
 
 /*
  * Kernel and tiling choices of the routed linear, for tests and tuning.  Every call that

@@ -224,6 +224,12 @@ const mbq_opts* checked_opts(const mbq_opts* o) {
   return o;
 }
 
+bool linear_ptrs_ok(const void* packed, const void* x, const int32_t* perm, const int32_t* offsets,
+                    const void* y) {
+  return packed && x && perm && offsets && y && aligned(packed, 256) && aligned(x, 16) && aligned(y, 16) &&
+         aligned(perm, 4) && aligned(offsets, 4);
+}
+
 mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                        mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,
                        const uint16_t* a, const uint16_t* b, int32_t rank, void* y,
@@ -238,10 +244,7 @@ mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, cons
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
   if (rank && !rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
   if (t == 0) return MBQ_OK;  // nothing to compute; t-sized pointers may be NULL
-  if (!packed || !x || !perm || !offsets || !y) return MBQ_ERR_ARG;
-  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 16) || !aligned(perm, 4) ||
-      !aligned(offsets, 4))
-    return MBQ_ERR_ARG;
+  if (!linear_ptrs_ok(packed, x, perm, offsets, y)) return MBQ_ERR_ARG;
   if (rank && (!a || !b || !aligned(a, 16) || !aligned(b, 16))) return MBQ_ERR_ARG;
   const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16, lr = rank > 0;
   const size_t ub = lr ? u_bytes(t, desc->k, rank) : 0, need = ub + linear_ws(*desc, t, xb, lr);
@@ -327,6 +330,7 @@ mbq_status mbq_linear_static(const mbq_desc* desc, const void* packed, int32_t t
   if (!checked_opts(opts)) return MBQ_ERR_ARG;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return MBQ_ERR_ARG;
+  if (t > 0 && !linear_ptrs_ok(packed, x, perm, offsets, y)) return MBQ_ERR_ARG;  // before any device call
   const size_t need = t > 0 ? linear_ws(*desc, t, x_dtype == MBQ_BF16, false) : 0;
   if (need > kStaticScratchBytes) return MBQ_ERR_WORKSPACE;
   void* ws = nullptr;
