@@ -300,9 +300,9 @@ def bench_sweep(api, torch, inputs, dev, iters=20):
                 api.linear(blobs[i % nb], X, perm, off, y=y)
             torch.cuda.synchronize()
             fn = lambda i: api.linear(blobs[i % nb], X, perm, off, y=y)
-            # decode launches from HIP-graph replays (no host submission between them), the
-            # prefill's long launches eagerly
-            s = graph_steps(torch, fn, nb, iters, 10)[1] if T <= 64 else time_events(torch, fn, iters)
+            # decode launches from replays of graphs that hold one launch per weight copy (no
+            # host submission between launches), the prefill's long launches eagerly
+            s = graph_steps(torch, fn, nb, nb * max(2, -(-iters // nb)), nb)[1] if T <= 64 else time_events(torch, fn, iters)
             counts = torch.diff(off).cpu().tolist()
             jmax = max(j + 1 for j in range(3) if counts[j] > 0)
             r = {"us": s * 1e6, "tokens_per_s": T / s, "budget_counts": counts,
@@ -399,14 +399,16 @@ def bench_bitplane(api, torch, inputs, dev):
 
 def bench_lowrank(api, torch, inputs, dev, iters=30):
     """The low-rank side path (rank 16) on the decode workload (T = 16) and the prefill
-    workload (T = 2048): routed linear with and without it, and u = x A^T alone."""
+    workload (T = 2048): routed linear with and without it over rotated weight copies
+    (decode from graph replays, prefill eagerly)."""
     out = {}
     for cfg, T in ((2, 16), (3, 2048)):
         d = inputs.make_config(cfg)
         N, K = d["N"], d["K"]
         W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
-        p = api.pack(W, 128, 3)
+        blobs = make_blobs(api, torch, W, 128, 3, dev)
         del W
+        nb = len(blobs)
         X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
         if d["budget"] is not None:
             perm, off = api.regroup(torch.from_numpy(d["budget"]).to(dev), 3)
@@ -416,24 +418,27 @@ def bench_lowrank(api, torch, inputs, dev, iters=30):
         A = torch.from_numpy(lr["A"]).to(dev, torch.bfloat16)
         B = torch.from_numpy(lr["B"]).to(dev, torch.bfloat16)
         y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-        ws0 = torch.empty(max(1, api.linear_workspace(p, T)), dtype=torch.uint8, device=dev)
-        ws1 = torch.empty(max(1, api.linear_lowrank_workspace(p, T, 16)), dtype=torch.uint8, device=dev)
-        plain = lambda i: api.linear(p, X, perm, off, y=y, workspace=ws0)
-        side = lambda i: api.linear_lowrank(p, X, perm, off, A, B, y=y, workspace=ws1)
+        ws0 = torch.empty(max(1, api.linear_workspace(blobs[0], T)), dtype=torch.uint8, device=dev)
+        ws1 = torch.empty(max(1, api.linear_lowrank_workspace(blobs[0], T, 16)), dtype=torch.uint8, device=dev)
+        plain = lambda i: api.linear(blobs[i % nb], X, perm, off, y=y, workspace=ws0)
+        side = lambda i: api.linear_lowrank(blobs[i % nb], X, perm, off, A, B, y=y, workspace=ws1)
         for f in (plain, side):
             for i in range(3):
                 f(i)
         torch.cuda.synchronize()
-        t0 = time_events(torch, plain, iters)
-        t1 = time_events(torch, side, iters)
-        res = {"N": N, "K": K, "T": T, "rank": 16, "linear_us": t0 * 1e6, "linear_lowrank_us": t1 * 1e6,
-               "overhead_frac": t1 / t0 - 1.0}
         if T <= 64:
-            g0 = graph_time(torch, lambda: plain(0))
-            g1 = graph_time(torch, lambda: side(0))
-            res.update({"linear_us_graph": g0 * 1e6, "linear_lowrank_us_graph": g1 * 1e6})
-        out[f"t{T}_{N}x{K}"] = res
-        del p
+            steps = nb * max(2, -(-iters // nb))
+            t0 = graph_steps(torch, plain, nb, steps, nb)[1]
+            t1 = graph_steps(torch, side, nb, steps, nb)[1]
+            how = "graph"
+        else:
+            t0 = time_events(torch, plain, iters)
+            t1 = time_events(torch, side, iters)
+            how = "eager"
+        out[f"t{T}_{N}x{K}"] = {"N": N, "K": K, "T": T, "rank": 16, "copies": nb, "timing": how,
+                                "linear_us": t0 * 1e6, "linear_lowrank_us": t1 * 1e6,
+                                "overhead_frac": t1 / t0 - 1.0}
+        del blobs
     return out
 
 
@@ -555,6 +560,7 @@ def main():
         sys.exit(1)
 
     if args.only == "prefill":
+        bench_copy(torch, dev)          # a copy of known size first: the counter passes' calibration
         r = bench_prefill(api, torch, inputs, dev, iters=max(args.steps, 1))
         print(json.dumps({"workload": "prefill", **r}))
         return

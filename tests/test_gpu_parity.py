@@ -403,6 +403,21 @@ def test_prefill_every_variant(mbq, G, S, dtype, generic):
     assert token_errors(yg, yref).max() <= TOL
 
 
+@pytest.mark.parametrize("G,S", [(64, 2), (64, 3), (128, 3), (128, 4), (256, 2), (256, 4)])
+@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (40, "bf16"), (16, "f32")])
+def test_decode_single_slice(mbq, G, S, T, dtype):
+    """Every token at budget 1 (the one-slice instantiation of the streaming loop, the
+    other slices' loads out of range).  2307 row blocks (ragged N) give every workgroup
+    about nine, so every buffer rotation and a ragged last round are crossed; every
+    output row is compared."""
+    say(f"single-slice decode G={G} S={S} T={T} {dtype}")
+    d = inputs.make_linear(G + S + T, 36904, 512, T, group=G, slices=S, dtype=dtype)
+    yg, yref, _ = run_linear(mbq, d, np.ones(T, np.int32))
+    err = token_errors(yg, yref)
+    say(f"  max token error {err.max():.3e}")
+    assert err.max() <= TOL
+
+
 def test_decode_step_graph_replays_match_eager(mbq):
     """The decode step (route + routed linear) captured in a HIP graph and replayed
     several times, with eager work in between, gives exactly the eager outputs."""

@@ -207,3 +207,16 @@ def test_route_prepare_then_prepared(mbq, G, S, K, T):
     deq = O.dequant_slices(pk["codes"], pk["scale"], pk["zero"], G)
     assert token_errors(got2[0].cpu().numpy(), O.linear(d["X"], deq, b2)).max() <= TOL
 
+
+
+@pytest.mark.parametrize("T,mul,launches", [(1, None, 0), (4, None, 0), (16, None, 0), (16, "bf16", 0),
+                                            (16, "fp8fp4", 1)])
+def test_route_linear_single_slice(mbq, T, mul, launches):
+    """Router columns all equal: every logit ties, every token takes budget 1 (the first
+    argmax), and the step streams one slice after routing in the kernel (one launch) or
+    on prepared operands (two launches).  2307 row blocks; every row."""
+    say(f"route_linear single slice T={T} mul={mul} launches={launches}")
+    d = inputs.make_linear(500 + T, 36904, 1024, T, group=128, slices=3, dtype="bf16")
+    d["Wr"] = np.repeat(d["Wr"][:, :1], 3, axis=1)
+    run_case(mbq, 36904, 1024, 128, 3, T, "bf16", 0, mul=mul, d=d, launches=launches,
+             f4=(mul == "fp8fp4" or (mul is None and T >= 4)))
