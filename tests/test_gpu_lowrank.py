@@ -110,3 +110,13 @@ def test_lowrank_generic_kernels(mbq, T):
 def test_lowrank_generic_decode_g64_s4_f32(mbq):
     """Group 64, 4 slices, float32 activations: only the generic decode takes it."""
     check(*run(mbq, 64, 512, 64, 4, 16, "f32", 16, seed=8))
+
+
+@pytest.mark.parametrize("K,dtype,rank", [(2304, "bf16", 8), (2304, "bf16", 16), (2304, "f32", 16),
+                                          (1280, "f32", 8), (4096, "bf16", 16), (8192, "bf16", 16),
+                                          (2304, "bf16", 32)])
+def test_lowrank_decode_tiles_chunks_ranks(mbq, K, dtype, rank):
+    """The decode side path across one and two k tiles per wave, K within one workgroup
+    and split over workgroups (8192), both activation types and ranks 8, 16 and 32."""
+    say(f"lowrank u placement K={K} {dtype} r={rank}")
+    check(*run(mbq, 130, K, 128, 3, 16, dtype, rank, seed=K + rank))
