@@ -220,3 +220,48 @@ def test_route_linear_single_slice(mbq, T, mul, launches):
     d["Wr"] = np.repeat(d["Wr"][:, :1], 3, axis=1)
     run_case(mbq, 36904, 1024, 128, 3, T, "bf16", 0, mul=mul, d=d, launches=launches,
              f4=(mul == "fp8fp4" or (mul is None and T >= 4)))
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_route_linear_graph_replays_match_eager(mbq, T):
+    """The routed step captured in a HIP graph (one launch at 4 tokens, two at 16: the
+    operands prepared in the workspace first) and replayed several times, with eager work
+    in between, writes exactly the eager outputs: y, logits, budget, perm and offsets."""
+    say(f"route_linear graph replays T={T}")
+    d = inputs.make_linear(70 + T, 16400, 1280, T, group=128, slices=3, dtype="bf16")
+    x = to_dev(d["X"], torch.bfloat16)
+    wr = to_dev(d["Wr"], torch.float32)
+    p = mbq.pack(to_dev(d["W"], torch.bfloat16), group=128, slices=3)
+    outs = dict(y=torch.empty((T, 16400), dtype=torch.bfloat16, device=DEV),
+                logits=torch.empty((T, 3), dtype=torch.float32, device=DEV),
+                budget=torch.empty(T, dtype=torch.int32, device=DEV),
+                perm=torch.empty(T, dtype=torch.int32, device=DEV),
+                offsets=torch.empty(4, dtype=torch.int32, device=DEV))
+    ws = torch.empty(max(1, mbq.route_linear_workspace(p, T)), dtype=torch.uint8, device=DEV)
+
+    def step():
+        mbq.route_linear(p, x, wr, workspace=ws, **outs)
+
+    step()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        for v in outs.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], want[k]), k
+        step()                       # eager work between replays
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], want[k]), k

@@ -434,8 +434,9 @@ def route_linear(p: PackedLinear, x: torch.Tensor, wr: torch.Tensor, out_dtype: 
                  y: torch.Tensor | None = None, logits=None, budget=None, perm=None, offsets=None,
                  workspace: torch.Tensor | None = None, options: MbqOpts | None = None):
     """One decode step: route (logits x . wr, budgets, stable regroup) and the routed linear.
-    Returns (y, logits, budget, perm, offsets); one launch for bfloat16 x and t <= 16 when
-    K fits one workgroup, else route then linear."""
+    Returns (y, logits, budget, perm, offsets).  For bfloat16 x, t <= 16 and K within one
+    workgroup: one launch up to 4 tokens, two from 5 (the fp8 operands prepared once in the
+    workspace); otherwise route, then linear."""
     _dev(x, "x")
     if x.dim() != 2:
         raise ValueError("x must be 2-D [t, k]")
