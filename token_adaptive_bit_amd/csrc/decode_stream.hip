@@ -1017,19 +1017,20 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   stream(std::integral_constant<int, S>{});
 }
 
-// The first launch of the two-launch decode step (PA): one wave per k tile of 256 inputs
-// prepares what every workgroup of the streaming kernel would otherwise derive from the
-// raw activations on its own: the tile's fp8 A operands (prep_a_f4), their group sums
-// (the same instruction against all-ones codes) and the tile's partial router logits
-// (Wr as three exact bfloat16 planes on the bf16 matrix instruction, as in the in-kernel
-// routing).  bfloat16 x [t x K], t <= 16; tokens past t repeat the last one (their rows
-// are never used).  Output layout: PrepLayout.
+// The first launch of the two-launch decode step (PA): two waves per k tile of 256 inputs
+// prepare what every workgroup of the streaming kernel would otherwise derive from the
+// raw activations on its own.  Wave 1 takes the tile's fp8 A operands (prep_a_f4) and
+// their group sums (the same instruction against all-ones codes); wave 0, in parallel, the
+// tile's partial router logits (Wr as three exact bfloat16 planes on the bf16 matrix
+// instruction, as in the in-kernel routing).  bfloat16 x [t x K], t <= 16; tokens past t
+// repeat the last one (their rows are never used).  Output layout: PrepLayout.
 template <int G, int S>
-__global__ __launch_bounds__(64) void decode_prep_kernel(const uint8_t* __restrict__ x, int T, int K, int KB,
-                                                         const float* __restrict__ wr, uint8_t* __restrict__ prep) {
+__global__ __launch_bounds__(128) void decode_prep_kernel(const uint8_t* __restrict__ x, int T, int K, int KB,
+                                                          const float* __restrict__ wr, uint8_t* __restrict__ prep) {
   asm volatile("" ::"s"(x), "s"(wr), "s"(prep), "s"(T), "s"(K), "s"(KB));
   constexpr int GPT = 256 / G;
-  const int t = blockIdx.x, lane = threadIdx.x, r = lane & 15, c = lane >> 4;
+  const int t = blockIdx.x, lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int xr = min(r, T - 1);
   auto xk = [&](int i, int h) { return 128 * (i >> 1) + 64 * (c & 1) + 16 * (c >> 1) + 32 * (i & 1) + 8 * h; };
   u32x4_t a[4][2];
@@ -1040,45 +1041,58 @@ __global__ __launch_bounds__(64) void decode_prep_kernel(const uint8_t* __restri
       const int k = t * 256 + xk(i, h);
       a[i][h] = ldg16(x + (size_t(xr) * K + (k < K ? k : 0)) * 2);   // past K: zeroed below
     }
-  const __amdgpu_buffer_rsrc_t rw = slice_rsrc(reinterpret_cast<const uint8_t*>(wr), uint32_t(K) * S * 4);
-  u32x4_t wl[S];
+  const PrepLayout pl(KB, G);
+  if (wv == 0) {
+    const __amdgpu_buffer_rsrc_t rw = slice_rsrc(reinterpret_cast<const uint8_t*>(wr), uint32_t(K) * S * 4);
+    u32x4_t wl[S];
 #pragma unroll
-  for (int q = 0; q < S; ++q)
-    wl[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t(t) * 256 * S + (64 * q + lane) * 4) * 4, 0, 0));
+    for (int q = 0; q < S; ++q)
+      wl[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t(t) * 256 * S + (64 * q + lane) * 4) * 4, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (t * 256 + xk(i, h) >= K) a[i][h] = u32x4_t{0u, 0u, 0u, 0u};
+    // Wr rows of the tile as three bf16 planes, column-major (plane, logit, input), in LDS;
+    // logits^T = Wr^T x^T with the activations as the B operand (see the in-kernel routing)
+    __shared__ __align__(16) uint16_t wrp[3][4][256 + 8];
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; u += 2) {
+        const int f = 4 * (64 * q + lane) + u;
+        const float a0 = __uint_as_float(wl[q][u]), b0 = __uint_as_float(wl[q][u + 1]);
+        const uint32_t p0 = pk_bf16(a0, b0);
+        const float a1 = a0 - __uint_as_float(p0 << 16), b1 = b0 - __uint_as_float(p0 & 0xFFFF0000u);
+        const uint32_t p1 = pk_bf16(a1, b1);
+        const uint32_t p2 = pk_bf16(a1 - __uint_as_float(p1 << 16), b1 - __uint_as_float(p1 & 0xFFFF0000u));
+        wrp[0][f % S][f / S] = uint16_t(p0);
+        wrp[1][f % S][f / S] = uint16_t(p1);
+        wrp[2][f % S][f / S] = uint16_t(p2);
+        wrp[0][(f + 1) % S][(f + 1) / S] = uint16_t(p0 >> 16);
+        wrp[1][(f + 1) % S][(f + 1) / S] = uint16_t(p1 >> 16);
+        wrp[2][(f + 1) % S][(f + 1) / S] = uint16_t(p2 >> 16);
+      }
+    const int jr = min(r & 3, S - 1);
+    f32x4_t Lp[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int pn = 0; pn < 3; ++pn)
+          Lp[pn] = mfma(*reinterpret_cast<const u32x4_t*>(&wrp[pn][jr][xk(i, h)]), a[i][h], Lp[pn]);
+    chain_fence();
+    const f32x4_t L = (Lp[2] + Lp[1]) + Lp[0];
+    // lanes (n, 0) hold token n's logits
+    if (c == 0) reinterpret_cast<f32x4_t*>(prep + pl.lg)[size_t(t) * 16 + r] = L;
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       if (t * 256 + xk(i, h) >= K) a[i][h] = u32x4_t{0u, 0u, 0u, 0u};
-  // Wr rows of the tile as three bf16 planes, column-major (plane, logit, input), in LDS;
-  // logits^T = Wr^T x^T with the activations as the B operand (see the in-kernel routing)
-  __shared__ __align__(16) uint16_t wrp[3][4][256 + 8];
-#pragma unroll
-  for (int q = 0; q < S; ++q)
-#pragma unroll
-    for (int u = 0; u < 4; u += 2) {
-      const int f = 4 * (64 * q + lane) + u;
-      const float a0 = __uint_as_float(wl[q][u]), b0 = __uint_as_float(wl[q][u + 1]);
-      const uint32_t p0 = pk_bf16(a0, b0);
-      const float a1 = a0 - __uint_as_float(p0 << 16), b1 = b0 - __uint_as_float(p0 & 0xFFFF0000u);
-      const uint32_t p1 = pk_bf16(a1, b1);
-      const uint32_t p2 = pk_bf16(a1 - __uint_as_float(p1 << 16), b1 - __uint_as_float(p1 & 0xFFFF0000u));
-      wrp[0][f % S][f / S] = uint16_t(p0);
-      wrp[1][f % S][f / S] = uint16_t(p1);
-      wrp[2][f % S][f / S] = uint16_t(p2);
-      wrp[0][(f + 1) % S][(f + 1) / S] = uint16_t(p0 >> 16);
-      wrp[1][(f + 1) % S][(f + 1) / S] = uint16_t(p1 >> 16);
-      wrp[2][(f + 1) % S][(f + 1) / S] = uint16_t(p2 >> 16);
-    }
-  const int jr = min(r & 3, S - 1);
-  f32x4_t Lp[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int pl = 0; pl < 3; ++pl)
-        Lp[pl] = mfma(*reinterpret_cast<const u32x4_t*>(&wrp[pl][jr][xk(i, h)]), a[i][h], Lp[pl]);
   // fp8 pairs and scales of the two 128-input blocks, then their group sums
   AF4 af[2];
 #pragma unroll
@@ -1099,8 +1113,6 @@ __global__ __launch_bounds__(64) void decode_prep_kernel(const uint8_t* __restri
     }
   }
   chain_fence();
-  const f32x4_t L = (Lp[2] + Lp[1]) + Lp[0];
-  const PrepLayout pl(KB, G);
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(prep + pl.a) + (size_t(t) * 8 + 4 * m) * 64 + lane;
@@ -1110,13 +1122,12 @@ __global__ __launch_bounds__(64) void decode_prep_kernel(const uint8_t* __restri
     dst[192] = u32x4_t{uint32_t(af[m].lo[4]), uint32_t(af[m].lo[5]), uint32_t(af[m].lo[6]), uint32_t(af[m].lo[7])};
   }
   reinterpret_cast<uint2*>(prep + pl.sc)[size_t(t) * 64 + lane] = make_uint2(af[0].sc, af[1].sc);
-  // lanes (0, c) hold the group sums of tokens 4c .. 4c + 3; lanes (n, 0) token n's logits
+  // lanes (0, c) hold the group sums of tokens 4c .. 4c + 3
   if (r == 0) {
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi)
       *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(prep + pl.xs) + (size_t(t) * GPT + gi) * 16 + 4 * c) = xs[gi];
   }
-  if (c == 0) reinterpret_cast<f32x4_t*>(prep + pl.lg)[size_t(t) * 16 + r] = L;
 }
 
 // Sums the k chunks' float32 partials in a fixed order (deterministic) and writes y.
@@ -1282,7 +1293,7 @@ hipError_t launch_prep_g(const mbq_desc& d, int32_t t, const void* x, const floa
                          hipStream_t stream) {
   const auto x8 = static_cast<const uint8_t*>(x);
   auto p8 = static_cast<uint8_t*>(prep);
-  const dim3 grid(d.k_tiles), block(64);
+  const dim3 grid(d.k_tiles), block(128);   // per k tile: a routing wave and an fp8 wave
   switch (d.slices) {
     case 2: hipLaunchKernelGGL((decode_prep_kernel<G, 2>), grid, block, 0, stream, x8, t, d.k, d.k_tiles, wr, p8); break;
     case 3: hipLaunchKernelGGL((decode_prep_kernel<G, 3>), grid, block, 0, stream, x8, t, d.k, d.k_tiles, wr, p8); break;
