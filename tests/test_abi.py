@@ -326,6 +326,11 @@ def test_route_prepare_validation():
     st1, d1 = desc(200, 640, 128, 1)            # one slice: no fp8 x fp4 step
     assert L.mbq_route_prepare_workspace(ctypes.byref(d1), 16, ctypes.byref(n)) == OK and n.value == 0
     assert L.mbq_route_prepare(ctypes.byref(d1), 16, f, f, f, need, None) == UNSUP
+    st2, d2 = desc(200, 640, 32, 3)             # groups of 32: the generic kernels only
+    assert st2 == OK
+    assert L.mbq_route_prepare_workspace(ctypes.byref(d2), 16, ctypes.byref(n)) == OK and n.value == 0
+    assert L.mbq_route_prepare(ctypes.byref(d2), 16, f, f, f, need, None) == UNSUP
+    assert L.mbq_linear_workspace(ctypes.byref(d2), 16, BF16, ctypes.byref(n)) == OK and n.value == 0
 
 
 def test_linear_static_limits():
