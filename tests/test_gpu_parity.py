@@ -456,3 +456,16 @@ def test_decode_step_graph_replays_match_eager(mbq):
         step()                       # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(y, want)
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 3, 4])
+def test_linear_small_every_variant(mbq, G, S, T):
+    """mbq_linear for 1 to 4 tokens: every group / slice count, budgets mixed over all
+    slices, ragged N, 9 k tiles."""
+    say(f"linear small G={G} S={S} T={T}")
+    d = inputs.make_linear(G + S + T + 900, 300, 2304, T, group=G, slices=S, dtype="bf16")
+    budget = (np.arange(T) % S + 1).astype(np.int32)[::-1].copy()
+    yg, yref, _ = run_linear(mbq, d, budget)
+    assert token_errors(yg, yref).max() <= TOL

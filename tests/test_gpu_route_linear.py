@@ -9,8 +9,9 @@ Bars (as for mbq_route and mbq_linear called apart):
   * y within the per-token bar of 1e-2 against the float64 oracle on those budgets.
 Where budgets agree with the two-call path (mbq_route, then mbq_linear), y must equal its
 y bit for bit (the in-kernel routing changes where budgets come from, not the products),
-except on the fp8 x fp4 multiply (mbq_opts decode_mul, chosen by the plan from 4 row blocks
-per workgroup), a different summation whose y must stay within 1e-3 per token of it.
+except on the fp8 x fp4 multiply (mbq_opts decode_mul, chosen by the plan from 4 tokens and
+4 row blocks per workgroup), a different summation whose y must stay within 1e-3 per token
+of it.
 """
 import numpy as np
 import pytest
@@ -265,3 +266,24 @@ def test_route_linear_graph_replays_match_eager(mbq, T):
         torch.cuda.synchronize()
         for k in outs:
             assert torch.equal(outs[k], want[k]), k
+
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_route_linear_small_every_variant(mbq, G, S, T):
+    """The plan's routed step for 1 to 4 tokens (one launch; the fp8 x fp4 multiply from 4
+    tokens where a workgroup streams 4 row blocks): every group / slice count / token count,
+    ragged N, K over 9 k tiles, router-mixed budgets."""
+    say(f"route_linear small G={G} S={S} T={T}")
+    run_case(mbq, 300, 2304, G, S, T, "bf16", seed=G + 10 * S + T, mul=None, f4=True)
+
+
+@pytest.mark.parametrize("N,K,G,S,T", [(64, 13824, 128, 3, 1), (40, 256, 64, 2, 3), (17, 768, 256, 4, 4),
+                                       (2048, 4096, 128, 3, 4)])
+def test_route_linear_small_shapes(mbq, N, K, G, S, T):
+    """The routed step for 1 to 4 tokens on a long K (54 k tiles: split over workgroups, so
+    route then linear), a single tile, a row block that is mostly padding, and 128 row
+    blocks."""
+    say(f"route_linear small N={N} K={K} G={G} S={S} T={T}")
+    run_case(mbq, N, K, G, S, T, "bf16", seed=N + K + T, mul=None, f4=True)
