@@ -17,7 +17,7 @@ Sources (the pages; cited by title and section):
     (R_1 = W, W_e = Q(R_e), R_{e+1} = R_e - W_e, and W^(b) = sum of the slices) and
     section 2.2 MoBiRoute.
 
-Readings where the pages leave a step open (each one is listed in the design doc):
+Readings where the pages leave a step open:
   * Q is 2-bit asymmetric min/max round-to-nearest per group of G consecutive inputs of
     one output row: scale = (max - min) / 3, zero = min, both stored as IEEE half, codes
     = clamp(rint((r - zero) / scale), 0, 3) computed with the *stored* (rounded) params,
