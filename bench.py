@@ -185,7 +185,7 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev, variants=True):
     """The decode step on the 18944 x 3584 workload: route (logits, argmax, regroup) and the
     routed linear through mbq_route_linear with the plan's choices; its dominant kernel (the
     streaming linear) timed alone on prepared operands; and the step's other forms."""
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
     Wr = torch.from_numpy(d["Wr"]).to(dev, torch.float32)
@@ -243,7 +243,7 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev, variants=True):
 
 
 def bench_pack(api, torch, inputs, dev):
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     out = torch.empty(int(api.describe(d["N"], d["K"], 128, 3).total_bytes), dtype=torch.uint8, device=dev)
     api.pack(W, 128, 3, out=out)
@@ -252,7 +252,7 @@ def bench_pack(api, torch, inputs, dev):
 
 
 def bench_prefill(api, torch, inputs, dev, iters=20):
-    d = inputs.make_config(3)
+    d = inputs.make_workload("prefill_11008x4096")
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     X = torch.from_numpy(d["X"]).to(dev, torch.bfloat16)
     budget = torch.from_numpy(d["budget"]).to(dev)
@@ -281,7 +281,7 @@ def bench_copy(torch, dev, nbytes=1 << 30):
 def bench_sweep(api, torch, inputs, dev, iters=20):
     """Elasticity sweep, W 14336 x 4096: T in {32, 1024}, budgets forced to 1, 2, 3 and
     router-mixed; bytes of weight read and throughput for each."""
-    d = inputs.make_config(5)
+    d = inputs.make_workload("sweep_14336x4096")
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     blobs = make_blobs(api, torch, W, 128, 3, dev)
     del W
@@ -373,7 +373,7 @@ def bench_bitplane(api, torch, inputs, dev):
     """Residual slices against bit-plane slices on the decode weight (18944 x 3584, G128,
     S3): relative error of x . W^(b)^T against the float32 product x . W^T for each b
     (every token forced to b), the routed linear's time on each blob, and pack times."""
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     T = 16
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
@@ -402,8 +402,8 @@ def bench_lowrank(api, torch, inputs, dev, iters=30):
     workload (T = 2048): routed linear with and without it over rotated weight copies
     (decode from graph replays, prefill eagerly)."""
     out = {}
-    for cfg, T in ((2, 16), (3, 2048)):
-        d = inputs.make_config(cfg)
+    for name, T, seed in (("decode_18944x3584", 16, 102), ("prefill_11008x4096", 2048, 103)):
+        d = inputs.make_workload(name)
         N, K = d["N"], d["K"]
         W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
         blobs = make_blobs(api, torch, W, 128, 3, dev)
@@ -414,7 +414,7 @@ def bench_lowrank(api, torch, inputs, dev, iters=30):
             perm, off = api.regroup(torch.from_numpy(d["budget"]).to(dev), 3)
         else:
             _, _, perm, off = api.route(X, torch.from_numpy(d["Wr"]).to(dev, torch.float32))
-        lr = inputs.make_lowrank(cfg + 100, N, K, rank=16)
+        lr = inputs.make_lowrank(seed, N, K, rank=16)
         A = torch.from_numpy(lr["A"]).to(dev, torch.bfloat16)
         B = torch.from_numpy(lr["B"]).to(dev, torch.bfloat16)
         y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
@@ -447,11 +447,11 @@ def bench_layer(api, torch, inputs, dev, iters=20):
     input: total time of route + 7 routed linears, and HBM fraction of the linears; then
     the same layer with q/k/v and gate/up fused (one blob and one launch per shared input):
     route + 4 routed linears."""
-    cfg = inputs.make_config(4)
-    T = cfg["T"]
-    x0 = torch.from_numpy(cfg["X_layer"]).to(dev, torch.bfloat16)
-    Wr = torch.from_numpy(cfg["Wr"]).to(dev, torch.float32)
-    lin = {l["name"]: l for l in cfg["linears"]}
+    lay = inputs.make_workload("layer14b_t64")
+    T = lay["T"]
+    x0 = torch.from_numpy(lay["X_layer"]).to(dev, torch.bfloat16)
+    Wr = torch.from_numpy(lay["Wr"]).to(dev, torch.float32)
+    lin = {l["name"]: l for l in lay["linears"]}
     Wd = {n: torch.from_numpy(l["W"]).to(dev, torch.bfloat16) for n, l in lin.items()}
     Xd = {n: torch.from_numpy(l["X"]).to(dev, torch.bfloat16) for n, l in lin.items()}
     _, _, perm, off = api.route(x0, Wr)
@@ -495,7 +495,7 @@ def run_traffic(api, torch, inputs, dev, T, launches=20):
     """For the counter passes: a copy of 1 GiB (known bytes), then `launches` decode steps
     (mbq_route_linear, the plan's path) over rotated weight copies."""
     bench_copy(torch, dev)
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     W = torch.from_numpy(d["W"]).to(dev, torch.bfloat16)
     X = torch.from_numpy(d["X"][:T]).to(dev, torch.bfloat16)
     Wr = torch.from_numpy(d["Wr"]).to(dev, torch.float32)
@@ -523,7 +523,7 @@ def cpu_baseline(inputs, T):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     rows = 4736                                  # a quarter of the 18944 output rows
     p = O.pack(d["W"][:rows], 128, 3)
     X = d["X"][:T]

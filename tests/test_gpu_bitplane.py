@@ -98,7 +98,7 @@ def test_pack_bitplane_status_flags(mbq):
 
 def test_pack_bitplane_full_decode_weight(mbq):
     say("bitplane pack full 18944x3584")
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     want, _ = oracle_bp_blob(d["W"], 128, 3)
     p, st = gpu_bp(mbq, d["W"], 128, 3, "bf16")
     assert st == 0

@@ -81,25 +81,25 @@ def check_routes(logits, budget, perm, off, X, Wr, S):
 
 # ---------------------------------------------------------------- decode GEMV 18944 x 3584
 @pytest.fixture(scope="module")
-def cfg2(mbq):
+def decode_w(mbq):
     say("packing the 18944 x 3584 decode weight (oracle and GPU)")
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     pw = Packed(mbq, d["W"])
     yield d, pw
     del pw
 
 
-def test_cfg2_blob_bitexact(cfg2):
-    cfg2[1].check_blob()
+def test_decode_18944x3584_blob_bitexact(decode_w):
+    decode_w[1].check_blob()
 
 
 @pytest.mark.parametrize("T", [1, 4, 16])
 @pytest.mark.parametrize("mul,launches", [(None, 0), ("bf16", 1), ("fp8fp4", 1), ("fp8fp4", 2)])
-def test_cfg2_route_linear_every_row(mbq, cfg2, T, mul, launches):
+def test_decode_18944x3584_route_linear_every_row(mbq, decode_w, T, mul, launches):
     """The decode step in one call (the benchmark's step) on the workload's own inputs, on
     the plan's choices and on each multiply and launch count forced."""
-    d, pw = cfg2
-    say(f"cfg2 route_linear T={T} decode_mul={mul} launches={launches}")
+    d, pw = decode_w
+    say(f"decode 18944x3584 route_linear T={T} decode_mul={mul} launches={launches}")
     X = d["X"][:T]
     y, lg, b, perm, off = mbq.route_linear(pw.p, to_dev(X, torch.bfloat16), to_dev(d["Wr"], torch.float32),
                                            options=mbq.opts(decode_mul=mul, decode_launches=launches))
@@ -109,11 +109,11 @@ def test_cfg2_route_linear_every_row(mbq, cfg2, T, mul, launches):
 
 
 @pytest.mark.parametrize("T", [1, 4, 16, 17, 33, 64])
-def test_cfg2_two_call_every_row(mbq, cfg2, T):
+def test_decode_18944x3584_two_call_every_row(mbq, decode_w, T):
     """mbq_route then mbq_linear for every decode batch size (two 16-token blocks per
     workgroup above 32 tokens)."""
-    d, pw = cfg2
-    say(f"cfg2 route + linear T={T}")
+    d, pw = decode_w
+    say(f"decode 18944x3584 route + linear T={T}")
     X = d["X"][:T] if T <= 16 else inputs.make_linear(2, 8, 3584, T)["X"]
     x = to_dev(X, torch.bfloat16)
     lg, b, perm, off = mbq.route(x, to_dev(d["Wr"], torch.float32))
@@ -124,9 +124,9 @@ def test_cfg2_two_call_every_row(mbq, cfg2, T):
 
 
 # ---------------------------------------------------------------- prefill 11008 x 4096
-def test_cfg3_prefill_every_row(mbq):
-    say("cfg3 prefill 11008 x 4096, T = 2048, forced 614 / 1024 / 410")
-    d = inputs.make_config(3)
+def test_prefill_11008x4096_every_row(mbq):
+    say("prefill 11008 x 4096, T = 2048, forced 614 / 1024 / 410")
+    d = inputs.make_workload("prefill_11008x4096")
     pw = Packed(mbq, d["W"])
     pw.check_blob()
     perm, off = mbq.regroup(to_dev(d["budget"], torch.int32), 3)
@@ -134,28 +134,28 @@ def test_cfg3_prefill_every_row(mbq):
     torch.cuda.synchronize()
     assert off.cpu().tolist() == [0, 614, 1638, 2048]
     assert np.array_equal(budget_from_perm(perm.cpu().numpy(), off.cpu().numpy()), d["budget"])
-    compare(y, pw.yref(d["X"], d["budget"]), what="cfg3")
+    compare(y, pw.yref(d["X"], d["budget"]), what="prefill_w")
 
 
 # ---------------------------------------------------------------- elasticity sweep 14336 x 4096
 @pytest.fixture(scope="module")
-def cfg5(mbq):
+def sweep_w(mbq):
     say("packing the 14336 x 4096 sweep weight (oracle and GPU)")
-    d = inputs.make_config(5)
+    d = inputs.make_workload("sweep_14336x4096")
     pw = Packed(mbq, d["W"])
     yield d, pw
     del pw
 
 
-def test_cfg5_blob_bitexact(cfg5):
-    cfg5[1].check_blob()
+def test_sweep_14336x4096_blob_bitexact(sweep_w):
+    sweep_w[1].check_blob()
 
 
 @pytest.mark.parametrize("T", [32, 1024])
 @pytest.mark.parametrize("mode", ["b1", "b2", "b3", "router"])
-def test_cfg5_sweep_every_row(mbq, cfg5, T, mode):
-    d, pw = cfg5
-    say(f"cfg5 T={T} {mode}")
+def test_sweep_14336x4096_every_row(mbq, sweep_w, T, mode):
+    d, pw = sweep_w
+    say(f"sweep 14336x4096 T={T} {mode}")
     X = d["X"][:T]
     x = to_dev(X, torch.bfloat16)
     if mode == "router":
@@ -172,20 +172,20 @@ def test_cfg5_sweep_every_row(mbq, cfg5, T, mode):
 
 # ---------------------------------------------------------------- 14B-like layer, T = 64
 @pytest.fixture(scope="module")
-def cfg4(mbq):
-    cfg = inputs.make_config(4)
-    x0 = to_dev(cfg["X_layer"], torch.bfloat16)
-    lg, b, perm, off = mbq.route(x0, to_dev(cfg["Wr"], torch.float32))
+def layer_w(mbq):
+    lay = inputs.make_workload("layer14b_t64")
+    x0 = to_dev(lay["X_layer"], torch.bfloat16)
+    lg, b, perm, off = mbq.route(x0, to_dev(lay["Wr"], torch.float32))
     torch.cuda.synchronize()
-    budget = check_routes(lg, b, perm, off, cfg["X_layer"], cfg["Wr"], 3)
-    return cfg, perm, off, budget
+    budget = check_routes(lg, b, perm, off, lay["X_layer"], lay["Wr"], 3)
+    return lay, perm, off, budget
 
 
-def test_cfg4_layer_every_row(mbq, cfg4):
+def test_layer14b_every_row(mbq, layer_w):
     """The seven linears one by one: blob bytes and every output row."""
-    cfg, perm, off, budget = cfg4
-    for lin in cfg["linears"]:
-        say(f"cfg4 {lin['name']} {lin['W'].shape}")
+    lay, perm, off, budget = layer_w
+    for lin in lay["linears"]:
+        say(f"layer14b {lin['name']} {lin['W'].shape}")
         pw = Packed(mbq, lin["W"])
         pw.check_blob()
         y = mbq.linear(pw.p, to_dev(lin["X"], torch.bfloat16), perm, off)
@@ -194,14 +194,14 @@ def test_cfg4_layer_every_row(mbq, cfg4):
         del pw
 
 
-def test_cfg4_fused_every_row(mbq, cfg4):
+def test_layer14b_fused_every_row(mbq, layer_w):
     """q/k/v and gate/up packed as one blob each (row concatenation) and run as one
     launch each: the fused blob is the oracle's pack of the stacked rows, and every
     output column of the fused y is compared."""
-    cfg, perm, off, budget = cfg4
-    lin = {l["name"]: l for l in cfg["linears"]}
+    lay, perm, off, budget = layer_w
+    lin = {l["name"]: l for l in lay["linears"]}
     for names, xname in ((["q", "k", "v"], "q"), (["gate", "up"], "gate")):
-        say(f"cfg4 fused {'/'.join(names)}")
+        say(f"layer14b fused {'/'.join(names)}")
         Ws = [lin[n]["W"] for n in names]
         p, starts = mbq.pack_concat([to_dev(W, torch.bfloat16) for W in Ws], 128, 3)
         X = lin[xname]["X"]
@@ -218,13 +218,13 @@ def test_cfg4_fused_every_row(mbq, cfg4):
 
 
 # ---------------------------------------------------------------- low-rank side path, full sizes
-@pytest.mark.parametrize("cfg,T", [(2, 16), (3, 2048)])
-def test_lowrank_full_every_row(mbq, cfg, T):
+@pytest.mark.parametrize("name,T,seed", [("decode_18944x3584", 16, 202), ("prefill_11008x4096", 2048, 203)])
+def test_lowrank_full_every_row(mbq, name, T, seed):
     """Rank-16 side path on the decode and prefill workloads' weights (B ~ N(0, 0.1^2),
     so the side path is a large part of every output)."""
-    d = inputs.make_config(cfg)
-    say(f"lowrank full cfg{cfg} T={T}")
-    lr = inputs.make_lowrank(cfg + 200, d["N"], d["K"], rank=16, b_scale=0.1)
+    d = inputs.make_workload(name)
+    say(f"lowrank full {name} T={T}")
+    lr = inputs.make_lowrank(seed, d["N"], d["K"], rank=16, b_scale=0.1)
     X = d["X"][:T]
     x = to_dev(X, torch.bfloat16)
     if d["budget"] is not None:
@@ -237,4 +237,4 @@ def test_lowrank_full_every_row(mbq, cfg, T):
     pw = Packed(mbq, d["W"])
     y = mbq.linear_lowrank(pw.p, x, perm, off, to_dev(lr["A"], torch.bfloat16), to_dev(lr["B"], torch.bfloat16))
     torch.cuda.synchronize()
-    compare(y, pw.yref(X, budget) + O.lowrank_term(X, lr["A"], lr["B"]), what=f"lowrank cfg{cfg}")
+    compare(y, pw.yref(X, budget) + O.lowrank_term(X, lr["A"], lr["B"]), what=f"lowrank {name}")

@@ -104,7 +104,7 @@ def test_pack_status_flags(mbq):
 def test_pack_full_decode_workload(mbq):
     """The 18944 x 3584 bf16 decode weight with outlier columns, all three slices."""
     say("pack full 18944x3584")
-    d = inputs.make_config(2)
+    d = inputs.make_workload("decode_18944x3584")
     want, _ = oracle_blob(d["W"], 128, 3)
     p, st = gpu_pack(mbq, d["W"], 128, 3, "bf16")
     assert st == 0

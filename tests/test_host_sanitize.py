@@ -42,7 +42,7 @@ def checker():
     steps = [
         # the library's host code: sanitizers on the host side of the hipcc compile only
         [hipcc, *B.COMMON, "-O1", "-g", *san, "-c", os.path.join(B.CSRC, "api.hip"), "-o", api_o],
-        # the driver is plain host C++
+        # the test program is plain host C++
         ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
          "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
          "-c", os.path.join(ROOT, "tests", "abi_host_check.cpp"), "-o", drv_o],

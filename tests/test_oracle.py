@@ -120,7 +120,7 @@ def test_residual_within_half_step_and_shrinks():
 
 
 def test_error_nonincreasing_on_workload_inputs():
-    """Reconstruction error falls with every slice (Frobenius and max), config-1-like data."""
+    """Reconstruction error falls with every slice (Frobenius and max), data shaped like the tiny 512x256 workload."""
     d = inputs.make_linear(1, 512, 256, 16, group=64, dtype="f32", n_outliers=4, outlier_scale=20.0)
     p = O.pack(d["W"], 64, 3)
     deq = O.dequant_slices(p["codes"], p["scale"], p["zero"], 64)

@@ -123,21 +123,28 @@ LAYER14B = [("q", 5120, 5120), ("k", 5120, 5120), ("v", 5120, 5120), ("o", 5120,
             ("gate", 13824, 5120), ("up", 13824, 5120), ("down", 5120, 13824)]
 
 
-def make_config(cfg: int) -> dict:
-    """The full-size synthetic workload of a numbered configuration."""
-    if cfg == 1:
+WORKLOADS = ("tiny_512x256", "decode_18944x3584", "prefill_11008x4096", "layer14b_t64", "sweep_14336x4096")
+
+
+def make_workload(name: str) -> dict:
+    """One of the full-size synthetic workloads, by name:
+    tiny_512x256 (G 64, float32, 16 tokens, outlier columns), decode_18944x3584 (16 tokens,
+    router), prefill_11008x4096 (2048 tokens at forced budgets 30/50/20 %), layer14b_t64
+    (the seven linears of a 14B-like decoder layer at 64 tokens) and sweep_14336x4096 (1024
+    tokens, forced budgets or the router)."""
+    if name == "tiny_512x256":
         return make_linear(1, 512, 256, 16, group=64, dtype="f32", n_outliers=4,
                            outlier_scale=20.0)
-    if cfg == 2:
+    if name == "decode_18944x3584":
         return make_linear(2, 18944, 3584, 16, n_outliers=round(0.005 * 3584),
                            outlier_scale=10.0)
-    if cfg == 3:
+    if name == "prefill_11008x4096":
         return make_linear(3, 11008, 4096, 2048, forced_counts=forced_mix(2048, [0.3, 0.5, 0.2]))
-    if cfg == 5:
+    if name == "sweep_14336x4096":
         return make_linear(5, 14336, 4096, 1024)
-    if cfg == 4:
+    if name == "layer14b_t64":
         return make_layer14b()
-    raise ValueError(cfg)
+    raise ValueError(name)
 
 
 def make_layer14b(T: int = 64, seed: int = 4, scale_down: int = 1) -> dict:
