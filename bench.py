@@ -227,7 +227,7 @@ def bench_decode(api, torch, inputs, T, steps, warmup, dev, variants=True):
     out["step_s"], out["step_event_s"] = graph_steps(torch, step, nb, steps, warmup)
     # the plan's path: two launches when the operands are prepared (prep_bytes > 0 and the
     # fp8 x fp4 multiply), else one; the dominant kernel alone on prepared operands
-    two = prep_bytes > 0 and T > 4
+    two = prep_bytes > 0 and T > 8
     out["launches"] = 2 if two else 1
     if two:
         prep = api.route_prepare(blobs[0], X, Wr)
@@ -513,7 +513,7 @@ def run_traffic(api, torch, inputs, dev, T, launches=20):
     torch.cuda.synchronize()
     counts = torch.diff(off).cpu().tolist()
     jmax = max(j + 1 for j in range(3) if counts[j] > 0)
-    prep = api.route_prepare_workspace(blobs[0], T) if T > 4 else 0
+    prep = api.route_prepare_workspace(blobs[0], T) if T > 8 else 0
     return {"workload": "traffic", "copy_bytes": 2 * (1 << 30),
             "decode_bytes": decode_bytes(blobs[0], T, jmax, router=True, prep_bytes=prep), "launches": launches}
 

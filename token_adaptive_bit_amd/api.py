@@ -435,7 +435,7 @@ def route_linear(p: PackedLinear, x: torch.Tensor, wr: torch.Tensor, out_dtype: 
                  workspace: torch.Tensor | None = None, options: MbqOpts | None = None):
     """One decode step: route (logits x . wr, budgets, stable regroup) and the routed linear.
     Returns (y, logits, budget, perm, offsets).  For bfloat16 x, t <= 16 and K within one
-    workgroup: one launch up to 4 tokens, two from 5 (the fp8 operands prepared once in the
+    workgroup: one launch up to 8 tokens, two from 9 (the fp8 operands prepared once in the
     workspace); otherwise route, then linear."""
     _dev(x, "x")
     if x.dim() != 2:

@@ -1387,19 +1387,22 @@ hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t,
                                int32_t* offsets, void* y, bool y_bf16, int mul, int launches, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
   // Two launches (decode_prep_kernel prepares the fp8 operands, the partial logits and the
-  // group sums once, instead of in every workgroup) pay from about 8 tokens: below, the
-  // second launch costs more than the per-workgroup preparation it saves.
+  // group sums once, instead of in every workgroup) pay from about 10 tokens: below, the
+  // second launch costs more than the per-workgroup preparation it saves (18944 x 3584,
+  // graph replays, one launch against two: 19.6 / 20.3 us at 5 tokens, 20.2 / 20.4 at 8,
+  // 20.9 / 20.7 at 12, 21.6 / 20.5 at 16).
   const bool room = ws && ws_bytes >= PrepLayout(d.k_tiles, d.group).bytes;
-  bool pa = launches == 2 || (launches == 0 && t > 4 && room);
+  bool pa = launches == 2 || (launches == 0 && t > 8 && room);
   const RouteIO rio{wr, logits, budget, perm, offsets, static_cast<const uint8_t*>(ws)};
   const Plan pl = make_plan(d, t, true, false);
   // The fp8 x fp4 multiply saves ~1/4 of a row block's time but its activation split
   // costs every workgroup about two row blocks' worth up front: taken from 4 row blocks
-  // per workgroup, 2 slices and 4 tokens on (with fewer tokens fewer slices tend to be
-  // read, and a one-token step on the 18944 x 3584 weight measured faster in bf16: 13.2
-  // against 14.3 us), unless the caller chooses (mul).
+  // per workgroup, 2 slices and 2 tokens on (one token reads one slice more often than
+  // not; on the 18944 x 3584 weight, bf16 against fp8 x fp4 in one launch: 13.7 / 14.1 us
+  // at 1 token, 16.6 / 15.7 at 2, 16.4 / 15.7 at 3, 20.2 / 19.5 at 4), unless the
+  // caller chooses (mul).
   const int grid = std::min(d.row_blocks, std::max(8, cu_count() & ~7));
-  bool f4 = d.slices >= 2 && t >= 4 && (d.row_blocks + grid - 1) / grid >= 4;
+  bool f4 = d.slices >= 2 && t >= 2 && (d.row_blocks + grid - 1) / grid >= 4;
   if (mul == MBQ_MUL_BF16) f4 = false;
   if (mul == MBQ_MUL_FP8_FP4) f4 = true;
   if (!f4 || d.slices < 2) pa = false;

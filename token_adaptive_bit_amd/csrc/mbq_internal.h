@@ -60,7 +60,7 @@ size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool l
 bool decode_route_supported(const mbq_desc& d, int32_t t);
 // mul: an mbq_mul (MBQ_MUL_AUTO lets the plan choose); launches: 0 (the plan's choice), 1
 // or 2.  The fp8 x fp4 step runs as two launches (the prepared operands in ws, which must
-// then hold decode_route_workspace() bytes) when asked to or, by default, above 4 tokens
+// then hold decode_route_workspace() bytes) when asked to or, by default, above 8 tokens
 // with that much workspace; otherwise as one.
 size_t decode_route_workspace(const mbq_desc& d, int32_t t);
 // The two launches apart: the prepared operands (decode_prep_kernel), and the streaming
