@@ -34,6 +34,11 @@ namespace mbq {
 namespace {
 
 constexpr int kMaxWaves = 8;
+// In-kernel routing: batches of at most this many tokens issue row block 1 only once the
+// budgets are known, with the slices some token uses (a one-token step usually reads one
+// of three slices, and row block 1's loads, issued earlier, stalled the routing behind
+// the memory queue).
+constexpr int kLateRow1 = 1;
 constexpr int kMaxTokens = 64;  // tokens per launch (16 per workgroup row)
 constexpr uint32_t kNeg128 = 0xC300C300u, kNeg32 = 0xC200C200u, kNeg8 = 0xC100C100u;
 constexpr uint32_t kOnes = 0x3F803F80u;
@@ -905,7 +910,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
         load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (kThreeBuffers && tp == TPW - 1) {
+      if (kThreeBuffers && tp == TPW - 1 && T > kLateRow1) {
         __builtin_amdgcn_sched_barrier(0);
         load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
         __builtin_amdgcn_sched_barrier(0);
@@ -964,6 +969,13 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
 #pragma unroll
     for (int j = 0; j < S; ++j)
       if (j >= jmax) rs[j] = slice_rsrc(packed + uint64_t(j) * ss, 0u);
+    if constexpr (!PA && kThreeBuffers) {
+      if (T <= kLateRow1) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     if (blockIdx.x == 0 && blockIdx.z == 0 && wave == 0) {
       // the regroup: stable ascending order by budget, ranks from ballots
       const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
