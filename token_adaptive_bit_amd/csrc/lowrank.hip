@@ -8,11 +8,12 @@
 // two MFMAs per row block; MFMA prefill: two per output block after the last chunk).  The
 // generic fallback kernels add it afterwards with lowrank_update_kernel.
 //
-// lowrank_u_kernel: workgroups of 16 waves over 16 tokens x one of KSU chunks of K (few
+// lowrank_u_kernel: workgroups of 4 waves over 16 tokens x one of KSU chunks of K (few
 // tokens get several chunks, so the launch spreads over the chip).  The waves split the
 // chunk into contiguous ranges of 32-input steps; each multiplies 16 tokens x 16 ranks per
 // step on bf16 MFMA (float32 x as a bf16 hi + lo pair) with two load groups in flight,
-// and LDS sums the 16 partial tiles in a fixed order.  Chunk z writes u_part[z] [T x R];
+// and LDS sums the 4 partial tiles in a fixed order.  (16 waves per workgroup, each with
+// fewer steps, measured 0.5 us slower per decode step at 16 tokens, K = 3584.)  Chunk z writes u_part[z] [T x R];
 // the consumers add the chunks in order 0, 1, ..., so u repeats exactly from run to run.
 #include <type_traits>
 
@@ -89,11 +90,13 @@ struct LrFrag {
 
 // u_part [KSU x T x R]: chunk blockIdx.y of x [T x K] . A^T, A [R x K] bf16.
 // NF = ceil(R / 16) rank fragments; kpc 32-input steps per chunk.
+constexpr int kUWaves = 4;
+
 template <bool XBF16, bool VEC, int NF>
-__global__ __launch_bounds__(1024) void lowrank_u_kernel(const void* __restrict__ x, int T, int K,
-                                                         const uint16_t* __restrict__ A, int R,
-                                                         int kpc, float* __restrict__ u) {
-  constexpr int NW = 16, ESZ = XBF16 ? 2 : 4;
+__global__ __launch_bounds__(64 * kUWaves) void lowrank_u_kernel(const void* __restrict__ x, int T, int K,
+                                                                 const uint16_t* __restrict__ A, int R,
+                                                                 int kpc, float* __restrict__ u) {
+  constexpr int NW = kUWaves, ESZ = XBF16 ? 2 : 4;
   __shared__ float red[NW][16][16 * NF];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * 16;
@@ -223,7 +226,7 @@ hipError_t launch_lowrank_u(int32_t t, int32_t k, const void* x, bool x_bf16, co
   const dim3 grid((t + 15) / 16, ksu);
   auto go = [&](auto xb, auto vv, auto nf) {
     hipLaunchKernelGGL((lowrank_u_kernel<decltype(xb)::value, decltype(vv)::value, decltype(nf)::value>),
-                       grid, dim3(1024), 0, stream, x, t, k, a, rank, kpc, u);
+                       grid, dim3(64 * kUWaves), 0, stream, x, t, k, a, rank, kpc, u);
   };
   auto go_nf = [&](auto xb, auto vv) {
     if (rank > 16) go(xb, vv, std::integral_constant<int, 2>{});
