@@ -223,6 +223,21 @@ def test_route_linear_single_slice(mbq, T, mul, launches):
              f4=(mul == "fp8fp4" or (mul is None and T >= 2)))
 
 
+@pytest.mark.parametrize("b", [2, 3])
+def test_route_linear_one_token_deep_budget(mbq, b):
+    """One token whose router picks 2 or 3 slices on 1184 row blocks (4-5 per workgroup):
+    the one-token step issues row block 1 only after routing, with the slices the budget
+    reads; y must equal the two-call path's bit for bit (bf16 multiply) and the oracle's
+    within the bar.  Router column b - 1 dominates, so the budget is b."""
+    say(f"route_linear one token, budget {b}")
+    d = inputs.make_linear(600 + b, 18944, 1024, 1, group=128, slices=3, dtype="bf16")
+    wr = np.zeros_like(d["Wr"])
+    wr[:, b - 1] = np.abs(d["Wr"][:, b - 1]) * np.sign(d["X"][0]).astype(wr.dtype)
+    d["Wr"] = wr
+    bg = run_case(mbq, 18944, 1024, 128, 3, 1, "bf16", 0, mul=None, d=d)
+    assert list(bg) == [b]
+
+
 @pytest.mark.parametrize("T", [4, 16])
 def test_route_linear_graph_replays_match_eager(mbq, T):
     """The routed step captured in a HIP graph (one launch at 4 tokens, two at 16: the
