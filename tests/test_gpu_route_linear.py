@@ -223,18 +223,20 @@ def test_route_linear_single_slice(mbq, T, mul, launches):
              f4=(mul == "fp8fp4" or (mul is None and T >= 2)))
 
 
+@pytest.mark.parametrize("mul", [None, "fp8fp4"])
 @pytest.mark.parametrize("b", [2, 3])
-def test_route_linear_one_token_deep_budget(mbq, b):
+def test_route_linear_one_token_deep_budget(mbq, b, mul):
     """One token whose router picks 2 or 3 slices on 1184 row blocks (4-5 per workgroup):
     the one-token step issues row block 1 only after routing, with the slices the budget
-    reads; y must equal the two-call path's bit for bit (bf16 multiply) and the oracle's
-    within the bar.  Router column b - 1 dominates, so the budget is b."""
-    say(f"route_linear one token, budget {b}")
+    reads; y must equal the two-call path's bit for bit (the plan's bf16 multiply; within
+    1e-3 per token on the fp8 x fp4 one) and the oracle's within the bar.  Router column
+    b - 1 dominates, so the budget is b."""
+    say(f"route_linear one token, budget {b}, mul {mul}")
     d = inputs.make_linear(600 + b, 18944, 1024, 1, group=128, slices=3, dtype="bf16")
     wr = np.zeros_like(d["Wr"])
     wr[:, b - 1] = np.abs(d["Wr"][:, b - 1]) * np.sign(d["X"][0]).astype(wr.dtype)
     d["Wr"] = wr
-    bg = run_case(mbq, 18944, 1024, 128, 3, 1, "bf16", 0, mul=None, d=d)
+    bg = run_case(mbq, 18944, 1024, 128, 3, 1, "bf16", 0, mul=mul, d=d, f4=mul is not None)
     assert list(bg) == [b]
 
 
