@@ -424,7 +424,7 @@ def bench_lowrank(api, torch, inputs, dev, iters=30):
         B = torch.from_numpy(lr["B"]).to(dev, torch.bfloat16)
         y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
         ws0 = torch.empty(max(1, api.linear_workspace(blobs[0], T)), dtype=torch.uint8, device=dev)
-        ws1 = torch.empty(max(1, api.linear_lowrank_workspace(blobs[0], T, 16)), dtype=torch.uint8, device=dev)
+        ws1 = torch.zeros(max(1, api.linear_lowrank_workspace(blobs[0], T, 16)), dtype=torch.uint8, device=dev)  # call state starts at zero
         plain = lambda i: api.linear(blobs[i % nb], X, perm, off, y=y, workspace=ws0)
         side = lambda i: api.linear_lowrank(blobs[i % nb], X, perm, off, A, B, y=y, workspace=ws1)
         for f in (plain, side):
@@ -440,9 +440,13 @@ def bench_lowrank(api, torch, inputs, dev, iters=30):
             t0 = time_events(torch, plain, iters)
             t1 = time_events(torch, side, iters)
             how = "eager"
+        torch.cuda.synchronize()
+        # the side path's call state words: launches that computed u inside the streaming
+        # decode, an unused word (0), error flags (0)
+        state = ws1[:12].view(torch.int32).cpu().tolist()
         out[f"t{T}_{N}x{K}"] = {"N": N, "K": K, "T": T, "rank": 16, "copies": nb, "timing": how,
                                 "linear_us": t0 * 1e6, "linear_lowrank_us": t1 * 1e6,
-                                "overhead_frac": t1 / t0 - 1.0}
+                                "overhead_frac": t1 / t0 - 1.0, "u_in_launch_state": state}
         del blobs
     return out
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MBQ_ABI_VERSION 2
+#define MBQ_ABI_VERSION 3
 
 typedef enum {
   MBQ_OK = 0,
@@ -360,10 +360,13 @@ mbq_status mbq_route_linear(const mbq_desc* desc, const void* packed, int32_t t,
                             void* workspace, size_t ws_bytes, const mbq_opts* opts,
                             hipStream_t stream);
 
-/* Host only: bytes of device workspace mbq_linear_lowrank needs: u as c float32 partials
- * over chunks of K ([c x t x rank], c <= 8 chosen from t and k; rounded up to 256 bytes)
- * followed by the routed linear's split-K partials under the side path's plan (one
- * 16-token block per workgroup).  0 when t == 0. */
+/* Host only: bytes of device workspace mbq_linear_lowrank needs: the side path's call
+ * state (256 bytes, 512 check-in lines of 128 bytes, then u of every 16-token block as
+ * 8-byte pairs: 16 ceil(t/16) rank x 8 bytes rounded up to 256), u as c float32
+ * partials over chunks of K ([c x t x rank],
+ * c <= 8 chosen from t and k; rounded up to 256 bytes), then the routed linear's split-K
+ * partials under the side path's plan (one 16-token block per workgroup).  0 when
+ * t == 0. */
 mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dtype x_dtype,
                                         int32_t rank, size_t* bytes);
 
@@ -375,13 +378,21 @@ mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dty
  *   a:     [rank x k] bfloat16 bit patterns, row-major, 16-byte aligned.
  *   b:     [n x rank] bfloat16 bit patterns, row-major, 16-byte aligned.
  *   rank:  a multiple of 8 in [8, 32] (MBQ_ERR_UNSUPPORTED otherwise).
- *   workspace: at least mbq_linear_lowrank_workspace() bytes, 16-byte aligned.
+ *   workspace: at least mbq_linear_lowrank_workspace() bytes, 16-byte aligned.  Its
+ *           front part carries state from one call to the next: fill the whole workspace
+ *           with zeros before its first call and write nothing into it between calls
+ *           (every call leaves that state ready for the next; calls on one workspace must
+ *           not overlap).  A workspace at least as large serves every t and shape.
  *   Other arguments (opts too) as in mbq_linear.
- * u = x . A^T is computed first (float32 accumulation over k; float32 x as a bf16 hi + lo
- * pair), then the linear kernels add u . B^T to their float32 accumulators before the one
- * rounding to y (u enters their MFMAs as a bf16 hi + lo pair).  Kernels without that
- * fusion (the generic decode and prefill) add it to y afterwards; bfloat16 y is then
- * rounded twice.
+ * u = x . A^T (float32 accumulation over k; float32 x as a bf16 hi + lo pair) is added
+ * as u . B^T to the linear kernels' float32 accumulators before the one rounding to y (u
+ * enters their MFMAs as a bf16 hi + lo pair).  The streaming decode (t <= 64, K within
+ * one workgroup) computes u inside its own launch: workgroup 0 of every 16-token block
+ * multiplies the activations by A and publishes u in the workspace with this call's tag;
+ * the other workgroups stream the weight and pick u up for their first row block one row
+ * block later.  Elsewhere u is computed by a launch of its own first.  Kernels without
+ * the fusion (the generic decode and prefill) add u . B^T to y afterwards; bfloat16 y is
+ * then rounded twice.
  */
 mbq_status mbq_linear_lowrank(const mbq_desc* desc, const void* packed, int32_t t, const void* x,
                               mbq_dtype x_dtype, const int32_t* perm, const int32_t* offsets,

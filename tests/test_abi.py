@@ -32,7 +32,7 @@ def test_exports_match_header():
     assert set(names) == set(lib_mod.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.mbq_abi_version() == 2
+    assert L.mbq_abi_version() == 3
 
 
 def test_status_strings():
@@ -124,18 +124,20 @@ def test_pack_rows_validation():
     (11008, 4096, 128, 3, 2048, 16, 1, 1),  # prefill: u only
 ])
 def test_linear_lowrank_workspace(N, K, G, S, t, rank, uchunks, chunks):
-    """u as uchunks float32 partials [uchunks x t x rank] (rounded up to 256 bytes), then
-    the decode's split-K partials under the side path's plan (one 16-token block per
-    workgroup)."""
+    """The side path's call state (256 bytes, 512 check-in lines of 128 bytes, then u of
+    every 16-token block as 8-byte pairs rounded up to 256 bytes), u as uchunks float32
+    partials [uchunks x t x rank] (rounded up to 256 bytes), then the decode's split-K
+    partials under the side path's plan (one 16-token block per workgroup)."""
     st, d = desc(N, K, G, S)
     n = ctypes.c_size_t(123)
     assert L.mbq_linear_lowrank_workspace(ctypes.byref(d), t, BF16, rank, ctypes.byref(n)) == OK
+    fb = 256 + 512 * 128 + ((t + 15) // 16 * 16 * rank * 8 + 255) // 256 * 256
     ub = (uchunks * t * rank * 4 + 255) // 256 * 256
-    assert n.value == ub + (chunks * t * N * 4 if chunks > 1 else 0)
+    assert n.value == fb + ub + (chunks * t * N * 4 if chunks > 1 else 0)
     assert L.mbq_linear_lowrank_workspace(ctypes.byref(d), 0, BF16, rank, ctypes.byref(n)) == OK
     assert n.value == 0
     f = P(FAKE)
-    need = ub + (chunks * t * N * 4 if chunks > 1 else 0)
+    need = fb + ub + (chunks * t * N * 4 if chunks > 1 else 0)
     for ws, wsb in ((None, 0), (f, need - 1), (P(FAKE + 8), need)):
         assert L.mbq_linear_lowrank(ctypes.byref(d), f, t, f, BF16, f, f, f, f, rank, f, BF16, ws, wsb,
                                     None, None) == WS

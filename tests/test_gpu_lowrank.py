@@ -120,3 +120,78 @@ def test_lowrank_decode_tiles_chunks_ranks(mbq, K, dtype, rank):
     and split over workgroups (8192), both activation types and ranks 8, 16 and 32."""
     say(f"lowrank u placement K={K} {dtype} r={rank}")
     check(*run(mbq, 130, K, 128, 3, 16, dtype, rank, seed=K + rank))
+
+
+def test_lowrank_inline_u_call_state(mbq):
+    """Where the streaming decode computes u inside its own launch, the workspace carries
+    call state from one call to the next.  Calls on one workspace with different
+    activations, HIP-graph replays of one captured call with the activations changed
+    between replays, eager calls in between and a call with fewer tokens on the same
+    workspace all match the oracle; afterwards the state words read: launch count = calls
+    made, an unused word 0, no error flag.  293 row blocks over 255 streaming workgroups:
+    some stream two row blocks, most one."""
+    N, K, G, S, T, rank = 4688, 3584, 128, 3, 16, 16
+    d = inputs.make_linear(31, N, K, T, group=G, slices=S, dtype="bf16")
+    lr = inputs.make_lowrank(32, N, K, rank=rank, b_scale=0.1)
+    p = mbq.pack(to_dev(d["W"], torch.bfloat16), group=G, slices=S)
+    pk = O.pack(d["W"], G, S)
+    deq = O.dequant_slices(pk["codes"], pk["scale"], pk["zero"], G)
+    a, b = to_dev(lr["A"], torch.bfloat16), to_dev(lr["B"], torch.bfloat16)
+    wr = to_dev(d["Wr"], torch.float32)
+    xs = [d["X"]] + [inputs.make_linear(40 + i, 16, K, T, group=G, slices=S, dtype="bf16")["X"] for i in range(3)]
+    ws = torch.zeros(mbq.linear_lowrank_workspace(p, T, rank), dtype=torch.uint8, device=DEV)
+    xb = torch.empty((T, K), dtype=torch.bfloat16, device=DEV)
+    perm = torch.empty(T, dtype=torch.int32, device=DEV)
+    off = torch.empty(S + 1, dtype=torch.int32, device=DEV)
+    y = torch.empty((T, N), dtype=torch.float32, device=DEV)
+
+    def load(i):
+        xb.copy_(to_dev(xs[i], torch.bfloat16))
+        _, _, pm, of = mbq.route(xb, wr)
+        perm.copy_(pm)
+        off.copy_(of)
+        y.zero_()
+
+    def call():
+        mbq.linear_lowrank(p, xb, perm, off, a, b, y=y, workspace=ws)
+
+    def check(X, yy, pm, of):
+        torch.cuda.synchronize()
+        bud = budget_from_perm(pm.cpu().numpy(), of.cpu().numpy())
+        yref = O.linear(X, deq, bud) + O.lowrank_term(X, lr["A"], lr["B"])
+        err = token_errors(yy.cpu().numpy(), yref)
+        say(f"  max token error {err.max():.3e}")
+        assert err.max() <= TOL
+
+    calls = 0
+    for i in range(3):
+        load(i)
+        call()
+        calls += 1
+        check(xs[i], y, perm, off)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    calls += 1
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in (3, 0, 2, 1):
+        load(i)
+        g.replay()
+        calls += 1
+        check(xs[i], y, perm, off)
+        y.zero_()
+        call()                       # an eager call between replays
+        calls += 1
+        check(xs[i], y, perm, off)
+    x5 = to_dev(xs[3][:5], torch.bfloat16)
+    _, _, pm5, of5 = mbq.route(x5, wr)
+    y5 = mbq.linear_lowrank(p, x5, pm5, of5, a, b, out_dtype=torch.float32, workspace=ws)
+    calls += 1
+    check(xs[3][:5], y5, pm5, of5)
+    state = ws[:12].view(torch.int32).cpu().numpy().tolist()
+    assert state == [calls, 0, 0]

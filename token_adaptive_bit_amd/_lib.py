@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libmbq.so")
 
 MBQ_F32, MBQ_BF16 = 0, 1
 STATIC_SCRATCH_BYTES = 16 << 20      # MBQ_STATIC_SCRATCH_BYTES
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_ARG", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_RANGE",
           -4: "MBQ_ERR_WORKSPACE", -5: "MBQ_ERR_DEVICE", -6: "MBQ_ERR_UNSUPPORTED"}

@@ -483,8 +483,8 @@ def linear_lowrank(p: PackedLinear, x: torch.Tensor, perm: torch.Tensor, offsets
     _arg(b, "b", (p.n, rank), (torch.bfloat16,), x.device)
     need = linear_lowrank_workspace(p, t, rank, x.dtype)
     _workspace(workspace, "workspace", need, x.device)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if need and workspace is None:  # zero-filled: the call state starts from zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     check(_lib.LIB.mbq_linear_lowrank(ctypes.byref(p.desc), _p(p.blob), t, _p(x), _dtype(x), _p(perm),
                                       _p(offsets), _p(a), _p(b), rank, _p(y), _dtype(y), _p(workspace),

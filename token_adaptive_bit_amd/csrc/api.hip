@@ -211,6 +211,10 @@ size_t u_bytes(int32_t t, int32_t k, int32_t rank) {
   return align256(uint64_t(mbq::lowrank_u_chunks(t, k)) * uint64_t(t) * uint64_t(rank) * 4);
 }
 
+// The side path's call state at the front of its workspace (mbq::lr_state_bytes), used
+// where the streaming decode computes u inside its own launch.
+size_t lr_state_bytes(int32_t t, int32_t rank) { return mbq::lr_state_bytes(t, rank); }
+
 bool rank_ok(int32_t rank) { return rank >= 8 && rank <= 32 && rank % 8 == 0; }
 
 const mbq_opts kDefaultOpts{};
@@ -247,22 +251,29 @@ mbq_status linear_impl(const mbq_desc* desc, const void* packed, int32_t t, cons
   if (!linear_ptrs_ok(packed, x, perm, offsets, y)) return MBQ_ERR_ARG;
   if (rank && (!a || !b || !aligned(a, 16) || !aligned(b, 16))) return MBQ_ERR_ARG;
   const bool xb = x_dtype == MBQ_BF16, yb = y_dtype == MBQ_BF16, lr = rank > 0;
-  const size_t ub = lr ? u_bytes(t, desc->k, rank) : 0, need = ub + linear_ws(*desc, t, xb, lr);
+  // workspace: [side-path state][u partials][the linear's split-K partials]
+  const size_t fb = lr ? lr_state_bytes(t, rank) : 0, ub = lr ? u_bytes(t, desc->k, rank) : 0;
+  const size_t need = fb + ub + linear_ws(*desc, t, xb, lr);
   const int ksu = lr ? mbq::lowrank_u_chunks(t, desc->k) : 0;
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
     return MBQ_ERR_WORKSPACE;
-  float* u = lr ? static_cast<float*>(workspace) : nullptr;
-  void* lws = need > ub ? static_cast<uint8_t*>(workspace) + ub : nullptr;
-  if (lr) {
-    st = launched(mbq::launch_lowrank_u(t, desc->k, x, xb, a, rank, u, stream));
-    if (st != MBQ_OK) return st;
-  }
+  uint8_t* fz = lr ? static_cast<uint8_t*>(workspace) : nullptr;
+  float* u = lr ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + fb) : nullptr;
+  void* lws = need > fb + ub ? static_cast<uint8_t*>(workspace) + fb + ub : nullptr;
   // the generic kernels serve slices of 4 GiB and more (and activations of 4 GiB and more
   // in prefill), which the streaming decode's and the MFMA prefill's 32-bit buffer offsets
   // cannot reach; MBQ_PATH_GENERIC selects them for any size
-  if (!generic && mbq::decode_stream_supported(*desc, t, xb, lr))
-    return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb, lws, u,
-                                              ksu, b, rank, stream));
+  const bool streaming = !generic && mbq::decode_stream_supported(*desc, t, xb, lr);
+  // the streaming decode computes u inside its own launch where K fits one workgroup
+  const bool inline_u = lr && streaming && mbq::decode_stream_lr_inline(*desc, t, xb);
+  if (lr && !inline_u) {
+    st = launched(mbq::launch_lowrank_u(t, desc->k, x, xb, a, rank, u, stream));
+    if (st != MBQ_OK) return st;
+  }
+  if (streaming)
+    return launched(mbq::launch_decode_stream(*desc, packed, t, x, xb, perm, offsets, y, yb, lws,
+                                              inline_u ? nullptr : u, inline_u ? 0 : ksu, b, rank,
+                                              inline_u ? fz : nullptr, a, stream));
   if (!generic && t > 64 && mbq::prefill_mfma_supported(*desc, t, x, xb))
     return launched(mbq::launch_prefill_mfma(*desc, packed, t, x, xb, perm, offsets, y, yb, u, ksu, b,
                                              rank, opts->prefill_slots, stream));
@@ -429,7 +440,7 @@ mbq_status mbq_linear_lowrank_workspace(const mbq_desc* desc, int32_t t, mbq_dty
   if (!bytes || !valid_dtype(x_dtype)) return MBQ_ERR_ARG;
   if (t < 0 || t > (1 << 24)) return MBQ_ERR_SHAPE;
   if (!rank_ok(rank)) return MBQ_ERR_UNSUPPORTED;
-  *bytes = t == 0 ? 0 : u_bytes(t, desc->k, rank) + linear_ws(*desc, t, x_dtype == MBQ_BF16, true);
+  *bytes = t == 0 ? 0 : lr_state_bytes(t, rank) + u_bytes(t, desc->k, rank) + linear_ws(*desc, t, x_dtype == MBQ_BF16, true);
   return MBQ_OK;
 }
 

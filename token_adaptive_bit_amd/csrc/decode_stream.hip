@@ -40,6 +40,15 @@ constexpr int kMaxWaves = 8;
 // the memory queue).
 constexpr int kLateRow1 = 1;
 constexpr int kMaxTokens = 64;  // tokens per launch (16 per workgroup row)
+// Reads of u (side path with lr_fz) before giving up: each is a round trip to memory plus
+// a short sleep, so this bounds the wait at about a tenth of a second.
+constexpr int kLrSpin = 1 << 16;
+// Variants that carry the in-launch u (lr_fz): all but float32 activations over two k
+// tiles per wave, whose registers are full without it.
+constexpr bool lr_inline_fits(int NA, int TPW) { return !(NA == 2 && TPW == 2); }
+// Row blocks per workgroup whose float32 sums LDS can hold until the side path is added
+// (LR with lr_fz; 1 KiB each).  The host computes u in a launch of its own beyond this.
+constexpr int kLrStage = 48;
 constexpr uint32_t kNeg128 = 0xC300C300u, kNeg32 = 0xC200C200u, kNeg8 = 0xC100C100u;
 constexpr uint32_t kOnes = 0x3F803F80u;
 
@@ -308,7 +317,8 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     uint64_t po, const void* __restrict__ x, int T, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, void* __restrict__ y, int y_bf16, int kchunk,
     float* __restrict__ part, const float* __restrict__ lr_u, int lr_ks,
-    const uint16_t* __restrict__ lr_b, int lr_r, RouteIO rio) {
+    const uint16_t* __restrict__ lr_b, int lr_r, uint8_t* __restrict__ lr_fz,
+    const uint16_t* __restrict__ lr_a, RouteIO rio) {
   static_assert(!LR || TB == 1, "the side path is built for one token block per workgroup");
   static_assert(!RT || (TB == 1 && !LR), "in-kernel routing takes one token block, no side path");
   static_assert(!F4 || (NA == 1 && TB == 1 && !LR), "fp4 operands: bfloat16 activations, one token block");
@@ -319,6 +329,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   asm volatile("" ::"s"(packed), "s"(x), "s"(perm), "s"(offsets), "s"(y), "s"(part), "s"(lr_u), "s"(lr_b));
   asm volatile("" ::"s"(N), "s"(K), "s"(KB), "s"(NG), "s"(NB), "s"(ss), "s"(po), "s"(T), "s"(y_bf16),
                "s"(kchunk), "s"(lr_ks), "s"(lr_r));
+  if constexpr (LR) asm volatile("" ::"s"(lr_fz), "s"(lr_a));
   if constexpr (RT) asm volatile("" ::"s"(rio.wr), "s"(rio.logits), "s"(rio.budget), "s"(rio.perm), "s"(rio.offsets));
   if constexpr (PA) asm volatile("" ::"s"(rio.prep));
   constexpr int GPT = 256 / G, WPG = G / 64;
@@ -327,7 +338,12 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // the wave index is uniform: telling the compiler keeps tile addresses in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, c = lane >> 4;
-  const int step = gridDim.x;
+  // LR with lr_fz: workgroup 0 of each token block computes u itself (see lr_produce)
+  // and the others stream the row blocks, so they count from blockIdx.x - 1
+  // (not built where the wave's registers are already full: float32 activations over two
+  // tiles; the host computes u in a launch of its own there)
+  const bool lrf = lr_inline_fits(NA, TPW) && LR && lr_fz != nullptr;
+  const int step = lrf ? int(gridDim.x) - 1 : int(gridDim.x);
 
   // k tiles [kb0, kend) of this workgroup's k chunk (blockIdx.z)
   const int kb0 = blockIdx.z * kchunk, kend = min(KB, kb0 + kchunk);
@@ -380,6 +396,19 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     rlr_b = slice_rsrc(reinterpret_cast<const uint8_t*>(lr_b), (wave == 0 && blockIdx.z == 0) ? uint32_t(N) * lr_r * 2 : 0u);
     lr_lane = 8 * c < lr_r ? (uint32_t(r) * lr_r + 8 * c) * 2 : 0x80000000u;
   }
+  // With lr_fz the side path's u comes from this launch's workgroup 0 (lr_produce) instead
+  // of lr_u.  lr_fz holds: word 0, the launch count E (one more after every launch);
+  // word 2, error flags (bit 0: u never arrived, so the side path was left out; bit 1: not
+  // every workgroup checked in); from byte kLrSlots, one 128-byte line per workgroup whose
+  // first word it sets to E + 1 once it has read E (separate lines: no two workgroups write
+  // one line, and there is no read-modify-write atomic, which serialises in memory while
+  // the weights stream); from byte kLrPairs, u of token block y, token t, rank q as the
+  // 8-byte pair (E + 1) << 32 | float bits, at ((16 y + t) R + q).
+  // A pair is one store and one load at device scope, so a reader that sees this launch's
+  // tag sees that store's value; pairs left by an earlier launch carry an older tag.
+  uint32_t lrE = 0;
+  if constexpr (LR)
+    if (lrf) lrE = __hip_atomic_load(reinterpret_cast<uint32_t*>(lr_fz), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- 2. this wave's activations.  Workgroup row blockIdx.y takes the TB 16-token
   // blocks starting at token tb0 = 16 TB blockIdx.y; in block b, MFMA row r is token
@@ -580,6 +609,32 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       }
     }
   };
+  // bf16 activations are used in place; float32 ones (8 values in two registers) are split
+  // once, in place, into bf16 high and low parts
+  auto split_x = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (NA == 1) continue;
+          const u32x4_t q0 = Araw[b][tp][i][h][0], q1 = Araw[b][tp][i][h][NA - 1];
+          u32x4_t hi, lo;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float v0 = __uint_as_float(d < 2 ? q0[2 * d] : q1[2 * d - 4]);
+            const float v1 = __uint_as_float(d < 2 ? q0[2 * d + 1] : q1[2 * d - 3]);
+            const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
+            const uint32_t l0 = bf16_bits_rne(v0 - bf16_bits_to_float(h0));
+            const uint32_t l1 = bf16_bits_rne(v1 - bf16_bits_to_float(h1));
+            hi[d] = h0 | (h1 << 16);
+            lo[d] = l0 | (l1 << 16);
+          }
+          Araw[b][tp][i][h][0] = hi;
+          Araw[b][tp][i][h][NA - 1] = lo;
+        }
+  };
   auto setup_a = [&]() {
     if constexpr (F4) {
 #pragma unroll
@@ -588,31 +643,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     }
 #pragma unroll
     for (int b = 0; b < TB; ++b) {
-#pragma unroll
-      for (int tp = 0; tp < TPW; ++tp)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            if (NA == 1) {
-              // used in place
-            } else {
-              const u32x4_t q0 = Araw[b][tp][i][h][0], q1 = Araw[b][tp][i][h][NA - 1];
-              u32x4_t hi, lo;
-#pragma unroll
-              for (int d = 0; d < 4; ++d) {
-                const float v0 = __uint_as_float(d < 2 ? q0[2 * d] : q1[2 * d - 4]);
-                const float v1 = __uint_as_float(d < 2 ? q0[2 * d + 1] : q1[2 * d - 3]);
-                const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
-                const uint32_t l0 = bf16_bits_rne(v0 - bf16_bits_to_float(h0));
-                const uint32_t l1 = bf16_bits_rne(v1 - bf16_bits_to_float(h1));
-                hi[d] = h0 | (h1 << 16);
-                lo[d] = l0 | (l1 << 16);
-              }
-              Araw[b][tp][i][h][0] = hi;
-              Araw[b][tp][i][h][NA - 1] = lo;
-            }
-          }
+      split_x(b);
 #pragma unroll
       for (int tp = 0; tp < TPW; ++tp)
 #pragma unroll
@@ -664,6 +695,47 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // then two (one row block in flight).
   constexpr bool kThreeBuffers = !(G == 64 && S == 4);
   Codes<G, S, TPW, LR> c0, c1, c2;
+  // LR with lr_fz: u is not known while the row blocks stream (Uop stays zero, so the
+  // epilogue's side-path MFMAs add nothing and B rows are not loaded).  The storing
+  // threads keep each row block's float32 sums in LDS (ystage, row block lr_m of the
+  // workgroup) and the side path is added after the last one: see lr_finish_rows.
+  int lr_m = 0;
+  __shared__ float ystage[LR ? kLrStage : 1][256];
+  __shared__ __align__(16) uint32_t ushare[LR ? 64 : 1][8];
+  __shared__ u32x4_t bstage[LR ? kLrStage : 1][64];  // wave 0: B rows of staged row block m
+  uint32_t* const lr_hdr = reinterpret_cast<uint32_t*>(lr_fz);
+  uint64_t* const lr_pairs =
+      lrf ? reinterpret_cast<uint64_t*>(lr_fz + kLrPairs) + size_t(blockIdx.y) * 16 * size_t(lr_r) : nullptr;
+  // Every workgroup but (0, 0) checks in once it has read E: wave 0, lane 0 sets its own
+  // slot to E + 1 (nothing waits for the store).  Workgroup (0, 0), once its u is out,
+  // waits until every slot of the launch reads E + 1, then advances E for the next launch:
+  // no workgroup reads E after that in this launch, and the next launch starts only after
+  // this one ends.
+  uint32_t* const lr_slot = reinterpret_cast<uint32_t*>(lr_fz + kLrSlots);
+  const uint32_t lr_wg = blockIdx.y * gridDim.x + blockIdx.x, lr_nwg = gridDim.x * gridDim.y;
+  auto lr_check_in = [&]() __attribute__((always_inline)) {
+    if (wave == 0 && lane == 0 && lr_wg != 0) {
+      uint32_t e1 = lrE + 1u;
+      asm volatile("" : "+v"(e1));
+      __hip_atomic_store(lr_slot + 32 * lr_wg, e1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto lr_advance = [&]() __attribute__((always_inline)) {  // wave 0 of workgroup (0, 0)
+    if (lr_wg != 0) return;
+    const uint32_t want = lrE + 1u;
+    for (int it = 0;; ++it) {
+      bool ok = true;
+      for (uint32_t w = 1 + lane; w < lr_nwg; w += 64)
+        ok = ok && __hip_atomic_load(lr_slot + 32 * w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+      if (__ballot(!ok) == 0ull) break;
+      if (it >= kLrSpin) {
+        if (lane == 0) __hip_atomic_fetch_or(lr_hdr + 2, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (lane == 0) __hip_atomic_store(lr_hdr, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   // Multiplies one row block.  JM, the slices processed, is a compile-time count, so the
   // MFMA chains and epilogues of a group form one straight-line block that the compiler
   // interleaves (a runtime test per slice or tile would split it into small blocks and
@@ -804,7 +876,13 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
       float sum = 0.f;
       for (int w = 0; w < NW; ++w) sum += red[buf][w][b][ln][v];
       const int n = nb * 16 + n16, tok = 16 * b + p;
-      if (tok < Tw && n < N) {
+      if (LR && lrf) {
+        if (lr_m < kLrStage) {  // finished after the last row block
+          ystage[lr_m][threadIdx.x] = sum;
+          if constexpr (LR)
+            if (wave == 0) bstage[lr_m][lane] = C.lr.v;
+        }
+      } else if (tok < Tw && n < N) {
         const size_t idx = size_t(tb0 + tok) * N + n;
         if (part)  // one k chunk of several: a float32 partial, summed by splitk_reduce
           part[size_t(blockIdx.z) * T * N + idx] = sum;
@@ -814,6 +892,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
           reinterpret_cast<float*>(y)[idx] = sum;
       }
     }
+    if constexpr (LR) ++lr_m;
   };
 
   // Three register buffers with fixed roles: step m issues the loads of row block m + 2
@@ -824,8 +903,9 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   // inside each copy every path into the loop header carries the same pending loads in
   // the same order, which keeps the compiler's waits on the in-order load counter exact.
   // A load past the end (row block -1) goes out of range: zeros, no memory traffic.
-  const int rb0 = blockIdx.x;
-  auto nbl = [&](int m) { const int n = rb0 + m * step; return n < NB ? n : -1; };
+  const int rb0 = lrf ? int(blockIdx.x) - 1 : int(blockIdx.x);
+  // (rb0 < 0: the side path's producer, which streams nothing)
+  auto nbl = [&](int m) { const int n = rb0 + m * step; return rb0 >= 0 && n < NB ? n : -1; };
   // (scheduling fences keep the issue order perm, x, row block 0, row block 1, so each
   // wait below covers exactly the loads it needs)
   __builtin_amdgcn_sched_barrier(0);
@@ -1020,13 +1100,155 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   };
   // one instantiation per slice count read, so the time follows the slices the batch needs
   // (with the side path, whose registers leave no room for more copies, 1 and S only)
-  if constexpr (S >= 2)
-    if (jmax == 1) return stream(std::integral_constant<int, 1>{});
-  if constexpr (S >= 3 && !LR)
-    if (jmax == 2) return stream(std::integral_constant<int, 2>{});
-  if constexpr (S >= 4 && !LR)
-    if (jmax == 3) return stream(std::integral_constant<int, 3>{});
-  stream(std::integral_constant<int, S>{});
+  // lr_produce (LR with lr_fz, workgroup 0 of each token block, which streams no row
+  // block): u = x A^T of the block's 16 token rows, float32, on the same bf16 MFMA as the
+  // codes -- every wave multiplies the activations it holds (prepared as for the stream)
+  // by the matching A rows (lane (q, c) of the B operand: rank q, the lane's 8 inputs),
+  // the waves' tiles are summed in LDS in wave order, and wave 0 stores u as tagged pairs.
+  auto lr_produce = [&]() __attribute__((always_inline)) {
+    {
+      const __amdgpu_buffer_rsrc_t ra =
+          slice_rsrc(reinterpret_cast<const uint8_t*>(lr_a), uint32_t(lr_r) * uint32_t(K) * 2u);
+      f32x4_t ua[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (16 * f >= lr_r) break;
+        const int q = 16 * f + r;
+        u32x4_t Af[TPW][4][2];
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int k = kt[tp] * 256 + xk(i, h);
+              const uint32_t off =
+                  (live[tp] && q < lr_r && k < K) ? (uint32_t(q) * uint32_t(K) + uint32_t(k)) * 2u : 0x80000000u;
+              Af[tp][i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+            }
+#pragma unroll
+        for (int tp = 0; tp < TPW; ++tp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int pa = 0; pa < NA; ++pa) ua[f] = mfma(aop(0, tp, i, h, pa), Af[tp][i][h], ua[f]);
+      }
+      chain_fence();
+      red[0][wave][0][lane] = ua[0];
+      red[1][wave][0][lane] = ua[1];
+      __syncthreads();
+      if (wave == 0) {
+        const uint64_t tag = uint64_t(lrE + 1u) << 32;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int q = 16 * f + r;
+          if (16 * f < lr_r) {
+            f32x4_t sm = red[f][0][0][lane];
+            for (int w = 1; w < NW; ++w) sm += red[f][w][0][lane];
+            if (q < lr_r) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)  // lane (q, c) holds tokens 4c + v
+                __hip_atomic_store(lr_pairs + (4 * c + v) * lr_r + q, tag | uint64_t(__float_as_uint(sm[v])),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+        lr_advance();
+      }
+    }
+  };
+
+  auto run = [&]() __attribute__((always_inline)) {
+    if constexpr (S >= 2)
+      if (jmax == 1) return stream(std::integral_constant<int, 1>{});
+    if constexpr (S >= 3 && !LR)
+      if (jmax == 2) return stream(std::integral_constant<int, 2>{});
+    if constexpr (S >= 4 && !LR)
+      if (jmax == 3) return stream(std::integral_constant<int, 3>{});
+    stream(std::integral_constant<int, S>{});
+  };
+  if (lrf && blockIdx.x == 0) {
+    if constexpr (LR) {
+      lr_check_in();
+      lr_produce();
+    }
+    return;
+  }
+  if constexpr (LR)
+    if (lrf) lr_check_in();
+  run();
+  // lr_finish_rows (LR with lr_fz): wave 0 waits (bounded) for this launch's u, turns it
+  // into the MFMA's bf16 hi + lo pairs and shares them through LDS; each wave then adds
+  // u . B^T of row blocks m = wave, wave + NW, ... to the staged sums (tokens whose budget
+  // is 0 are left out, as in the epilogue), and the storing threads write every row
+  // block once, rounded once.  If u never comes, the side path is left out and error
+  // bit 0 is set rather than waiting forever.
+  if constexpr (LR) {
+    if (lrf) {
+      const int nst = min(lr_m, kLrStage);
+      if (wave == 0) {
+        const uint32_t want = lrE + 1u;
+        uint64_t pv[8];
+        for (int it = 0;; ++it) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pv[e] = 8 * c < lr_r ? __hip_atomic_load(lr_pairs + r * lr_r + 8 * c + e, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0;
+          bool ok = true;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ok = ok && (8 * c >= lr_r || uint32_t(pv[e] >> 32) == want);
+          if (__ballot(!ok) == 0ull) break;
+          if (it >= kLrSpin) {
+            if (lane == 0) __hip_atomic_fetch_or(lr_hdr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv[e] = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float v0 = __uint_as_float(uint32_t(pv[2 * d])), v1 = __uint_as_float(uint32_t(pv[2 * d + 1]));
+          const uint32_t h0 = bf16_bits_rne(v0), h1 = bf16_bits_rne(v1);
+          const uint32_t l0 = bf16_bits_rne(v0 - bf16_bits_to_float(h0));
+          const uint32_t l1 = bf16_bits_rne(v1 - bf16_bits_to_float(h1));
+          ushare[lane][d] = h0 | (h1 << 16);
+          ushare[lane][4 + d] = l0 | (l1 << 16);
+        }
+      }
+      __syncthreads();
+      const u32x4_t uh = *reinterpret_cast<const u32x4_t*>(&ushare[lane][0]);
+      const u32x4_t ul = *reinterpret_cast<const u32x4_t*>(&ushare[lane][4]);
+      auto add_lr = [&](int m, const u32x4_t& bm) __attribute__((always_inline)) {
+        f32x4_t L = mfma(uh, bm, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        L = mfma(ul, bm, L);
+        chain_fence();
+#pragma unroll
+        for (int v = 0; v < 4; ++v)  // lane (n, c): tokens 4c + v of output row n
+          if (budT[4 * c + v] > 0) ystage[m][(4 * c + v) * 16 + r] += L[v];
+      };
+      for (int m = wave; m < nst; m += NW) add_lr(m, bstage[m][lane]);
+      __syncthreads();
+      if (threadIdx.x < 256) {
+        const int p = threadIdx.x >> 4, n16 = threadIdx.x & 15;
+        if (p < Tw)
+          for (int m = 0; m < nst; ++m) {
+            const int n = (rb0 + m * step) * 16 + n16;
+            if (n < N) {
+              const size_t idx = size_t(tb0 + p) * N + n;
+              const float val = ystage[m][threadIdx.x];
+              if (y_bf16)
+                reinterpret_cast<uint16_t*>(y)[idx] = uint16_t(bf16_bits_rne(val));
+              else
+                reinterpret_cast<float*>(y)[idx] = val;
+            }
+          }
+      }
+    }
+  }
 }
 
 // The first launch of the two-launch decode step (PA): two waves per k tile of 256 inputs
@@ -1222,6 +1444,8 @@ struct LrArgs {
   int ks;
   const uint16_t* b;
   int r;
+  uint8_t* fz;         // non-null: u computed inside the launch (see lr_produce), state here
+  const uint16_t* a;   // A [r x K], with fz
 };
 
 template <int G, int S, int NA, int TPW, int TB, bool LR, bool RT = false, bool F4 = false, bool PA = false>
@@ -1235,11 +1459,16 @@ hipError_t launch_gsn(const mbq_desc& d, const Plan& pl, const void* packed, int
   // at the same pace, so each weight line comes from HBM once and is served to the other
   // token groups by that XCD's L2.
   const int ty = (t + 16 * TB - 1) / (16 * TB);
-  const int grid = std::min(d.row_blocks, std::max(8, (cu_count() / (ty * pl.ks)) & ~7));
+  const int cap = std::max(8, (cu_count() / (ty * pl.ks)) & ~7);
+  // with u computed inside the launch, workgroup 0 of each token block computes it and
+  // the others stream: one CU of the cap goes to it
+  const bool fz = LR && lr_inline_fits(NA, TPW) && lr.fz != nullptr;
+  const int grid = fz ? std::min(d.row_blocks, cap - 1) + 1 : std::min(d.row_blocks, cap);
   hipLaunchKernelGGL((decode_stream_kernel<G, S, NA, TPW, TB, LR, RT, F4, PA>), dim3(grid, ty, pl.ks), dim3(64 * pl.nw),
                      0, stream, static_cast<const uint8_t*>(packed), d.n, d.k, d.k_tiles,
                      d.groups_padded, d.row_blocks, d.slice_stride, d.params_offset, x, t, perm,
-                     offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.ks, lr.b, lr.r, rio);
+                     offsets, y, int(y_bf16), pl.kchunk, part, lr.u, lr.ks, lr.b, lr.r,
+                     fz ? lr.fz : nullptr, lr.a, rio);
   return hipGetLastError();
 }
 
@@ -1435,11 +1664,26 @@ size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool l
   return pl.ks > 1 ? size_t(pl.ks) * size_t(t) * size_t(d.n) * sizeof(float) : 0;
 }
 
+// The side path's u computed inside the streaming launch needs all of K in one
+// workgroup (every token block's workgroup 0 multiplies the whole row of activations)
+// and every streaming workgroup's row blocks held in LDS until u is added.
+bool decode_stream_lr_inline(const mbq_desc& d, int32_t t, bool x_bf16) {
+  if (!decode_stream_supported(d, t, x_bf16, true)) return false;
+  const Plan pl = make_plan(d, t, x_bf16, true);
+  if (pl.ks != 1 || !lr_inline_fits(x_bf16 ? 1 : 2, pl.tpw)) return false;
+  const int ty = (t + 15) / 16;
+  const int cap = std::max(8, (cu_count() / ty) & ~7);
+  const int streaming = std::min(d.row_blocks, cap - 1);  // as in launch_gsn
+  return streaming >= 1 && (d.row_blocks + streaming - 1) / streaming <= kLrStage &&
+         (streaming + 1) * ty <= kLrMaxWg;
+}
+
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
                                 void* y, bool y_bf16, void* workspace, const float* lr_u,
-                                int32_t lr_ks, const uint16_t* lr_b, int32_t lr_r, hipStream_t stream) {
-  const LrArgs lr{lr_u, lr_ks, lr_b, lr_r};
+                                int32_t lr_ks, const uint16_t* lr_b, int32_t lr_r, uint8_t* lr_fz,
+                                const uint16_t* lr_a, hipStream_t stream) {
+  const LrArgs lr{lr_u, lr_ks, lr_b, lr_r, lr_fz, lr_a};
   const Plan pl = make_plan(d, t, x_bf16, lr_r > 0);
   float* part = pl.ks > 1 ? static_cast<float*>(workspace) : nullptr;
   hipError_t e;

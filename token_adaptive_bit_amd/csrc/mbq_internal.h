@@ -55,6 +55,17 @@ hipError_t launch_decode(const mbq_desc& d, const void* packed, int32_t t, const
                          bool y_bf16, void* ws, hipStream_t stream);
 bool decode_stream_supported(const mbq_desc& d, int32_t t, bool x_bf16, bool lr = false);
 size_t decode_stream_workspace(const mbq_desc& d, int32_t t, bool x_bf16, bool lr);
+bool decode_stream_lr_inline(const mbq_desc& d, int32_t t, bool x_bf16);
+// The low-rank side path's call state at the front of its workspace, where the streaming
+// decode computes u inside its launch: 256 bytes of words (launch count, error flags),
+// one 128-byte check-in line for each of at most kLrMaxWg workgroups (from byte 256),
+// then u of every 16-token block as 8-byte pairs (from byte kLrPairs, rounded up to 256
+// bytes).  The offsets do not depend on t, so calls of any size can share a workspace.
+constexpr int kLrMaxWg = 512;
+constexpr size_t kLrSlots = 256, kLrPairs = kLrSlots + size_t(kLrMaxWg) * 128;
+inline size_t lr_state_bytes(int32_t t, int32_t rank) {
+  return kLrPairs + (size_t((t + 15) / 16) * 16 * size_t(rank) * 8 + 255) / 256 * 256;
+}
 // Decode with the routing in the kernel (bfloat16 x, 1 <= t <= 16, K within one
 // workgroup): writes logits, budget, perm and offsets as launch_route does, and y.
 bool decode_route_supported(const mbq_desc& d, int32_t t);
@@ -78,7 +89,8 @@ hipError_t launch_decode_route(const mbq_desc& d, const void* packed, int32_t t,
 hipError_t launch_decode_stream(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                                 bool x_bf16, const int32_t* perm, const int32_t* offsets,
                                 void* y, bool y_bf16, void* ws, const float* lr_u, int32_t lr_ks,
-                                const uint16_t* lr_b, int32_t lr_r, hipStream_t stream);
+                                const uint16_t* lr_b, int32_t lr_r, uint8_t* lr_fz,
+                                const uint16_t* lr_a, hipStream_t stream);
 hipError_t launch_prefill(const mbq_desc& d, const void* packed, int32_t t, const void* x,
                           bool x_bf16, const int32_t* perm, const int32_t* offsets, void* y,
                           bool y_bf16, hipStream_t stream);
