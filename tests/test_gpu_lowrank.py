@@ -114,7 +114,7 @@ def test_lowrank_generic_decode_g64_s4_f32(mbq):
 
 @pytest.mark.parametrize("K,dtype,rank", [(2304, "bf16", 8), (2304, "bf16", 16), (2304, "f32", 16),
                                           (1280, "f32", 8), (4096, "bf16", 16), (8192, "bf16", 16),
-                                          (2304, "bf16", 32)])
+                                          (2304, "bf16", 32), (2304, "bf16", 24)])
 def test_lowrank_decode_tiles_chunks_ranks(mbq, K, dtype, rank):
     """The decode side path across one and two k tiles per wave, K within one workgroup
     and split over workgroups (8192), both activation types and ranks 8, 16 and 32."""
@@ -195,3 +195,10 @@ def test_lowrank_inline_u_call_state(mbq):
     check(xs[3][:5], y5, pm5, of5)
     state = ws[:12].view(torch.int32).cpu().numpy().tolist()
     assert state == [calls, 0, 0]
+
+
+def test_lowrank_inline_u_four_token_rows(mbq):
+    """u computed inside the launch for four 16-token rows (64 tokens, one producing
+    workgroup per row) with several row blocks parked per streaming workgroup."""
+    say("lowrank inline u, 64 tokens, 293 row blocks")
+    check(*run(mbq, 4688, 2304, 128, 3, 64, "bf16", 16, seed=77))
