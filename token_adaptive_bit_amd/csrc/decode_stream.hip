@@ -34,10 +34,11 @@ namespace mbq {
 namespace {
 
 constexpr int kMaxWaves = 8;
-// In-kernel routing: batches of at most this many tokens issue row block 1 only once the
-// budgets are known, with the slices some token uses (a one-token step usually reads one
-// of three slices, and row block 1's loads, issued earlier, stalled the routing behind
-// the memory queue).
+// In-kernel routing: batches of at most this many tokens issue row block 1's second and
+// later slices only once the budgets are known, with the slices some token uses (a
+// one-token step usually reads one of three slices, and those loads, issued earlier,
+// stalled the routing behind the memory queue); its first slice, which every token uses,
+// goes out with row block 0.
 constexpr int kLateRow1 = 1;
 constexpr int kMaxTokens = 64;  // tokens per launch (16 per workgroup row)
 // Reads of u (side path with lr_fz) before giving up: each is a round trip to memory plus
@@ -247,7 +248,9 @@ template <int G, int S, int TPW, bool LR>
 __device__ __forceinline__ void load_codes(Codes<G, S, TPW, LR>& C, const __amdgpu_buffer_rsrc_t (&rs)[S],
                                            int nb, const int (&kt)[TPW], int KB, int NG,
                                            uint32_t po, uint32_t lane_code,
-                                           const uint32_t (&lane_pv)[Codes<G, S, TPW, LR>::PH]) {
+                                           const uint32_t (&lane_pv)[Codes<G, S, TPW, LR>::PH],
+                                           int jlo = 0, int jhi = S) {
+  // (slices [jlo, jhi) only: the callers pass constants, so the loop below stays unrolled)
   constexpr int PH = Codes<G, S, TPW, LR>::PH;
   // nb < 0: a row block past the workgroup's last one.  Its loads still go out (every
   // path keeps the same loads in flight) but at an offset past every buffer's range
@@ -257,6 +260,7 @@ __device__ __forceinline__ void load_codes(Codes<G, S, TPW, LR>& C, const __amdg
   const uint32_t vc = dead ? kPastEnd : lane_code;
 #pragma unroll
   for (int j = 0; j < S; ++j) {
+    if (j < jlo || j >= jhi) continue;
 #pragma unroll
     for (int tp = 0; tp < TPW; ++tp) {
       const uint32_t tile = dead ? 0u : uint32_t(nb * KB + kt[tp]) * kTileBytes;
@@ -990,9 +994,15 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
         load_codes(c0, rs, rb0, kt, KB, NG, uint32_t(po), lane_code, lane_pv);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (kThreeBuffers && tp == TPW - 1 && T > kLateRow1) {
+      // Row block 1: every slice now above kLateRow1 tokens; otherwise only its first slice,
+      // which every token uses, now and the rest once the budgets are known (below).
+      // Either way its slices are pending in slice order when the stream starts.
+      if (kThreeBuffers && tp == TPW - 1) {
         __builtin_amdgcn_sched_barrier(0);
-        load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+        if (T > kLateRow1)
+          load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+        else
+          load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv, 0, 1);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -1052,7 +1062,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
     if constexpr (!PA && kThreeBuffers) {
       if (T <= kLateRow1) {
         __builtin_amdgcn_sched_barrier(0);
-        load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv);
+        load_codes(c1, rs, nbl(1), kt, KB, NG, uint32_t(po), lane_code, lane_pv, 1, S);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
