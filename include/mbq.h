@@ -206,8 +206,9 @@ mbq_status mbq_regroup(int32_t t, int32_t s, const int32_t* budget, int32_t* per
 
 /* Host only: bytes of device workspace mbq_route_mlp needs for t tokens of k inputs and
  * `hidden` hidden units: float32 partial hidden sums, c * t * hidden * 4 bytes, where c
- * is the number of K chunks the launch uses (c <= 64, chosen from t, k and hidden only).
- * 0 when t == 0. */
+ * is the number of K chunks the launch uses (c <= 64, chosen from t, k and hidden only),
+ * then, for t <= 64, 256 bytes of per-token budget words through which the gate's
+ * workgroups hand their budgets to the one that regroups.  0 when t == 0. */
 mbq_status mbq_route_mlp_workspace(int32_t t, int32_t k, int32_t hidden, size_t* bytes);
 
 /*

@@ -95,6 +95,8 @@ CASES = [
     ("f32", 300, 1000, 128, 2, 0.4),    # K % 32 != 0: a partial last k step
     ("bf16", 5, 100, 64, 3, 0.5),       # K % 8 != 0: element loads
     ("bf16", 33, 3584, 512, 4, 0.7),
+    ("bf16", 1, 3584, 256, 3, 0.4),     # one token: one gate workgroup
+    ("bf16", 63, 1024, 128, 3, 0.5),    # the last gate workgroup one wave short
     ("f32", 1, 64, 64, 3, 0.5),
     ("bf16", 16, 3584, 256, 1, 0.5),    # one slice: no scores, every budget 1
     ("bf16", 200, 13824, 64, 3, 0.45),  # long K (the down projection's input)

@@ -112,10 +112,14 @@ struct Frag {
 template <bool XBF16, bool VEC>
 __global__ __launch_bounds__(256) void mlp_hidden_small_kernel(const void* __restrict__ x, int T, int K,
                                                                const uint16_t* __restrict__ w1, int H,
-                                                               int kpc, float* __restrict__ part) {
+                                                               int kpc, float* __restrict__ part,
+                                                               int32_t* __restrict__ ready) {
   __shared__ float red[4][16][kHB];
   constexpr int ESZ = XBF16 ? 2 : 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the gate's per-token budget words start at zero (gate_multi_kernel reads them in the
+  // next launch)
+  if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x < T) ready[threadIdx.x] = 0;
   const int h0 = blockIdx.y * kHB;
   const int t0 = blockIdx.x * 16;
   const int nsteps = (K + 31) >> 5;
@@ -403,8 +407,57 @@ __global__ __launch_bounds__(256) void gate_kernel(int T, int H, int KS, const f
   if (lane == 0) budget[t] = b;
 }
 
-// t <= 64: sixteen waves gate the tokens, then wave 0 regroups them with ballot ranks
-// (stable: ranks follow token order within each budget).
+// t <= 64 with the hidden layer computed in the launch before: one wave per token over
+// ceil(t / 4) workgroups, so the chunk partials are read by several CUs at once.  Each wave
+// publishes its token's budget (>= 1) in a word the hidden launch cleared; wave 0 of
+// workgroup 0 then waits until every word is set and regroups with ballot ranks, as
+// gate_small_kernel does.  A budget is one word, so seeing it non-zero is seeing it whole.
+// The wait is bounded (a workgroup that never ran would leave its tokens at budget 1).
+constexpr int kGateSpin = 1 << 16;
+
+template <int R>
+__global__ __launch_bounds__(256) void gate_multi_kernel(int T, int S, int H, int KS,
+                                                         const float* __restrict__ part,
+                                                         const float* __restrict__ b1,
+                                                         const float* __restrict__ w2,
+                                                         const float* __restrict__ b2, float theta,
+                                                         float* __restrict__ scores, int32_t* __restrict__ budget,
+                                                         int32_t* __restrict__ perm, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ ready) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // wave-uniform
+  const int bt = token_budget<R, false>(t, T, H, KS, part, b1, w2, b2, theta, scores, lane);
+  if (lane == 0) __hip_atomic_store(ready + t, bt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (blockIdx.x != 0 || wave != 0) return;
+  int bl = 1;
+  for (int it = 0;; ++it) {
+    bl = lane < T ? __hip_atomic_load(ready + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+    if (__ballot(bl == 0) == 0ull) break;
+    if (it >= kGateSpin) {
+      bl = bl == 0 ? 1 : bl;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  const int b = lane < T ? bl : 0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int base = 0, pos = 0;
+  if (lane == 0) offsets[0] = 0;
+  for (int v = 1; v <= S; ++v) {
+    const uint64_t m = __ballot(b == v);
+    if (b == v) pos = base + __popcll(m & lt);
+    base += __popcll(m);
+    if (lane == 0) offsets[v] = base;
+  }
+  if (lane < T) {
+    perm[pos] = lane;
+    budget[lane] = b;
+  }
+}
+
+// t <= 64 with the scores given: sixteen waves gate the tokens, then wave 0 regroups them
+// with ballot ranks (stable: ranks follow token order within each budget).
 template <int R, bool SCORES_IN>
 __global__ __launch_bounds__(1024) void gate_small_kernel(int T, int S, int H, int KS,
                                                           const float* __restrict__ part,
@@ -469,10 +522,11 @@ MlpPlan mlp_plan(int32_t t, int32_t k, int32_t h) {
 
 }  // namespace
 
+// chunk partials [ks x t x h] float32, then (t <= 64) 256 bytes of per-token budget words
 size_t route_mlp_workspace(int32_t t, int32_t k, int32_t h) {
   if (t <= 0) return 0;
   const MlpPlan p = mlp_plan(t, k, h);
-  return size_t(p.ks) * size_t(t) * size_t(h) * sizeof(float);
+  return size_t(p.ks) * size_t(t) * size_t(h) * sizeof(float) + (t <= kSmallT ? 256 : 0);
 }
 
 hipError_t launch_route_mlp(int32_t t, int32_t k, int32_t s, int32_t h, const void* x, bool x_bf16,
@@ -488,6 +542,7 @@ hipError_t launch_route_mlp(int32_t t, int32_t k, int32_t s, int32_t h, const vo
                      (reinterpret_cast<uintptr_t>(w1) & 15) == 0;
     const dim3 grid(p.tiles, p.hblocks, p.ks);
     float* part = static_cast<float*>(ws);
+    int32_t* ready = reinterpret_cast<int32_t*>(part + size_t(p.ks) * size_t(t) * size_t(h));
     auto go = [&](auto xb, auto vv) {
       constexpr bool XB = decltype(xb)::value, VV = decltype(vv)::value;
       if (p.tiled)
@@ -495,7 +550,7 @@ hipError_t launch_route_mlp(int32_t t, int32_t k, int32_t s, int32_t h, const vo
                            h, p.kpc, part);
       else
         hipLaunchKernelGGL((mlp_hidden_small_kernel<XB, VV>), grid, dim3(256), 0, stream, x, t, k, w1,
-                           h, p.kpc, part);
+                           h, p.kpc, part, ready);
     };
     auto go_v = [&](auto xb) {
       if (vec) go(xb, std::true_type{});
@@ -510,7 +565,11 @@ hipError_t launch_route_mlp(int32_t t, int32_t k, int32_t s, int32_t h, const vo
   auto gate = [&](auto rr, auto si) {
     constexpr int RR = decltype(rr)::value;
     constexpr bool SI = decltype(si)::value;
-    if (t <= kSmallT)
+    if (t <= kSmallT && !SI && RR > 0)  // (the hidden launch ran and cleared the budget words)
+      hipLaunchKernelGGL((gate_multi_kernel<RR>), dim3((t + 3) / 4), dim3(256), 0, stream, t, s, h, p.ks,
+                         part, b1, w2, b2, theta, scores, budget, perm, offsets,
+                         const_cast<int32_t*>(reinterpret_cast<const int32_t*>(part + size_t(p.ks) * size_t(t) * size_t(h))));
+    else if (t <= kSmallT)
       hipLaunchKernelGGL((gate_small_kernel<RR, SI>), dim3(1), dim3(1024), 0, stream, t, s, h, p.ks,
                          part, b1, w2, b2, theta, scores, budget, perm, offsets);
     else
