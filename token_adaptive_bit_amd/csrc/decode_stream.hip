@@ -1261,15 +1261,20 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(
   }
 }
 
-// The first launch of the two-launch decode step (PA): two waves per k tile of 256 inputs
-// prepare what every workgroup of the streaming kernel would otherwise derive from the
-// raw activations on its own.  Wave 1 takes the tile's fp8 A operands (prep_a_f4) and
-// their group sums (the same instruction against all-ones codes); wave 0, in parallel, the
+// Whether the preparing launch gives each 128-input block of a k tile its own fp8 wave
+// (two or more groups per tile, so no group spans both blocks).
+constexpr bool prep_split(int G) { return G <= 128; }
+
+// The first launch of the two-launch decode step (PA): a workgroup per k tile of 256 inputs
+// prepares what every workgroup of the streaming kernel would otherwise derive from the
+// raw activations on its own.  Waves 1 and 2 take the fp8 A operands (prep_a_f4) of the
+// tile's two 128-input blocks and their group sums (the same instruction against all-ones
+// codes; wave 1 takes both blocks with groups of 256); wave 0, in parallel, the
 // tile's partial router logits (Wr as three exact bfloat16 planes on the bf16 matrix
 // instruction, as in the in-kernel routing).  bfloat16 x [t x K], t <= 16; tokens past t
 // repeat the last one (their rows are never used).  Output layout: PrepLayout.
 template <int G, int S>
-__global__ __launch_bounds__(128) void decode_prep_kernel(const uint8_t* __restrict__ x, int T, int K, int KB,
+__global__ __launch_bounds__(192) void decode_prep_kernel(const uint8_t* __restrict__ x, int T, int K, int KB,
                                                           const float* __restrict__ wr, uint8_t* __restrict__ prep) {
   asm volatile("" ::"s"(x), "s"(wr), "s"(prep), "s"(T), "s"(K), "s"(KB));
   constexpr int GPT = 256 / G;
@@ -1337,10 +1342,14 @@ __global__ __launch_bounds__(128) void decode_prep_kernel(const uint8_t* __restr
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       if (t * 256 + xk(i, h) >= K) a[i][h] = u32x4_t{0u, 0u, 0u, 0u};
-  // fp8 pairs and scales of the two 128-input blocks, then their group sums
+  // fp8 pairs and scales of the 128-input blocks, then their group sums.  With two or more
+  // groups per tile the blocks are independent: wave 1 + m takes block m (prep_split);
+  // with one group of 256 wave 1 takes both.
+  const int m_lo = prep_split(G) ? wv - 1 : 0, m_hi = prep_split(G) ? wv : 2;
   AF4 af[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) af[m] = prep_a_f4(a[2 * m][0], a[2 * m][1], a[2 * m + 1][0], a[2 * m + 1][1]);
+  for (int m = 0; m < 2; ++m)
+    if (m >= m_lo && m < m_hi) af[m] = prep_a_f4(a[2 * m][0], a[2 * m][1], a[2 * m + 1][0], a[2 * m + 1][1]);
   constexpr uint32_t kOne4 = 0x22222222u;
   f32x4_t xs[GPT];
 #pragma unroll
@@ -1348,6 +1357,7 @@ __global__ __launch_bounds__(128) void decode_prep_kernel(const uint8_t* __restr
     xs[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
+      if (m < m_lo || m >= m_hi) continue;
       if (G == 64 && m != (gi >> 1)) continue;
       if (G == 128 && m != gi) continue;
       const uint32_t lo = (G == 64 && (gi & 1)) ? 0u : kOne4, hi = (G == 64 && !(gi & 1)) ? 0u : kOne4;
@@ -1359,18 +1369,24 @@ __global__ __launch_bounds__(128) void decode_prep_kernel(const uint8_t* __restr
   chain_fence();
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
+    if (m < m_lo || m >= m_hi) continue;
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(prep + pl.a) + (size_t(t) * 8 + 4 * m) * 64 + lane;
     dst[0] = u32x4_t{uint32_t(af[m].hi[0]), uint32_t(af[m].hi[1]), uint32_t(af[m].hi[2]), uint32_t(af[m].hi[3])};
     dst[64] = u32x4_t{uint32_t(af[m].hi[4]), uint32_t(af[m].hi[5]), uint32_t(af[m].hi[6]), uint32_t(af[m].hi[7])};
     dst[128] = u32x4_t{uint32_t(af[m].lo[0]), uint32_t(af[m].lo[1]), uint32_t(af[m].lo[2]), uint32_t(af[m].lo[3])};
     dst[192] = u32x4_t{uint32_t(af[m].lo[4]), uint32_t(af[m].lo[5]), uint32_t(af[m].lo[6]), uint32_t(af[m].lo[7])};
   }
-  reinterpret_cast<uint2*>(prep + pl.sc)[size_t(t) * 64 + lane] = make_uint2(af[0].sc, af[1].sc);
-  // lanes (0, c) hold the group sums of tokens 4c .. 4c + 3
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    if (m >= m_lo && m < m_hi) reinterpret_cast<uint32_t*>(prep + pl.sc)[(size_t(t) * 64 + lane) * 2 + m] = af[m].sc;
+  // lanes (0, c) hold the group sums of tokens 4c .. 4c + 3 (of the wave's groups)
   if (r == 0) {
 #pragma unroll
-    for (int gi = 0; gi < GPT; ++gi)
+    for (int gi = 0; gi < GPT; ++gi) {
+      const int m = G == 64 ? gi >> 1 : (G == 128 ? gi : 0);
+      if (prep_split(G) && (m < m_lo || m >= m_hi)) continue;
       *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(prep + pl.xs) + (size_t(t) * GPT + gi) * 16 + 4 * c) = xs[gi];
+    }
   }
 }
 
@@ -1544,7 +1560,8 @@ hipError_t launch_prep_g(const mbq_desc& d, int32_t t, const void* x, const floa
                          hipStream_t stream) {
   const auto x8 = static_cast<const uint8_t*>(x);
   auto p8 = static_cast<uint8_t*>(prep);
-  const dim3 grid(d.k_tiles), block(128);   // per k tile: a routing wave and an fp8 wave
+  // per k tile: a routing wave and one fp8 wave per 128-input block (one for both at group 256)
+  const dim3 grid(d.k_tiles), block(prep_split(G) ? 192 : 128);
   switch (d.slices) {
     case 2: hipLaunchKernelGGL((decode_prep_kernel<G, 2>), grid, block, 0, stream, x8, t, d.k, d.k_tiles, wr, p8); break;
     case 3: hipLaunchKernelGGL((decode_prep_kernel<G, 3>), grid, block, 0, stream, x8, t, d.k, d.k_tiles, wr, p8); break;
